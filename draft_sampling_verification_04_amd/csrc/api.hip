@@ -1,0 +1,170 @@
+// api.hip -- exported C ABI (include/dspark.h): argument validation, workspace
+// sizing and dispatch to the kernel launchers.  Nothing here allocates device
+// memory or synchronises the stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dspark_status fail(dspark_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dspark_status ok() {
+    g_last_error[0] = '\0';
+    return DSPARK_OK;
+}
+
+bool valid_dtype(dspark_dtype d) { return d == DSPARK_F32 || d == DSPARK_BF16; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+dspark_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DSPARK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_version(void) { return "dspark-mi355x 0.1.0 (gfx950)"; }
+
+const char* dspark_last_error(void) { return g_last_error; }
+
+size_t dspark_draft_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r) {
+    if (B < 0 || K < 0 || V < 1 || r < 1) return 0;
+    return dspark::draft_workspace_bytes(B, K, V, r);
+}
+
+dspark_status dspark_draft_sample(const void* base_logits, dspark_dtype logit_dt, const void* A,
+                                  const void* W, dspark_dtype factor_dt,
+                                  const int32_t* prev_token, const float* temperature,
+                                  uint64_t seed, int32_t B, int32_t K, int32_t V, int32_t r,
+                                  int32_t* draft_tokens, float* draft_logp, float* draft_lse,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+    if (!valid_dtype(logit_dt) || !valid_dtype(factor_dt))
+        return fail(DSPARK_ERR_UNSUPPORTED_DTYPE, "draft_sample: unsupported dtype (%d, %d)",
+                    static_cast<int>(logit_dt), static_cast<int>(factor_dt));
+    if (B < 0 || K < 0) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: B=%d K=%d", B, K);
+    if (V < 1 || V >= (1 << 30)) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: V=%d", V);
+    if (r < 1 || r > 1024) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: r=%d", r);
+    if (B == 0 || K == 0) return ok();
+    if (!base_logits || !A || !W || !prev_token || !temperature || !draft_tokens)
+        return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: NULL required pointer");
+    if (static_cast<int64_t>(B) * K > (int64_t{1} << 31))
+        return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: B*K too large");
+    const size_t need = dspark::draft_workspace_bytes(B, K, V, r);
+    if (!workspace || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE_TOO_SMALL, "draft_sample: workspace %zu < %zu bytes",
+                    ws_bytes, need);
+    if (!aligned(workspace, 256))
+        return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: workspace not 256-byte aligned");
+    dspark::DraftArgs a{base_logits, logit_dt,     A,         W,          factor_dt,
+                        prev_token,  temperature,  seed,      B,          K,
+                        V,           r,            draft_tokens, draft_logp, draft_lse,
+                        workspace,   ws_bytes,     static_cast<hipStream_t>(stream)};
+    return hip_status(dspark::launch_draft(a), "draft_sample");
+}
+
+size_t dspark_schedule_workspace_bytes(int32_t B, int32_t K) {
+    if (B < 0 || K < 0) return 0;
+    return dspark::schedule_workspace_bytes(B, K);
+}
+
+dspark_status dspark_schedule(const float* conf, int32_t B, int32_t K, int64_t budget_tokens,
+                              const float* curve_n, const float* curve_latency, int32_t n_points,
+                              int32_t* lengths, int64_t* row_offsets, float* survival,
+                              void* workspace, size_t ws_bytes, void* stream) {
+    if (B < 0 || K < 0 || K > 64)
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: B=%d K=%d (0 <= K <= 64)", B, K);
+    if (static_cast<int64_t>(B) * K > (int64_t{1} << 22))
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: B*K too large");
+    if (n_points < 0 || n_points > dspark::kMaxCurvePoints)
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: n_points=%d", n_points);
+    if (n_points > 0 && (!curve_n || !curve_latency))
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: NULL curve arrays with n_points > 0");
+    if (!lengths || !row_offsets || (B > 0 && K > 0 && !conf))
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: NULL required pointer");
+    dspark::ScheduleArgs a;
+    a.n_points = n_points;
+    for (int i = 0; i < n_points; ++i) {
+        a.curve_n[i] = curve_n[i];
+        a.curve_tau[i] = curve_latency[i];
+        if (!(curve_latency[i] > 0.0f) || (i > 0 && !(curve_n[i] > curve_n[i - 1])))
+            return fail(DSPARK_ERR_INVALID_ARG,
+                        "schedule: curve needs increasing N and positive latency");
+    }
+    const size_t need = dspark::schedule_workspace_bytes(B, K);
+    if (ws_bytes < need || (need > 0 && !workspace))
+        return fail(DSPARK_ERR_WORKSPACE_TOO_SMALL, "schedule: workspace %zu < %zu bytes",
+                    ws_bytes, need);
+    if (workspace && !aligned(workspace, 256))
+        return fail(DSPARK_ERR_INVALID_ARG, "schedule: workspace not 256-byte aligned");
+    a.conf = conf;
+    a.B = B;
+    a.K = K;
+    a.budget = budget_tokens;
+    a.lengths = lengths;
+    a.row_offsets = row_offsets;
+    a.survival = survival;
+    a.ws = workspace;
+    a.ws_bytes = ws_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    return hip_status(dspark::launch_schedule(a), "schedule");
+}
+
+size_t dspark_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r) {
+    if (B < 0 || K < 0 || V < 1 || r < 1) return 0;
+    return dspark::verify_workspace_bytes(B, K, V, r);
+}
+
+dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_token,
+                            const float* draft_logp, const float* draft_lse,
+                            const void* base_logits, dspark_dtype logit_dt, const void* A,
+                            const void* W, dspark_dtype factor_dt, const void* target_logits,
+                            int64_t n_target_rows, const int64_t* target_row_offsets,
+                            const int32_t* lengths,
+                            const float* temperature, uint64_t seed, int32_t B, int32_t K,
+                            int32_t V, int32_t r, int32_t* accepted, int32_t* next_token,
+                            float* row_lse_t, float* row_logratio, void* workspace,
+                            size_t ws_bytes, void* stream) {
+    if (!valid_dtype(logit_dt) || !valid_dtype(factor_dt))
+        return fail(DSPARK_ERR_UNSUPPORTED_DTYPE, "verify: unsupported dtype (%d, %d)",
+                    static_cast<int>(logit_dt), static_cast<int>(factor_dt));
+    if (B < 0 || K < 0) return fail(DSPARK_ERR_INVALID_ARG, "verify: B=%d K=%d", B, K);
+    if (V < 1 || V >= (1 << 30)) return fail(DSPARK_ERR_INVALID_ARG, "verify: V=%d", V);
+    if (r < 1 || r > 1024) return fail(DSPARK_ERR_INVALID_ARG, "verify: r=%d", r);
+    if (n_target_rows < 0) return fail(DSPARK_ERR_INVALID_ARG, "verify: n_target_rows < 0");
+    if (B == 0) return ok();
+    if (!prev_token || !target_logits || !target_row_offsets || !temperature || !accepted ||
+        !next_token)
+        return fail(DSPARK_ERR_INVALID_ARG, "verify: NULL required pointer");
+    if (K > 0 && (!draft_tokens || !draft_logp || !draft_lse || !base_logits || !A || !W))
+        return fail(DSPARK_ERR_INVALID_ARG, "verify: NULL draft input");
+    if (static_cast<int64_t>(B) * (K + 1) > (int64_t{1} << 31))
+        return fail(DSPARK_ERR_INVALID_ARG, "verify: B*(K+1) too large");
+    const size_t need = dspark::verify_workspace_bytes(B, K, V, r);
+    if (!workspace || ws_bytes < need)
+        return fail(DSPARK_ERR_WORKSPACE_TOO_SMALL, "verify: workspace %zu < %zu bytes", ws_bytes,
+                    need);
+    if (!aligned(workspace, 256))
+        return fail(DSPARK_ERR_INVALID_ARG, "verify: workspace not 256-byte aligned");
+    dspark::VerifyArgs a{draft_tokens, prev_token,  draft_logp,  draft_lse,      base_logits,
+                         logit_dt,     A,           W,           factor_dt,      target_logits,
+                         n_target_rows, target_row_offsets,        lengths,     temperature,    seed,
+                         B,            K,           V,           r,              accepted,
+                         next_token,   row_lse_t,   row_logratio, workspace,     ws_bytes,
+                         static_cast<hipStream_t>(stream)};
+    return hip_status(dspark::launch_verify(a), "verify");
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// common.hpp -- device helpers shared by the draft, verify and schedule
+// kernels for gfx950 (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "../../include/dspark.h"
+
+namespace dspark {
+
+constexpr int kWave = 64;
+constexpr uint32_t kTagDraft = 0;
+constexpr uint32_t kTagAccept = 1;
+constexpr uint32_t kTagResample = 2;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- loads
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox4x32-10 (Salmon et al., SC'11, section 3): ten rounds of two 32x32->64
+// multiplies; the high halves are mixed into the other two words with the
+// round key, the words are re-ordered, and the key advances by two Weyl
+// constants per round.
+struct u32x4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                          uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+        const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        c1 = static_cast<uint32_t>(p1);
+        c3 = static_cast<uint32_t>(p0);
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return {c0, c1, c2, c3};
+}
+
+// Block of four draws for vocab indices 4q .. 4q+3.
+__device__ __forceinline__ u32x4 philox_block(uint64_t seed, uint32_t b, uint32_t pos,
+                                              uint32_t tag, uint32_t q) {
+    return philox10(q, pos, b, tag, static_cast<uint32_t>(seed),
+                    static_cast<uint32_t>(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t pick(const u32x4& r, int i) {
+    return i == 0 ? r.x : (i == 1 ? r.y : (i == 2 ? r.z : r.w));
+}
+
+// u = ((w >> 9) + 0.5) 2^-23, exact in fp32 (24 significant bits).
+__device__ __forceinline__ float uniform_of(uint32_t w) {
+    return __fmaf_rn(static_cast<float>(w >> 9), 0x1p-23f, 0x1p-24f);
+}
+
+__device__ __forceinline__ float gumbel_of(uint32_t w) {
+    return -logf(-logf(uniform_of(w)));
+}
+
+// Upper bound of gumbel_of(w) that costs no transcendental:
+// G = -log(-log u) <= -log(1 - u) and 1 - u >= n 2^-24 with n = 2^23 - (w >> 9),
+// so G <= (24 - floor(log2 n)) ln 2 = (clz(n) - 7) ln 2.  A margin of 1e-4
+// covers the rounding of the fp32 evaluation of G.
+__device__ __forceinline__ float gumbel_upper(uint32_t w) {
+    const uint32_t n = 0x800000u - (w >> 9);
+    return static_cast<float>(__clz(static_cast<int>(n)) - 7) * kLn2 + 1e-4f;
+}
+
+// ---------------------------------------------------------------- row state
+// Partial reduction state of one logits row over a subset of the vocabulary:
+// online-softmax max m and sum s = sum exp(z - m); the Gumbel-max winner
+// (perturbed value, logit at the winner, index).  Ties go to the smaller index.
+struct RowState {
+    float m;
+    float s;
+    float pert;
+    float zb;
+    int idx;
+};
+
+__device__ __forceinline__ RowState row_empty() {
+    return {-INFINITY, 0.0f, -INFINITY, -INFINITY, 0x7fffffff};
+}
+
+__device__ __forceinline__ bool beats(float p1, int i1, float p0, int i0) {
+    return p1 > p0 || (p1 == p0 && i1 < i0);
+}
+
+__device__ __forceinline__ void row_merge(RowState& a, const RowState& b) {
+    const float m = fmaxf(a.m, b.m);
+    if (m != -INFINITY) {
+        const float sa = (a.m == -INFINITY) ? 0.0f : a.s * expf(a.m - m);
+        const float sb = (b.m == -INFINITY) ? 0.0f : b.s * expf(b.m - m);
+        a.s = sa + sb;
+        a.m = m;
+    }
+    if (beats(b.pert, b.idx, a.pert, a.idx)) {
+        a.pert = b.pert;
+        a.zb = b.zb;
+        a.idx = b.idx;
+    }
+}
+
+__device__ __forceinline__ RowState shfl_xor_row(const RowState& a, int mask) {
+    RowState o;
+    o.m = __shfl_xor(a.m, mask, kWave);
+    o.s = __shfl_xor(a.s, mask, kWave);
+    o.pert = __shfl_xor(a.pert, mask, kWave);
+    o.zb = __shfl_xor(a.zb, mask, kWave);
+    o.idx = __shfl_xor(a.idx, mask, kWave);
+    return o;
+}
+
+__device__ __forceinline__ void wave_reduce_row(RowState& a) {
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) row_merge(a, shfl_xor_row(a, mask));
+}
+
+// Stored form of a partial: (m, s, pert, zb) and the index.
+struct PartialBuf {
+    float4* v;
+    int32_t* idx;
+};
+
+__device__ __forceinline__ void store_partial(PartialBuf p, size_t slot, const RowState& a) {
+    p.v[slot] = make_float4(a.m, a.s, a.pert, a.zb);
+    p.idx[slot] = a.idx;
+}
+
+__device__ __forceinline__ RowState load_partial(PartialBuf p, size_t slot) {
+    const float4 v = p.v[slot];
+    return {v.x, v.y, v.z, v.w, p.idx[slot]};
+}
+
+__device__ __forceinline__ float inv_temperature(float T) { return 1.0f / T; }
+
+// Token ids and lengths come from device memory the host cannot check; they are
+// clamped before they index anything.
+__device__ __forceinline__ int clamp_token(int x, int V) { return min(max(x, 0), V - 1); }
+__device__ __forceinline__ int clamp_len(int L, int K) { return min(max(L, 0), K); }
+
+}  // namespace dspark

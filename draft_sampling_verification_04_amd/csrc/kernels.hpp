@@ -1,0 +1,90 @@
+// kernels.hpp -- host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dspark.h"
+
+namespace dspark {
+
+// Vocabulary entries per partial (one workgroup strip) of the two draft paths.
+constexpr int kValuStrip = 1024;  // 256 threads x 4 entries
+constexpr int kMfmaStrip = 128;   // 4 MFMA row tiles of 32
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct DraftArgs {
+    const void* base;
+    dspark_dtype logit_dt;
+    const void* A;
+    const void* W;
+    dspark_dtype factor_dt;
+    const int32_t* prev_token;
+    const float* temperature;
+    uint64_t seed;
+    int B, K, V, r;
+    int32_t* tokens;
+    float* logp;
+    float* lse;
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+size_t draft_workspace_bytes(int B, int K, int V, int r);
+bool draft_uses_mfma(const DraftArgs& a);
+hipError_t launch_draft(const DraftArgs& a);
+
+struct VerifyArgs {
+    const int32_t* tokens;
+    const int32_t* prev_token;
+    const float* draft_logp;
+    const float* draft_lse;
+    const void* base;
+    dspark_dtype logit_dt;
+    const void* A;
+    const void* W;
+    dspark_dtype factor_dt;
+    const void* target;
+    int64_t n_rows;
+    const int64_t* row_off;
+    const int32_t* lengths;
+    const float* temperature;
+    uint64_t seed;
+    int B, K, V, r;
+    int32_t* accepted;
+    int32_t* next_token;
+    float* row_lse_t;
+    float* row_logratio;
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+size_t verify_workspace_bytes(int B, int K, int V, int r);
+hipError_t launch_verify(const VerifyArgs& a);
+
+constexpr int kMaxCurvePoints = 64;
+
+struct ScheduleArgs {
+    const float* conf;
+    int B, K;
+    int64_t budget;
+    int n_points;
+    double curve_n[kMaxCurvePoints];
+    double curve_tau[kMaxCurvePoints];
+    int32_t* lengths;
+    int64_t* row_offsets;
+    float* survival;
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+size_t schedule_workspace_bytes(int B, int K);
+hipError_t launch_schedule(const ScheduleArgs& a);
+
+}  // namespace dspark

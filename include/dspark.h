@@ -1,0 +1,176 @@
+/*
+ * dspark.h -- C ABI of the DSpark-style draft / schedule / verify hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the three calls compute (sources are the DSpark write-ups):
+ *   dspark_draft_sample  Markov-head draft: for every request and draft
+ *       position k, p_d(x_k | x_{k-1}) = softmax((base_logit_k + bias) / T)
+ *       with bias_v = A[x_{k-1}, :] . W[:, v], a rank-r factorisation of the
+ *       V x V transition matrix; x_k is drawn from it and fed to step k+1
+ *       (yage.ai "DSpark: speculative decoding and hardware scheduling",
+ *       paragraph on the first-order Markov head; freeaitool.com "DeepSeek
+ *       DSpark complete guide", section 3.1).
+ *   dspark_schedule  confidence-scheduled prefix selection: survival products
+ *       S_k = c_1 ... c_k per request, then a greedy sort of all (request,
+ *       position) items by S with an early stop against a token budget and an
+ *       optional throughput curve (freeaitool guide, sections 4.1-4.2; yage.ai
+ *       analysis, scheduler paragraph; legalagi.cn "Reading DSpark as a
+ *       lawyer", section 5).
+ *   dspark_verify  lossless rejection-sampling verification with strict
+ *       prefix semantics: accept x_j with probability min(1, p_t/p_d), on the
+ *       first rejection resample from normalise(max(0, p_t - p_d)), append a
+ *       bonus token from the target when every verified position is accepted
+ *       (yage.ai analysis, paragraphs on prefix matching and on rejection
+ *       sampling; legalagi.cn reading, section 3).
+ *
+ * Random draws: Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit seed
+ * (low word, high word) with counter (v >> 2, position, request, tag), word
+ * v & 3; uniform u = ((w >> 9) + 0.5) * 2^-23; Gumbel G = -log(-log u).
+ * Tags: 0 draft Gumbel (position k = 1..K), 1 accept uniform (v = 0,
+ * position j), 2 residual or bonus Gumbel (position of the resampled row).
+ * Temperature: per request; T > 0 multiplies logits by the fp32 reciprocal
+ * 1/T on both the draft and the target side, T == 0 is greedy on both sides
+ * (argmax, ties to the smallest index).  T must be finite and >= 0.
+ *
+ * Conventions shared by every call:
+ *   - Every array pointer is DEVICE memory owned by the caller, except the
+ *     schedule curve arrays, which are HOST memory read during the call.
+ *   - Layouts are row-major with the vocabulary innermost.
+ *   - The library allocates nothing: scratch memory comes in `workspace`
+ *     (size from the matching *_workspace_bytes query, 256-byte aligned).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and returns without synchronising.  Calls on different
+ *     streams with different workspaces may run concurrently.
+ *   - Host-side validation failures return a status and launch nothing;
+ *     dspark_last_error() (per thread) then describes the failure.  Launch
+ *     failures return DSPARK_ERR_HIP.  Non-finite logits give undefined
+ *     (but memory-safe) results.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dspark_status {
+    DSPARK_OK = 0,
+    DSPARK_ERR_INVALID_ARG = 1,        /* NULL pointer, bad size or out-of-range value */
+    DSPARK_ERR_UNSUPPORTED_DTYPE = 2,  /* dtype not in dspark_dtype */
+    DSPARK_ERR_WORKSPACE_TOO_SMALL = 3,
+    DSPARK_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} dspark_status;
+
+typedef enum dspark_dtype {
+    DSPARK_F32 = 0,
+    DSPARK_BF16 = 1
+} dspark_dtype;
+
+/* Library version string (static storage). */
+const char* dspark_version(void);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* ------------------------------------------------------------------ draft */
+/* Workspace bytes dspark_draft_sample needs for these sizes (any dtype). */
+size_t dspark_draft_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r);
+
+/*
+ * Markov-head draft sampling of K tokens for each of B requests.
+ *   base_logits  [B, K, V]  logit_dt    backbone logits per draft position
+ *   A            [V, r]     factor_dt   transition factor looked up by the previous token
+ *   W            [r, V]     factor_dt   transition factor over the next token
+ *   prev_token   [B] int32              x_0, the last committed token (0 <= x_0 < V)
+ *   temperature  [B] float              T per request
+ *   seed                                Philox key
+ * Outputs (device):
+ *   draft_tokens [B, K] int32           x_1 .. x_K
+ *   draft_logp   [B, K] float           log p_d(x_k) = z_{x_k} - lse_d (0 for T == 0); nullable
+ *   draft_lse    [B, K] float           lse_d = log sum_v exp(z_v), z = (base + bias)/T
+ *                                       (the row maximum for T == 0); nullable
+ * Sizes: B >= 0, K >= 0 (either 0 is a no-op), 1 <= V < 2^30, 1 <= r <= 1024.
+ */
+dspark_status dspark_draft_sample(const void* base_logits, dspark_dtype logit_dt, const void* A,
+                                  const void* W, dspark_dtype factor_dt,
+                                  const int32_t* prev_token, const float* temperature,
+                                  uint64_t seed, int32_t B, int32_t K, int32_t V, int32_t r,
+                                  int32_t* draft_tokens, float* draft_logp, float* draft_lse,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------- schedule */
+size_t dspark_schedule_workspace_bytes(int32_t B, int32_t K);
+
+/*
+ * Confidence-scheduled verification lengths.
+ *   conf        [B, K] float in [0, 1]  c_k: probability that draft token k is
+ *                                       accepted given that tokens 1..k-1 were
+ *   budget_tokens                       target batch tokens for this step; it
+ *                                       counts the B root tokens, so at most
+ *                                       D = max(0, budget - B) draft tokens are chosen
+ *   curve_n, curve_latency [n_points]   HOST arrays: piecewise-linear step
+ *                                       latency tau(N) of the target over N batch
+ *                                       tokens (strictly increasing N; constant left
+ *                                       of the first point, last slope right of the
+ *                                       last).  NULL / 0 = budget only.  n_points <= 64.
+ * Items (b, k) are taken in order of S = c_1..c_k descending (ties: smaller k,
+ * then smaller b) while fewer than D are taken, S > 0 and, with a curve, the
+ * objective (B + sum of taken S) / tau(B + taken) rises strictly.
+ * Outputs (device):
+ *   lengths     [B] int32               L_b in [0, K], the number of draft tokens to verify
+ *   row_offsets [B + 1] int64           exclusive scan of L_b + 1 (row_offsets[B] = rows)
+ *   survival    [B, K] float            S (sequential fp32 products); nullable
+ * Sizes: B >= 0, 0 <= K <= 64, B * K <= 2^22.
+ */
+dspark_status dspark_schedule(const float* conf, int32_t B, int32_t K, int64_t budget_tokens,
+                              const float* curve_n, const float* curve_latency, int32_t n_points,
+                              int32_t* lengths, int64_t* row_offsets, float* survival,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------- verify */
+size_t dspark_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r);
+
+/*
+ * Rejection-sampling verification of the drafted tokens.
+ *   draft_tokens [B, K] int32, prev_token [B] int32, draft_logp / draft_lse
+ *   [B, K] float: as written by dspark_draft_sample.
+ *   base_logits [B, K, V], A [V, r], W [r, V]: the draft inputs (the draft row
+ *   at the first rejected position is recomputed for the residual).
+ *   target_logits [rows, V] logit_dt: request b's verify rows j = 1 .. L_b + 1
+ *   are rows target_row_offsets[b] + j - 1 (row L_b + 1 gives the bonus).
+ *   Dense layout: offsets b * (K + 1); ragged layout: dspark_schedule's
+ *   row_offsets (its first B entries).
+ *   n_target_rows: rows in target_logits.  A request whose rows do not lie in
+ *   [0, n_target_rows) gets accepted = 0 and next_token = -1 (nothing is read).
+ *   lengths [B] int32 in [0, K]: verified draft tokens per request; NULL = K.
+ *   Out-of-range lengths are clamped to [0, K]; token ids are clamped to
+ *   [0, V) before they index A or a target row.
+ * Outputs (device):
+ *   accepted    [B] int32   a_b = number of leading accepted draft tokens (<= L_b)
+ *   next_token  [B] int32   residual sample at a_b + 1 when a_b < L_b, else the bonus
+ *   row_lse_t   [rows] float  target log-normaliser per visited row (row maximum
+ *                             for T == 0); nullable
+ *   row_logratio [rows] float log p_t(x_j) - log p_d(x_j) for rows j <= L_b
+ *                             (T == 0: 0 if x_j is the target argmax, else -inf;
+ *                             bonus row: 0); nullable
+ * Rows that belong to no request are not touched.
+ */
+dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_token,
+                            const float* draft_logp, const float* draft_lse,
+                            const void* base_logits, dspark_dtype logit_dt, const void* A,
+                            const void* W, dspark_dtype factor_dt, const void* target_logits,
+                            int64_t n_target_rows, const int64_t* target_row_offsets,
+                            const int32_t* lengths,
+                            const float* temperature, uint64_t seed, int32_t B, int32_t K,
+                            int32_t V, int32_t r, int32_t* accepted, int32_t* next_token,
+                            float* row_lse_t, float* row_logratio, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

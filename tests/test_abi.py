@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched):
+the library loads, exports every function include/dspark.h declares, and its
+argument validation returns the documented status codes before any launch."""
+import ctypes
+
+import pytest
+import torch
+
+import draft_sampling_verification_04_amd as d
+from draft_sampling_verification_04_amd import binding as bd
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def L():
+    return d.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = d.header_functions()
+    assert {"dspark_draft_sample", "dspark_schedule", "dspark_verify"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert d.dspark_version().startswith("dspark")
+
+
+def test_workspace_queries(L):
+    a = d.dspark_draft_workspace_bytes(256, 16, 151936, 256)
+    b = d.dspark_draft_workspace_bytes(512, 16, 151936, 256)
+    assert 0 < a < b and a % 256 == 0
+    assert d.dspark_verify_workspace_bytes(256, 16, 151936, 256) > 0
+    assert d.dspark_schedule_workspace_bytes(1024, 16) >= 8 * 1024 * 16
+    assert d.dspark_draft_workspace_bytes(-1, 1, 1, 1) == 0
+
+
+def _draft(L, **kw):
+    args = dict(base=FAKE, ldt=1, A=FAKE, W=FAKE, fdt=1, prev=FAKE, temp=FAKE, seed=0, B=4, K=2,
+                V=100, r=16, tok=FAKE, logp=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return L.dspark_draft_sample(args["base"], args["ldt"], args["A"], args["W"], args["fdt"],
+                                 args["prev"], args["temp"], args["seed"], args["B"], args["K"],
+                                 args["V"], args["r"], args["tok"], args["logp"], args["lse"],
+                                 args["ws"], args["wsb"], args["stream"])
+
+
+def test_draft_validation(L):
+    assert _draft(L, ldt=7) == bd.DSPARK_ERR_UNSUPPORTED_DTYPE
+    assert b"dtype" in L.dspark_last_error()
+    assert _draft(L, fdt=-1) == bd.DSPARK_ERR_UNSUPPORTED_DTYPE
+    assert _draft(L, base=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, tok=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, V=0) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, r=2000) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, B=-1) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, wsb=16) == bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
+    assert _draft(L, ws=None) == bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
+    assert _draft(L, ws=ctypes.c_void_p(0x1004)) == bd.DSPARK_ERR_INVALID_ARG  # misaligned
+    # empty problems are valid no-ops (nothing is launched, pointers unused)
+    assert _draft(L, B=0, base=None, ws=None, wsb=0) == bd.DSPARK_OK
+    assert L.dspark_last_error() == b""
+    assert _draft(L, K=0, base=None, ws=None, wsb=0) == bd.DSPARK_OK
+
+
+def test_schedule_validation(L):
+    f = L.dspark_schedule
+    cn = (ctypes.c_float * 2)(10.0, 20.0)
+    ct = (ctypes.c_float * 2)(1.0, 2.0)
+    bad_ct = (ctypes.c_float * 2)(1.0, -2.0)
+    ws = 1 << 20
+    assert f(FAKE, 4, 65, 10, None, None, 0, FAKE, FAKE, None, FAKE, ws, None) == \
+        bd.DSPARK_ERR_INVALID_ARG
+    assert f(FAKE, 4, 4, 10, None, None, 65, FAKE, FAKE, None, FAKE, ws, None) == \
+        bd.DSPARK_ERR_INVALID_ARG
+    assert f(FAKE, 4, 4, 10, None, None, 2, FAKE, FAKE, None, FAKE, ws, None) == \
+        bd.DSPARK_ERR_INVALID_ARG
+    assert f(FAKE, 4, 4, 10, cn, bad_ct, 2, FAKE, FAKE, None, FAKE, ws, None) == \
+        bd.DSPARK_ERR_INVALID_ARG
+    dec = (ctypes.c_float * 2)(20.0, 10.0)
+    assert f(FAKE, 4, 4, 10, dec, ct, 2, FAKE, FAKE, None, FAKE, ws, None) == \
+        bd.DSPARK_ERR_INVALID_ARG
+    assert f(FAKE, 4, 4, 10, None, None, 0, None, FAKE, None, FAKE, ws, None) == \
+        bd.DSPARK_ERR_INVALID_ARG
+    assert f(FAKE, 100, 16, 10, None, None, 0, FAKE, FAKE, None, FAKE, 8, None) == \
+        bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
+    assert f(FAKE, 2048, 2049, 10, None, None, 0, FAKE, FAKE, None, FAKE, ws, None) == \
+        bd.DSPARK_ERR_INVALID_ARG
+
+
+def test_verify_validation(L):
+    f = L.dspark_verify
+
+    def call(**kw):
+        a = dict(tok=FAKE, prev=FAKE, logp=FAKE, lse=FAKE, base=FAKE, ldt=1, A=FAKE, W=FAKE, fdt=1,
+                 tgt=FAKE, rows=100, offs=FAKE, lens=None, temp=FAKE, seed=1, B=4, K=3, V=50, r=16,
+                 acc=FAKE, nxt=FAKE, rl=None, rr=None, ws=FAKE, wsb=1 << 30, stream=None)
+        a.update(kw)
+        return f(a["tok"], a["prev"], a["logp"], a["lse"], a["base"], a["ldt"], a["A"], a["W"],
+                 a["fdt"], a["tgt"], a["rows"], a["offs"], a["lens"], a["temp"], a["seed"], a["B"],
+                 a["K"], a["V"], a["r"], a["acc"], a["nxt"], a["rl"], a["rr"], a["ws"], a["wsb"],
+                 a["stream"])
+
+    assert call(ldt=3) == bd.DSPARK_ERR_UNSUPPORTED_DTYPE
+    assert call(tgt=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert call(lse=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert call(rows=-1) == bd.DSPARK_ERR_INVALID_ARG
+    assert call(wsb=10) == bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
+    assert call(B=0, tgt=None, ws=None, wsb=0) == bd.DSPARK_OK
+    # K = 0: draft inputs may be NULL (only the bonus row is used); still needs workspace
+    assert call(K=0, tok=None, logp=None, lse=None, base=None, A=None, W=None,
+                wsb=1) == bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros((2, 2, 8))
+    with pytest.raises(d.DsparkError):
+        d.dspark_draft_sample(x, torch.zeros((8, 4)), torch.zeros((4, 8)),
+                              torch.zeros(2, dtype=torch.int32), torch.ones(2), 0)

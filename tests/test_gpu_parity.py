@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes span several vocabulary strips and a ragged tail; the named workloads
+run at their full sizes with the oracle on a sampled subset of requests
+(requests are independent, so per-request parity at the real V, r and K is
+complete evidence for those requests).  See tests/parity.py for the rules.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsp():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import draft_sampling_verification_04_amd as d
+
+    d.lib()  # raises when the HIP library is missing
+    return d
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    from draft_sampling_verification_04_amd import inputs as m
+
+    return m
+
+
+def _sample_requests(temp, n_per_temp=1, extra=()):
+    """A few requests covering every temperature present (plus extra ones)."""
+    t = temp.cpu().numpy()
+    idx = []
+    for v in sorted(set(t.tolist())):
+        idx += [int(i) for i in np.nonzero(t == v)[0][:n_per_temp]]
+    idx += [int(i) for i in extra if i < len(t)]
+    return sorted(set(idx))
+
+
+def _draft_and_verify(dsp, orc, inp, seed, idx, tol, lengths=None, row_off=None, target=None):
+    """GPU draft on all requests, oracle on idx; then verify with the oracle's
+    draft for idx (GPU draft elsewhere) and compare."""
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], seed)
+    torch.cuda.synchronize()
+    ora = P.oracle_draft(orc, inp, idx, seed)
+    tally = P.Tally()
+    P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
+                    inp["temp"].cpu().numpy(), tol, tally)
+    B, K, V = inp["base"].shape
+    # verify inputs: oracle draft outputs on the sampled requests
+    for b in idx:
+        tok[b] = torch.from_numpy(ora[b][0]).to(tok.device)
+        logp[b] = torch.from_numpy(ora[b][1]).to(tok.device)
+        lse[b] = torch.from_numpy(ora[b][2]).to(tok.device)
+    if target is None:
+        target = inp["target"].reshape(-1, V)
+        row_off = torch.arange(B, dtype=torch.int64, device=tok.device) * (K + 1)
+    acc, nxt, rl, rr = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                         inp["W"], target, row_off, inp["temp"], seed, lengths)
+    torch.cuda.synchronize()
+    L = {b: (K if lengths is None else int(lengths[b])) for b in idx}
+    ro = row_off.cpu().numpy()
+    rows = {b: P.np32(target[int(ro[b]):int(ro[b]) + L[b] + 1]) for b in idx}
+    orv = P.oracle_verify(orc, inp, idx, {b: ora[b][0] for b in idx}, rows, L, seed)
+    P.compare_verify(acc.cpu().numpy(), nxt.cpu().numpy(), rl.cpu().numpy(), rr.cpu().numpy(),
+                     ro, orv, tol, tally)
+    return tally, (tok, logp, lse, acc, nxt)
+
+
+def test_tiny_full_parity(dsp, orc, inputs):
+    w = inputs.WORKLOADS["tiny"]
+    inp = inputs.make_inputs(w, "cuda", seed=0)
+    tally, _ = _draft_and_verify(dsp, orc, inp, 0, list(range(w.B)), P.tol_for(w.dtype))
+    print(tally)
+    assert tally.compared >= w.B
+
+
+@pytest.mark.parametrize("V,r,K,B,ldt,fdt", [
+    (3001, 32, 3, 6, torch.bfloat16, torch.bfloat16),
+    (777, 16, 2, 3, torch.float32, torch.bfloat16),
+    (5, 16, 4, 4, torch.bfloat16, torch.float32),
+    (1, 16, 2, 2, torch.float32, torch.float32),
+    (4099, 48, 5, 9, torch.float32, torch.float32),
+])
+def test_small_shapes_parity(dsp, orc, inputs, V, r, K, B, ldt, fdt):
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=B, K=K, V=V, r=r, dtype=ldt)
+    inp = inputs.make_inputs(w, "cuda", seed=V + K)
+    inp["A"] = inp["A"].to(fdt)
+    inp["W"] = inp["W"].to(fdt)
+    tally, _ = _draft_and_verify(dsp, orc, inp, 11, list(range(B)), P.tol_for(ldt))
+    print(tally)
+    assert tally.compared >= 1
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b", "long_draft", "high_conc"])
+def test_full_size_sampled_parity(dsp, orc, inputs, name):
+    w = inputs.WORKLOADS[name]
+    inp = inputs.make_inputs(w, "cuda", seed=1)
+    idx = _sample_requests(inp["temp"], 1, extra=(w.B - 1,))
+    tally, _ = _draft_and_verify(dsp, orc, inp, 5, idx, P.tol_for(w.dtype))
+    print(name, idx, tally)
+    assert tally.compared >= 1
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_conf_sched_pipeline_parity(dsp, orc, inputs):
+    """Draft -> schedule -> ragged verify of the scheduled prefixes only."""
+    w = inputs.WORKLOADS["conf_sched"]
+    inp = inputs.make_inputs(w, "cuda", seed=3, with_target=False)
+    conf, _ = inputs.make_confidence(w, "cuda", seed=3)
+    cn, ct = w.curve()
+    L, offs, S = dsp.dspark_schedule(conf, w.budget, cn, ct)
+    torch.cuda.synchronize()
+    oL, ooffs, oS, n = orc.schedule(conf.cpu().numpy(), w.budget, np.array(cn), np.array(ct))
+    np.testing.assert_array_equal(S.cpu().numpy(), oS)
+    np.testing.assert_array_equal(L.cpu().numpy(), oL)
+    np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+    assert int(offs[-1]) <= w.budget
+    target = inputs.ragged_target(w, inp["base"], L, offs, "cuda", seed=3)
+    idx = [0, 1, 2, w.B - 1]
+    tally, _ = _draft_and_verify(dsp, orc, inp, 9, idx, P.tol_for(w.dtype), lengths=L,
+                                 row_off=offs, target=target)
+    print(tally)
+    assert tally.compared >= 1
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_schedule_parity_random(dsp, orc, seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 300))
+    K = int(rng.integers(1, 17))
+    conf = rng.beta(5, 2, (B, K)).astype(np.float32)
+    if seed == 1:
+        conf[:] = 1.0  # all ties: order by k then b
+    if seed == 2:
+        conf[rng.random((B, K)) < 0.2] = 0.0
+    for budget in (0, B - 1, B, B + 1, B + int(rng.integers(1, B * K + 1)), B * (K + 1) + 5):
+        for curve in (None, (np.array([B + 3.0, B + 40.0]), np.array([1.0, 2.0]))):
+            c = torch.from_numpy(conf).cuda()
+            if curve is None:
+                L, offs, S = dsp.dspark_schedule(c, budget)
+                oL, ooffs, oS, _ = orc.schedule(conf, budget)
+            else:
+                L, offs, S = dsp.dspark_schedule(c, budget, curve[0].tolist(), curve[1].tolist())
+                oL, ooffs, oS, _ = orc.schedule(conf, budget, curve[0].astype(np.float32)
+                                                .astype(np.float64), curve[1])
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(S.cpu().numpy(), oS)
+            np.testing.assert_array_equal(L.cpu().numpy(), oL)
+            np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+
+
+def test_schedule_high_conc_parity(dsp, orc, inputs):
+    w = inputs.WORKLOADS["high_conc"]
+    conf, _ = inputs.make_confidence(w, "cuda", seed=4)
+    L, offs, S = dsp.dspark_schedule(conf, w.budget)
+    torch.cuda.synchronize()
+    oL, ooffs, oS, n = orc.schedule(conf.cpu().numpy(), w.budget)
+    np.testing.assert_array_equal(L.cpu().numpy(), oL)
+    np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+    assert n == w.budget - w.B
+
+
+def test_verify_edge_cases(dsp, orc, inputs):
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=5, K=3, V=700, r=16)
+    inp = inputs.make_inputs(w, "cuda", seed=21)
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], 2)
+    target = inp["target"].reshape(-1, w.V)
+    offs = torch.arange(w.B, dtype=torch.int64, device="cuda") * (w.K + 1)
+    # L = 0 everywhere: bonus from row 1
+    L0 = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    acc, nxt, rl, _ = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                        inp["W"], target, offs, inp["temp"], 2, L0)
+    torch.cuda.synchronize()
+    assert (acc == 0).all()
+    for b in range(w.B):
+        res = orc.verify_request(tok[b].cpu().numpy(), int(inp["prev"][b]),
+                                 P.np32(inp["base"][b]), P.np32(inp["A"]), P.np32(inp["W"]),
+                                 P.np32(target[b * (w.K + 1):b * (w.K + 1) + 1]), 0,
+                                 float(inp["temp"][b]), 2, b)
+        assert int(nxt[b]) == res["next_token"] or res["next_gap"] < P.NEAR_TIE
+    # rows outside the target tensor: accepted 0, next -1, nothing read
+    bad = offs.clone()
+    bad[1] = 10**9
+    bad[3] = -1
+    acc, nxt, _, _ = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                       inp["W"], target, bad, inp["temp"], 2)
+    torch.cuda.synchronize()
+    assert int(acc[1]) == 0 and int(nxt[1]) == -1
+    assert int(acc[3]) == 0 and int(nxt[3]) == -1
+    assert (nxt[[0, 2, 4]] >= 0).all()
+
+
+def test_two_streams_and_determinism(dsp, inputs):
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=32, K=4, V=20000, r=64)
+    inp = inputs.make_inputs(w, "cuda", seed=8, with_target=False)
+    ref = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"], inp["temp"], 3)
+    again = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"], inp["temp"], 3)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, again):
+        assert torch.equal(x, y)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        o1 = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"], inp["temp"], 3,
+                                     stream=s1)
+    with torch.cuda.stream(s2):
+        o2 = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"], inp["temp"], 4,
+                                     stream=s2)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, o1):
+        assert torch.equal(x, y)
+    o4 = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"], inp["temp"], 4)
+    torch.cuda.synchronize()
+    for x, y in zip(o2, o4):
+        assert torch.equal(x, y)
+
+
+def test_gpu_chi_square_and_bitexact(dsp, orc):
+    """10^6 requests (independent Philox streams): the first two emitted tokens
+    follow the target's joint law; the first 1500 match the oracle bit for bit."""
+    V, K, r, n, T, seed = 8, 2, 3, 1_000_000, 1.0, 77
+    rng = np.random.default_rng(5)
+    base = rng.normal(0, 1.2, (K, V)).astype(np.float32)
+    A = rng.normal(0, 0.8, (V, r)).astype(np.float32)
+    W = rng.normal(0, 0.8, (r, V)).astype(np.float32)
+    t1 = (rng.normal(0, 1.0, V) + 0.7 * base[0]).astype(np.float32)
+    t2 = rng.normal(0, 1.0, (V, V)).astype(np.float32)
+    t3 = rng.normal(0, 1.0, (V, V, V)).astype(np.float32)
+
+    def tgt(prefix):
+        return [t1, t2[prefix[0]] if len(prefix) > 0 else None,
+                t3[tuple(prefix[:2])] if len(prefix) > 1 else None][len(prefix)]
+
+    dev = "cuda"
+    g_base = torch.from_numpy(base).to(dev).expand(n, K, V).contiguous()
+    g_A, g_W = torch.from_numpy(A).to(dev), torch.from_numpy(W).to(dev)
+    prev = torch.full((n,), 3, dtype=torch.int32, device=dev)
+    temp = torch.full((n,), T, dtype=torch.float32, device=dev)
+    tok, logp, lse = dsp.dspark_draft_sample(g_base, g_A, g_W, prev, temp, seed)
+    x = tok.long()
+    rows = torch.stack([torch.from_numpy(t1).to(dev).expand(n, V),
+                        torch.from_numpy(t2).to(dev)[x[:, 0]],
+                        torch.from_numpy(t3).to(dev)[x[:, 0], x[:, 1]]], dim=1).contiguous()
+    offs = torch.arange(n, dtype=torch.int64, device=dev) * (K + 1)
+    acc, nxt, _, _ = dsp.dspark_verify(tok, prev, logp, lse, g_base, g_A, g_W,
+                                       rows.view(-1, V), offs, temp, seed)
+    torch.cuda.synchronize()
+    tok_c, acc_c, nxt_c = tok.cpu().numpy(), acc.cpu().numpy(), nxt.cpu().numpy()
+    # bit-exact against the oracle on a prefix of the requests
+    m = 1500
+    o_tok, o_logp, o_lse, o_gap = orc.draft_batch(np.broadcast_to(base, (m, K, V)), A, W,
+                                                  np.full(m, 3, np.int32), np.full(m, T, np.float32),
+                                                  seed)
+    o_rows = rows[:m].cpu().numpy().reshape(-1, V)
+    orv = orc.verify_batch(o_tok, np.full(m, 3, np.int32), np.broadcast_to(base, (m, K, V)), A, W,
+                           o_rows, np.arange(m, dtype=np.int64) * (K + 1), None,
+                           np.full(m, T, np.float32), seed)
+    near = 0
+    for b in range(m):
+        if (tok_c[b] != o_tok[b]).any():
+            assert o_gap[b].min() < P.NEAR_TIE
+            near += 1
+            continue
+        if acc_c[b] != orv["accepted"][b] or nxt_c[b] != orv["next_token"][b]:
+            assert min(orv["accept_gap"][b], orv["next_gap"][b]) < P.NEAR_TIE
+            near += 1
+    assert near <= 3
+    # law of the first two emitted tokens
+    z1 = np.where(acc_c >= 1, tok_c[:, 0], nxt_c)
+    z2 = np.where(acc_c >= 2, tok_c[:, 1], np.where(acc_c == 1, nxt_c, -1))
+    need = np.nonzero(z2 < 0)[0]
+    crng = np.random.default_rng(9)
+    for a in range(V):
+        sel = need[z1[need] == a]
+        if len(sel):
+            z2[sel] = crng.choice(V, size=len(sel), p=orc.target_probs(t2[a], T))
+    joint = orc.target_joint(tgt, T, V, 2)
+    expect = np.array([[joint[(a, b)] for b in range(V)] for a in range(V)]) * n
+    counts = np.zeros((V, V))
+    np.add.at(counts, (z1, z2), 1)
+    chi = ((counts - expect) ** 2 / expect).sum()
+    assert stats.chi2.sf(chi, V * V - 1) > 1e-3
+    # acceptance rate at position 1 against 1 - TV
+    pd = orc.draft_probs(base[0], A, W, 3, T)
+    pt = orc.target_probs(t1, T)
+    p_acc = np.minimum(pd, pt).sum()
+    rate = (acc_c >= 1).mean()
+    assert abs(rate - p_acc) < 5 * np.sqrt(p_acc * (1 - p_acc) / n)
