@@ -32,7 +32,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_draft")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=1)
+    ap.add_argument("--cpu-requests", type=int, default=24)
     return ap.parse_args()
 
 

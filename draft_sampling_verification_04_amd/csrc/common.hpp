@@ -8,6 +8,7 @@
 #include <cmath>
 
 #include "../../include/dspark.h"
+#include "kernels.hpp"
 
 namespace dspark {
 
@@ -37,14 +38,19 @@ struct u32x4 {
     uint32_t x, y, z, w;
 };
 
+// Three-way xor in one gfx950 VALU op (v_bitop3_b32, truth table 0x96 = odd parity).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ u32x4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                           uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
         const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
         const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
-        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3(static_cast<uint32_t>(p0 >> 32), c3, k1);
         c1 = static_cast<uint32_t>(p1);
         c3 = static_cast<uint32_t>(p0);
         c0 = n0;
@@ -73,6 +79,14 @@ __device__ __forceinline__ float uniform_of(uint32_t w) {
 
 __device__ __forceinline__ float gumbel_of(uint32_t w) {
     return -logf(-logf(uniform_of(w)));
+}
+
+// Same Gumbel from the hardware base-2 logarithm.  Both logarithm arguments
+// are normal floats (u >= 2^-24 and -ln u >= 5.9e-8), so no denormal handling
+// is needed; the result agrees with the fp64 value to a few fp32 ulps.
+__device__ __forceinline__ float gumbel_fast(uint32_t w) {
+    const float a = -__builtin_amdgcn_logf(uniform_of(w)) * kLn2;
+    return -__builtin_amdgcn_logf(a) * kLn2;
 }
 
 // Upper bound of gumbel_of(w) that costs no transcendental:
@@ -134,11 +148,21 @@ __device__ __forceinline__ void wave_reduce_row(RowState& a) {
     for (int mask = 32; mask >= 1; mask >>= 1) row_merge(a, shfl_xor_row(a, mask));
 }
 
-// Stored form of a partial: (m, s, pert, zb) and the index.
-struct PartialBuf {
-    float4* v;
-    int32_t* idx;
-};
+// Workgroup reduction of one RowState per thread; the result is valid in
+// thread 0.  red must hold one RowState per wavefront.
+template <int NT>
+__device__ __forceinline__ RowState block_reduce_row(RowState st, RowState* red) {
+    wave_reduce_row(st);
+    const int tid = threadIdx.x;
+    if ((tid & 63) == 0) red[tid >> 6] = st;
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < NT / kWave; ++w) row_merge(st, red[w]);
+    }
+    return st;
+}
+
 
 __device__ __forceinline__ void store_partial(PartialBuf p, size_t slot, const RowState& a) {
     p.v[slot] = make_float4(a.m, a.s, a.pert, a.zb);

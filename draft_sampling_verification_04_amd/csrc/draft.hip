@@ -129,20 +129,20 @@ __global__ __launch_bounds__(256) void draft_strip_valu(
     }
 }
 
-// Fold the strips of each request (one wavefront per request) and write x_k,
-// log p_d(x_k) and lse_d.
-__global__ __launch_bounds__(64) void draft_combine(PartialBuf part, int n_strips,
-                                                   const float* __restrict__ temperature, int K,
-                                                   int k, int32_t* __restrict__ tokens,
-                                                   float* __restrict__ logp,
-                                                   float* __restrict__ lse) {
+// Fold the strips of each request (one 256-thread workgroup per request) and
+// write x_k, log p_d(x_k) and lse_d.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void draft_combine(
+    PartialBuf part, int n_strips, const float* __restrict__ temperature, int K, int k,
+    int32_t* __restrict__ tokens, float* __restrict__ logp, float* __restrict__ lse) {
+    __shared__ RowState red[kCombineThreads / kWave];
     const int b = blockIdx.x;
-    const int lane = threadIdx.x;
     RowState st = row_empty();
-    for (int s = lane; s < n_strips; s += kWave)
+    for (int s = threadIdx.x; s < n_strips; s += kCombineThreads)
         row_merge(st, load_partial(part, static_cast<size_t>(b) * n_strips + s));
-    wave_reduce_row(st);
-    if (lane == 0) {
+    st = block_reduce_row<kCombineThreads>(st, red);
+    if (threadIdx.x == 0) {
         const size_t o = static_cast<size_t>(b) * K + k;
         tokens[o] = st.idx;
         if (temperature[b] > 0.0f) {
@@ -170,47 +170,71 @@ void launch_valu_strip(const DraftArgs& a, const int32_t* prev, int prev_stride,
 }  // namespace
 
 // Implemented in draft_mfma.hip.
+bool mfma_supported(const DraftArgs& a);
+hipError_t launch_temperature_order(const float* temperature, int B, int32_t* order,
+                                    hipStream_t stream);
 hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
-                                  PartialBuf part, int n_strips);
-bool mfma_supported(int r, dspark_dtype factor_dt);
+                                  const int32_t* order, PartialBuf part, int n_strips);
+
+namespace {
+
+struct DraftWs {
+    PartialBuf part;
+    int32_t* order;
+};
+
+DraftWs draft_ws(void* ws, int B, int V) {
+    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMfmaStrip);  // the larger strip count
+    char* w = static_cast<char*>(ws);
+    DraftWs d;
+    d.part.v = reinterpret_cast<float4*>(w);
+    d.part.idx = reinterpret_cast<int32_t*>(w + align256(n * sizeof(float4)));
+    d.order = reinterpret_cast<int32_t*>(w + align256(n * sizeof(float4)) +
+                                         align256(n * sizeof(int32_t)));
+    return d;
+}
+
+}  // namespace
 
 size_t draft_workspace_bytes(int B, int K, int V, int r) {
     (void)K;
     (void)r;
-    const size_t ns = static_cast<size_t>(ceil_div(V, kMfmaStrip));  // the larger count
-    const size_t n = static_cast<size_t>(B) * ns;
-    return align256(n * sizeof(float4)) + align256(n * sizeof(int32_t));
+    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMfmaStrip);
+    return align256(n * sizeof(float4)) + align256(n * sizeof(int32_t)) +
+           align256(static_cast<size_t>(B) * sizeof(int32_t));
 }
 
-bool draft_uses_mfma(const DraftArgs& a) { return mfma_supported(a.r, a.factor_dt); }
+bool draft_uses_mfma(const DraftArgs& a) { return mfma_supported(a); }
 
 hipError_t launch_draft(const DraftArgs& a) {
     if (a.B == 0 || a.K == 0) return hipSuccess;
     const bool mfma = draft_uses_mfma(a);
     const int n_strips = static_cast<int>(ceil_div(a.V, mfma ? kMfmaStrip : kValuStrip));
-    const size_t n = static_cast<size_t>(a.B) * n_strips;
-    PartialBuf part;
-    part.v = static_cast<float4*>(a.ws);
-    part.idx = reinterpret_cast<int32_t*>(static_cast<char*>(a.ws) + align256(n * sizeof(float4)));
+    const DraftWs ws = draft_ws(a.ws, a.B, a.V);
+    if (mfma) {
+        hipError_t e = launch_temperature_order(a.temperature, a.B, ws.order, a.stream);
+        if (e != hipSuccess) return e;
+    }
     for (int k = 0; k < a.K; ++k) {
         const int32_t* prev = (k == 0) ? a.prev_token : a.tokens + (k - 1);
         const int prev_stride = (k == 0) ? 1 : a.K;
         if (mfma) {
-            hipError_t e = launch_draft_mfma_step(a, prev, prev_stride, k, part, n_strips);
+            hipError_t e = launch_draft_mfma_step(a, prev, prev_stride, k, ws.order, ws.part,
+                                                  n_strips);
             if (e != hipSuccess) return e;
         } else if (a.logit_dt == DSPARK_BF16 && a.factor_dt == DSPARK_BF16) {
-            launch_valu_strip<bf16_t, bf16_t>(a, prev, prev_stride, k, part, n_strips);
+            launch_valu_strip<bf16_t, bf16_t>(a, prev, prev_stride, k, ws.part, n_strips);
         } else if (a.logit_dt == DSPARK_BF16) {
-            launch_valu_strip<bf16_t, float>(a, prev, prev_stride, k, part, n_strips);
+            launch_valu_strip<bf16_t, float>(a, prev, prev_stride, k, ws.part, n_strips);
         } else if (a.factor_dt == DSPARK_BF16) {
-            launch_valu_strip<float, bf16_t>(a, prev, prev_stride, k, part, n_strips);
+            launch_valu_strip<float, bf16_t>(a, prev, prev_stride, k, ws.part, n_strips);
         } else {
-            launch_valu_strip<float, float>(a, prev, prev_stride, k, part, n_strips);
+            launch_valu_strip<float, float>(a, prev, prev_stride, k, ws.part, n_strips);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0,
-                           a.stream, part, n_strips, a.temperature, a.K, k, a.tokens, a.logp,
+        hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)), dim3(kCombineThreads), 0,
+                           a.stream, ws.part, n_strips, a.temperature, a.K, k, a.tokens, a.logp,
                            a.lse);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

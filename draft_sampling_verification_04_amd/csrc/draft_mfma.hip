@@ -1,17 +1,424 @@
-// draft_mfma.hip -- MFMA form of the draft strip kernel (bf16 factors).
+// draft_mfma.hip -- MFMA strip kernels for bf16 logits and factors (rank a
+// multiple of 16, V a multiple of 8): the Markov-head draft step and the
+// verification residual.
+//
+// Both need, per (request, vocabulary entry), the transition bias of the
+// previous token: bias^T[v, b] = sum_i W[i, v] A[x_prev[b], i].  It is a dense
+// contraction (M = V, N = requests, K = r), so it runs on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation and never leaves registers;
+// the epilogue consumes the accumulators directly.
+//
+// Workgroup = NWAVES wavefronts = one 128-entry vocabulary strip x 32*NWAVES
+// requests.  The strip of W (r x 128 bf16) is staged once in LDS and shared by
+// the waves; each wave owns 32 requests (one MFMA column tile) and all four
+// 32-row tiles of the strip.  Tile rows map to vocabulary entries so that each
+// lane's accumulators cover 64 consecutive entries of one request
+// (v = strip start + 64 * (lane / 32) + 4 * i + t for accumulator i of tile t):
+// the epilogue reduces in registers, one Philox block serves 4 consecutive
+// entries, and a lane's logits are 128 contiguous bytes.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dspark {
+namespace {
 
-bool mfma_supported(int r, dspark_dtype factor_dt) {
-    (void)r;
-    (void)factor_dt;
-    return false;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kStripV = kMfmaStrip;  // 128 vocabulary entries per strip
+constexpr int kPitch = kStripV + 8;  // LDS row pitch in bf16 elements (272 bytes)
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8, q); }
+__device__ __forceinline__ float bf_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
+    return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+// element e (0..63) of 64 bf16 values held as 8 x uint4
+__device__ __forceinline__ float bf_elem(const uint4 (&q)[8], int e) {
+    const uint32_t dw = dword_of(q[e >> 3], (e & 7) >> 1);
+    return (e & 1) ? bf_hi(dw) : bf_lo(dw);
 }
 
-hipError_t launch_draft_mfma_step(const DraftArgs&, const int32_t*, int, int, PartialBuf, int) {
-    return hipErrorNotSupported;
+// 64 bf16 logits of one row starting at entry v (row points at entry 0).
+// Chunks past the end of the row are read from its last chunk instead (V >= 8
+// and V % 8 == 0), so every load is in bounds and unconditional; callers mask
+// the entries past V.
+__device__ __forceinline__ void load64(uint4 (&q)[8], const uint16_t* row, int v, int V) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        q[i] = *reinterpret_cast<const uint4*>(row + min(v + 8 * i, V - 8));
+}
+
+// Stage W[0:r, v0:v0+128] in LDS.  V % 8 == 0, so each 16-byte chunk is either
+// inside the vocabulary or wholly past its end (then zero).
+template <int NT>
+__device__ __forceinline__ void stage_w(uint16_t* w_sh, const uint16_t* __restrict__ W, int r,
+                                        int V, int v0) {
+    for (int c = threadIdx.x; c < r * (kStripV / 8); c += NT) {
+        const int row = c >> 4;
+        const int cc = c & 15;
+        const int v = v0 + cc * 8;
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (v < V) val = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(row) * V + v);
+        *reinterpret_cast<uint4*>(w_sh + row * kPitch + cc * 8) = val;
+    }
+}
+
+// acc[t] = (W^T tile t of the strip) x (factor row arow); arow points at the
+// lane's 8-element rank slice (A row + 8 * (lane / 32)).
+__device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_sh,
+                                           const uint16_t* arow, int r, int lane) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    const int m = lane & 31;
+    const int colm = 64 * ((m >> 2) & 1) + 16 * (m >> 3) + 4 * (m & 3);
+    const uint16_t* wl = w_sh + (8 * (lane >> 5)) * kPitch + colm;
+    for (int kk = 0; kk < r / 16; ++kk) {
+        const uint4 bq = *reinterpret_cast<const uint4*>(arow + kk * 16);
+        uint2 d[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            d[j] = *reinterpret_cast<const uint2*>(wl + (kk * 16 + j) * kPitch);
+        // 8 rank rows x 4 entries -> four vectors of 8 rank values
+        uint4 a0, a1, a2, a3;
+        a0.x = __builtin_amdgcn_perm(d[1].x, d[0].x, 0x05040100u);
+        a0.y = __builtin_amdgcn_perm(d[3].x, d[2].x, 0x05040100u);
+        a0.z = __builtin_amdgcn_perm(d[5].x, d[4].x, 0x05040100u);
+        a0.w = __builtin_amdgcn_perm(d[7].x, d[6].x, 0x05040100u);
+        a1.x = __builtin_amdgcn_perm(d[1].x, d[0].x, 0x07060302u);
+        a1.y = __builtin_amdgcn_perm(d[3].x, d[2].x, 0x07060302u);
+        a1.z = __builtin_amdgcn_perm(d[5].x, d[4].x, 0x07060302u);
+        a1.w = __builtin_amdgcn_perm(d[7].x, d[6].x, 0x07060302u);
+        a2.x = __builtin_amdgcn_perm(d[1].y, d[0].y, 0x05040100u);
+        a2.y = __builtin_amdgcn_perm(d[3].y, d[2].y, 0x05040100u);
+        a2.z = __builtin_amdgcn_perm(d[5].y, d[4].y, 0x05040100u);
+        a2.w = __builtin_amdgcn_perm(d[7].y, d[6].y, 0x05040100u);
+        a3.x = __builtin_amdgcn_perm(d[1].y, d[0].y, 0x07060302u);
+        a3.y = __builtin_amdgcn_perm(d[3].y, d[2].y, 0x07060302u);
+        a3.z = __builtin_amdgcn_perm(d[5].y, d[4].y, 0x07060302u);
+        a3.w = __builtin_amdgcn_perm(d[7].y, d[6].y, 0x07060302u);
+        const bf16x8 bv = as_bf16x8(bq);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bv, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bv, acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a2), bv, acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a3), bv, acc[3], 0, 0, 0);
+    }
+}
+
+// ------------------------------------------------------------------ draft
+template <int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(4)))
+void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
+                      const uint16_t* __restrict__ W, const int32_t* __restrict__ prev,
+                      int prev_stride, const float* __restrict__ temperature,
+                      const int32_t* __restrict__ order, uint64_t seed, int B, int K, int V,
+                      int r, int k, PartialBuf part, int n_strips) {
+    extern __shared__ uint16_t w_sh[];  // [r][kPitch]
+    const int lane = threadIdx.x & 63;
+    const int kh = lane >> 5;
+    const int strip = blockIdx.x;
+    const int v0 = strip * kStripV;
+    const int slot = (blockIdx.y * NWAVES + (threadIdx.x >> 6)) * 32 + (lane & 31);
+    const bool active = slot < B;
+    const int b = active ? order[slot] : 0;
+    stage_w<64 * NWAVES>(w_sh, W, r, V, v0);
+    const int p = active ? clamp_token(prev[static_cast<size_t>(b) * prev_stride], V) : 0;
+    __syncthreads();
+
+    f32x16 acc[4];
+    bias_tiles(acc, w_sh, A + static_cast<size_t>(p) * r + 8 * kh, r, lane);
+    if (!active) return;
+
+    const int vl = v0 + 64 * kh;  // entry e = 4 i + t of this lane is v = vl + e
+    uint4 bl[8];
+    load64(bl, base + (static_cast<size_t>(b) * K + k) * V, vl, V);
+    const bool full = vl + 64 <= V;
+    const float T = temperature[b];
+    const bool greedy = !(T > 0.0f);
+    const float it = greedy ? 1.0f : inv_temperature(T);
+    // The accumulators become the draft logits z = (base + bias) / T (for
+    // T == 0 the unscaled s = base + bias).  Entries past V become -inf.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int e = 4 * i + t;
+            float zz = (bf_elem(bl, e) + acc[t][i]) * it;
+            if (!full && vl + e >= V) zz = -INFINITY;
+            acc[t][i] = zz;
+            mx = fmaxf(mx, zz);
+        }
+    }
+    RowState st = row_empty();
+    float best = -INFINITY, bz = -INFINITY;
+    int bi = 0x7fffffff;
+    if (!greedy) {
+        const float mc = mx * kLog2e;
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], kLog2e, -mc));
+        st.m = mx;
+        st.s = sum;
+        // Gumbel-max; entries are visited in increasing v, so a tie never
+        // replaces the earlier (smaller) index.
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const u32x4 rnd = philox_block(seed, b, k + 1, kTagDraft, (vl + 4 * i) >> 2);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float pv = acc[t][i] + gumbel_fast(pick(rnd, t));
+                if (pv > best) {
+                    best = pv;
+                    bz = acc[t][i];
+                    bi = vl + 4 * i + t;
+                }
+            }
+            // one Philox block at a time keeps the register footprint small
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (acc[t][i] > best) {
+                    best = acc[t][i];
+                    bz = best;
+                    bi = vl + 4 * i + t;
+                }
+            }
+        }
+    }
+    st.pert = best;
+    st.zb = bz;
+    st.idx = bi;
+    // lanes l and l + 32 hold the two halves of the strip for one request
+    row_merge(st, shfl_xor_row(st, 32));
+    if (kh == 0) store_partial(part, static_cast<size_t>(b) * n_strips + strip, st);
+}
+
+// --------------------------------------------------------------- residual
+// For every request whose first rejection is at j* = a_b + 1 (sampled, T > 0):
+// recompute the draft logits z at j* (previous token x_{j*-1}), read the target
+// row y = t / T, and draw next ~ normalise(max(0, p_t - p_d)) by Gumbel-max of
+// log(p_t - p_d) over the positive entries (tag 2, position j*).  The Gumbel-max
+// of y with the same draws is kept as the fallback for a residual without
+// positive mass.  Rejected requests are listed in `list` (count entries).
+template <int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
+                         const uint16_t* __restrict__ W, const uint16_t* __restrict__ target,
+                         const int64_t* __restrict__ row_off, const int32_t* __restrict__ tokens,
+                         const int32_t* __restrict__ prev_token,
+                         const float* __restrict__ draft_lse, const float* __restrict__ temperature,
+                         const int32_t* __restrict__ accepted, const int32_t* __restrict__ list,
+                         const int32_t* __restrict__ count_ptr, const float* __restrict__ lse_tab,
+                         uint64_t seed, int K, int V, int r, PartialBuf res, PartialBuf fall,
+                         int n_strips) {
+    extern __shared__ uint16_t w_sh[];
+    const int count = *count_ptr;
+    const int slot0 = blockIdx.y * NWAVES * 32;
+    if (slot0 >= count) return;  // whole workgroup idle
+    const int lane = threadIdx.x & 63;
+    const int kh = lane >> 5;
+    const int strip = blockIdx.x;
+    const int v0 = strip * kStripV;
+    const int slot = slot0 + (threadIdx.x >> 6) * 32 + (lane & 31);
+    const bool active = slot < count;
+    const int b = active ? list[slot] : 0;
+    const int js = active ? accepted[b] + 1 : 1;
+    stage_w<64 * NWAVES>(w_sh, W, r, V, v0);
+    const int p = active ? clamp_token((js == 1) ? prev_token[b]
+                                                 : tokens[static_cast<size_t>(b) * K + js - 2],
+                                       V)
+                         : 0;
+    __syncthreads();
+
+    f32x16 acc[4];
+    bias_tiles(acc, w_sh, A + static_cast<size_t>(p) * r + 8 * kh, r, lane);
+    if (!active) return;
+
+    const int vl = v0 + 64 * kh;
+    uint4 bl[8], tl[8];
+    load64(bl, base + (static_cast<size_t>(b) * K + js - 1) * V, vl, V);
+    load64(tl, target + (row_off[b] + js - 1) * static_cast<int64_t>(V), vl, V);
+    const float it = inv_temperature(temperature[b]);
+    const float lse_d = draft_lse[static_cast<size_t>(b) * K + js - 1];
+    const float lse_t = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1];
+    float br = -INFINITY, bf = -INFINITY;
+    int ir = 0x7fffffff, jf = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vl + 4 * i) >> 2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int e = 4 * i + t;
+            if (vl + e >= V) continue;
+            const float z = (bf_elem(bl, e) + acc[t][i]) * it;
+            const float y = bf_elem(tl, e) * it;
+            const float g = gumbel_fast(pick(rnd, t));
+            const float rv = expf(y - lse_t) - expf(z - lse_d);
+            if (rv > 0.0f) {
+                const float pr = logf(rv) + g;
+                if (pr > br) {
+                    br = pr;
+                    ir = vl + e;
+                }
+            }
+            const float pf = y + g;
+            if (pf > bf) {
+                bf = pf;
+                jf = vl + e;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    RowState sr = {-INFINITY, 0.0f, br, br, ir};
+    RowState sf = {-INFINITY, 0.0f, bf, bf, jf};
+    row_merge(sr, shfl_xor_row(sr, 32));
+    row_merge(sf, shfl_xor_row(sf, 32));
+    if (kh == 0) {
+        store_partial(res, static_cast<size_t>(slot) * n_strips + strip, sr);
+        store_partial(fall, static_cast<size_t>(slot) * n_strips + strip, sf);
+    }
+}
+
+// ------------------------------------------------------------ visit order
+// Requests are visited greedy (T == 0) first, then sampled, each group in
+// request order, so a wavefront rarely mixes the two epilogues.  One workgroup.
+__global__ __launch_bounds__(1024) void temperature_order(const float* __restrict__ temperature,
+                                                          int B, int32_t* __restrict__ order) {
+    __shared__ int sh[1024 / kWave];
+    __shared__ int sh_total;
+    const int tid = threadIdx.x;
+    int local = 0;
+    for (int b = tid; b < B; b += 1024) local += !(temperature[b] > 0.0f);
+    for (int msk = 32; msk >= 1; msk >>= 1) local += __shfl_xor(local, msk, kWave);
+    if ((tid & 63) == 0) sh[tid >> 6] = local;
+    __syncthreads();
+    if (tid == 0) {
+        int t = 0;
+        for (int w = 0; w < 1024 / kWave; ++w) t += sh[w];
+        sh_total = t;
+    }
+    __syncthreads();
+    const int n_greedy = sh_total;
+    int off_g = 0, off_s = n_greedy;
+    for (int c0 = 0; c0 < B; c0 += 1024) {
+        const int b = c0 + tid;
+        const int g = (b < B) && !(temperature[b] > 0.0f);
+        const int s = (b < B) && !g;
+        int ig = g, is = s;
+        const int lane = tid & 63;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int og = __shfl_up(ig, d, kWave);
+            const int os = __shfl_up(is, d, kWave);
+            if (lane >= d) {
+                ig += og;
+                is += os;
+            }
+        }
+        __syncthreads();
+        if (lane == 63) sh[tid >> 6] = ig | (is << 16);
+        __syncthreads();
+        int bg = 0, bs = 0, tg = 0, ts = 0;
+        for (int w = 0; w < 1024 / kWave; ++w) {
+            const int vg = sh[w] & 0xFFFF, vs = sh[w] >> 16;
+            if (w < (tid >> 6)) {
+                bg += vg;
+                bs += vs;
+            }
+            tg += vg;
+            ts += vs;
+        }
+        if (g) order[off_g + bg + ig - 1] = b;
+        if (s) order[off_s + bs + is - 1] = b;
+        off_g += tg;
+        off_s += ts;
+    }
+}
+
+constexpr int kMaxLds = 160 * 1024;
+
+template <typename Kern>
+hipError_t allow_big_lds(Kern* kern, bool& done) {
+    if (done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
+template <int NWAVES>
+hipError_t launch_draft_strip(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
+                              const int32_t* order, PartialBuf part, int n_strips) {
+    static bool lds_ok = false;
+    hipError_t e = allow_big_lds(&draft_strip_mfma<NWAVES>, lds_ok);
+    if (e != hipSuccess) return e;
+    const size_t lds = sizeof(uint16_t) * static_cast<size_t>(a.r) * kPitch;
+    dim3 grid(static_cast<unsigned>(n_strips), static_cast<unsigned>(ceil_div(a.B, 32 * NWAVES)));
+    hipLaunchKernelGGL(draft_strip_mfma<NWAVES>, grid, dim3(64 * NWAVES), lds, a.stream,
+                       static_cast<const uint16_t*>(a.base), static_cast<const uint16_t*>(a.A),
+                       static_cast<const uint16_t*>(a.W), prev, prev_stride, a.temperature, order,
+                       a.seed, a.B, a.K, a.V, a.r, k, part, n_strips);
+    return hipGetLastError();
+}
+
+template <int NWAVES>
+hipError_t launch_residual_strip(const ResidualArgs& a) {
+    static bool lds_ok = false;
+    hipError_t e = allow_big_lds(&residual_strip_mfma<NWAVES>, lds_ok);
+    if (e != hipSuccess) return e;
+    const VerifyArgs& v = *a.v;
+    const size_t lds = sizeof(uint16_t) * static_cast<size_t>(v.r) * kPitch;
+    dim3 grid(static_cast<unsigned>(a.n_strips), static_cast<unsigned>(ceil_div(v.B, 32 * NWAVES)));
+    hipLaunchKernelGGL(residual_strip_mfma<NWAVES>, grid, dim3(64 * NWAVES), lds, v.stream,
+                       static_cast<const uint16_t*>(v.base), static_cast<const uint16_t*>(v.A),
+                       static_cast<const uint16_t*>(v.W), static_cast<const uint16_t*>(v.target),
+                       v.row_off, v.tokens, v.prev_token, v.draft_lse, v.temperature, v.accepted,
+                       a.list, a.count, a.lse_tab, v.seed, v.K, v.V, v.r, a.res, a.fall,
+                       a.n_strips);
+    return hipGetLastError();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool mfma_supported(const DraftArgs& a) {
+    return a.factor_dt == DSPARK_BF16 && a.logit_dt == DSPARK_BF16 && a.r % 16 == 0 &&
+           a.r <= 512 && a.V % 8 == 0 && aligned16(a.base) && aligned16(a.A) && aligned16(a.W);
+}
+
+bool residual_mfma_supported(const VerifyArgs& a) {
+    return a.factor_dt == DSPARK_BF16 && a.logit_dt == DSPARK_BF16 && a.r % 16 == 0 &&
+           a.r <= 512 && a.V % 8 == 0 && aligned16(a.base) && aligned16(a.A) &&
+           aligned16(a.W) && aligned16(a.target);
+}
+
+hipError_t launch_temperature_order(const float* temperature, int B, int32_t* order,
+                                    hipStream_t stream) {
+    hipLaunchKernelGGL(temperature_order, dim3(1), dim3(1024), 0, stream, temperature, B, order);
+    return hipGetLastError();
+}
+
+hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
+                                  const int32_t* order, PartialBuf part, int n_strips) {
+    if (a.B > 128) return launch_draft_strip<8>(a, prev, prev_stride, k, order, part, n_strips);
+    if (a.B > 64) return launch_draft_strip<4>(a, prev, prev_stride, k, order, part, n_strips);
+    return launch_draft_strip<2>(a, prev, prev_stride, k, order, part, n_strips);
+}
+
+hipError_t launch_residual_mfma(const ResidualArgs& a) {
+    if (a.v->B > 128) return launch_residual_strip<8>(a);
+    if (a.v->B > 64) return launch_residual_strip<4>(a);
+    return launch_residual_strip<2>(a);
 }
 
 }  // namespace dspark

@@ -13,6 +13,13 @@ namespace dspark {
 constexpr int kValuStrip = 1024;  // 256 threads x 4 entries
 constexpr int kMfmaStrip = 128;   // 4 MFMA row tiles of 32
 
+// Stored per-strip reduction partials: (max, sum, perturbed best, logit at the
+// best) as float4 plus the best index.
+struct PartialBuf {
+    float4* v;
+    int32_t* idx;
+};
+
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -65,6 +72,19 @@ struct VerifyArgs {
 };
 
 size_t verify_workspace_bytes(int B, int K, int V, int r);
+
+// Residual draw for the rejected sampled requests (MFMA path).
+struct ResidualArgs {
+    const VerifyArgs* v;
+    const int32_t* list;   // rejected requests
+    const int32_t* count;  // device count of list entries
+    const float* lse_tab;  // [B][K+1] target log-normalisers
+    PartialBuf res;
+    PartialBuf fall;
+    int n_strips;
+};
+bool residual_mfma_supported(const VerifyArgs& a);
+hipError_t launch_residual_mfma(const ResidualArgs& a);
 hipError_t launch_verify(const VerifyArgs& a);
 
 constexpr int kMaxCurvePoints = 64;

@@ -11,11 +11,12 @@
 //   j* = a_b + 1 (Gumbel-max over log of the positive residual, falling back to
 //   p_t when no residual mass is left);  a_b = L_b: next ~ p_t of row L_b + 1.
 //
-// Launches: (1) one workgroup per (request, row) streams the target row once:
-// log-normaliser, accept bit, argmax, and the bonus Gumbel-max on row L_b + 1;
-// (2) one thread per request finds the first rejection; (3) rejected sampled
-// requests recompute their draft row at j* (rank-r bias + base) and stream the
-// target row again for the residual Gumbel-max, split in vocabulary strips;
+// Launches: (1) one workgroup per (request, row) streams the target row once
+// with 16-byte loads: log-normaliser, accept bit, argmax, and the bonus
+// Gumbel-max on row L_b + 1; (2) one thread per request finds the first
+// rejection and lists the requests that need a residual draw; (3) the listed
+// requests recompute their draft row at j* (rank-r bias on MFMA for bf16, VALU
+// otherwise) and stream the target row j* again, split in vocabulary strips;
 // (4) the strips are folded into the next token.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -24,7 +25,7 @@ namespace dspark {
 namespace {
 
 constexpr int kRowThreads = 256;
-constexpr int kResRows = 8;  // rejected requests per workgroup of the residual kernel
+constexpr int kResRows = 8;  // rejected requests per workgroup of the VALU residual kernel
 
 struct VerifyWs {
     int32_t* accept;  // [B][K+1]
@@ -37,13 +38,40 @@ struct VerifyWs {
     PartialBuf fall;  // [B][n_strips] fallback (p_t) Gumbel-max partials
 };
 
-__device__ __forceinline__ void block_reduce_row(RowState& st, RowState* red /* [4] */) {
-    wave_reduce_row(st);
-    const int tid = threadIdx.x;
-    if ((tid & 63) == 0) red[tid >> 6] = st;
-    __syncthreads();
-    if (tid == 0) {
-        for (int w = 1; w < kRowThreads / kWave; ++w) row_merge(st, red[w]);
+// Eight consecutive logits of a row as floats; `vec` = the row is 16-byte
+// aligned and V is a multiple of the vector width, so a chunk starting below V
+// is whole.  Entries past V read as -inf.
+template <typename LT>
+__device__ __forceinline__ void load8(const LT* row, int v0, int V, bool vec, float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* row, int v0, int V, bool vec,
+                                              float (&x)[8]) {
+    if (vec) {
+        const uint4 q = *reinterpret_cast<const uint4*>(row + v0);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (v0 + i < V) ? to_f32(row[v0 + i]) : -INFINITY;
+    }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* row, int v0, int V, bool vec,
+                                             float (&x)[8]) {
+    if (vec) {
+        const float4 a = *reinterpret_cast<const float4*>(row + v0);
+        const float4 b = *reinterpret_cast<const float4*>(row + v0 + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (v0 + i < V) ? row[v0 + i] : -INFINITY;
     }
 }
 
@@ -52,8 +80,8 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows(
     const LT* __restrict__ target, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ lengths, const int32_t* __restrict__ tokens,
     const float* __restrict__ draft_logp, const float* __restrict__ temperature, uint64_t seed,
-    int K, int V, int64_t n_rows, float* __restrict__ row_lse_t, float* __restrict__ row_logratio,
-    VerifyWs ws) {
+    int K, int V, int64_t n_rows, bool vec_ok, float* __restrict__ row_lse_t,
+    float* __restrict__ row_logratio, VerifyWs ws) {
     __shared__ RowState red[kRowThreads / kWave];
     const int64_t id = blockIdx.x;
     const int b = static_cast<int>(id / (K + 1));
@@ -64,50 +92,71 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows(
     const int64_t row = row_off[b] + (j - 1);
     const float T = temperature[b];
     const bool greedy = !(T > 0.0f);
-    const float it = greedy ? 1.0f : inv_temperature(T);
     const bool bonus = (j == L + 1);
     const LT* trow = target + row * static_cast<int64_t>(V);
+    const bool vec = vec_ok && (V % 8 == 0);
     RowState st = row_empty();
-    for (int v0 = threadIdx.x * 4; v0 < V; v0 += kRowThreads * 4) {
-        float y[4];
+    if (greedy) {
+        // argmax of t, smallest index on ties (visited in increasing v per thread)
+        float best = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int v0 = threadIdx.x * 8; v0 < V; v0 += kRowThreads * 8) {
+            float x[8];
+            load8<LT>(trow, v0, V, vec, x);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) y[t] = (v0 + t < V) ? to_f32(trow[v0 + t]) * it : -INFINITY;
-        if (!greedy) {
-            float m = st.m;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) m = fmaxf(m, y[t]);
-            float sum = (st.m == -INFINITY) ? 0.0f : st.s * expf(st.m - m);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (v0 + t < V) sum += expf(y[t] - m);
-            st.m = m;
-            st.s = sum;
-            if (bonus) {
-                const u32x4 rnd = philox_block(seed, b, j, kTagResample, v0 >> 2);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if (v0 + t < V) {
-                        const float p = y[t] + gumbel_of(pick(rnd, t));
-                        if (beats(p, v0 + t, st.pert, st.idx)) {
-                            st.pert = p;
-                            st.zb = y[t];
-                            st.idx = v0 + t;
-                        }
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (v0 + t < V && beats(y[t], v0 + t, st.pert, st.idx)) {
-                    st.pert = y[t];
-                    st.zb = y[t];
-                    st.idx = v0 + t;
+            for (int e = 0; e < 8; ++e) {
+                if (x[e] > best) {
+                    best = x[e];
+                    bi = v0 + e;
                 }
             }
         }
+        st.pert = best;
+        st.zb = best;
+        st.idx = bi;
+    } else {
+        // log sum_v exp(t_v / T) around the running maximum m of t:
+        // s = sum 2^((t - m) c) with c = log2(e) / T
+        const float it = inv_temperature(T);
+        const float c = it * kLog2e;
+        float m = -INFINITY, s = 0.0f;
+        float best = -INFINITY, bz = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int v0 = threadIdx.x * 8; v0 < V; v0 += kRowThreads * 8) {
+            float x[8];
+            load8<LT>(trow, v0, V, vec, x);
+            float cm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            if (cm > m) {
+                s *= __builtin_amdgcn_exp2f((m - cm) * c);
+                m = cm;
+            }
+            const float mc = m * c;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
+            if (bonus) {
+                const u32x4 r0 = philox_block(seed, b, j, kTagResample, v0 >> 2);
+                const u32x4 r1 = philox_block(seed, b, j, kTagResample, (v0 >> 2) + 1);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float y = x[e] * it;
+                    const float pv = y + gumbel_fast(pick(e < 4 ? r0 : r1, e & 3));
+                    if (pv > best) {
+                        best = pv;
+                        bz = y;
+                        bi = v0 + e;
+                    }
+                }
+            }
+        }
+        // express (m, s) on the y = t / T scale for the shared merge
+        st.m = m * it;
+        st.s = s;
+        st.pert = best;
+        st.zb = bz;
+        st.idx = bi;
     }
-    block_reduce_row(st, red);
+    st = block_reduce_row<kRowThreads>(st, red);
     if (threadIdx.x == 0) {
         const size_t slot = static_cast<size_t>(b) * (K + 1) + (j - 1);
         const float lse_t = greedy ? st.pert : st.m + logf(st.s);
@@ -121,7 +170,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows(
             int acc;
             float ratio;
             if (!greedy) {
-                const float yx = to_f32(trow[x]) * it;
+                const float yx = to_f32(trow[x]) * inv_temperature(T);
                 ratio = (yx - lse_t) - draft_logp[static_cast<size_t>(b) * K + (j - 1)];
                 const u32x4 rnd = philox_block(seed, b, j, kTagAccept, 0);
                 acc = logf(uniform_of(rnd.x)) < ratio;
@@ -169,10 +218,8 @@ __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_ro
     }
 }
 
-// Residual strip kernel (VALU form): workgroup = (8 rejected requests) x (1024
-// vocabulary entries).  Recomputes the draft row at j* = a_b + 1 and streams the
-// target row j*: r_v = max(0, p_t - p_d), Gumbel-max of log r_v (tag 2, position
-// j*); in parallel the fallback Gumbel-max of y (same draws).
+// Residual strip kernel, VALU form (fp32 inputs, or shapes the MFMA form does
+// not take): workgroup = (8 rejected requests) x (1024 vocabulary entries).
 template <typename LT, typename FT>
 __global__ __launch_bounds__(256) void verify_residual_valu(
     const LT* __restrict__ base, const FT* __restrict__ A, const FT* __restrict__ W,
@@ -283,20 +330,22 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
     }
 }
 
-__global__ __launch_bounds__(64) void verify_residual_combine(VerifyWs ws, int n_strips,
-                                                             int32_t* __restrict__ next_token) {
+// Fold the residual strips of each listed request into its next token.
+__global__ __launch_bounds__(kRowThreads) void verify_residual_combine(
+    VerifyWs ws, int n_strips, int32_t* __restrict__ next_token) {
+    __shared__ RowState red[kRowThreads / kWave];
     const int slot = blockIdx.x;
     if (slot >= *ws.count) return;
-    const int lane = threadIdx.x;
     RowState sr = row_empty();
     RowState sf = row_empty();
-    for (int s = lane; s < n_strips; s += kWave) {
+    for (int s = threadIdx.x; s < n_strips; s += kRowThreads) {
         row_merge(sr, load_partial(ws.res, static_cast<size_t>(slot) * n_strips + s));
         row_merge(sf, load_partial(ws.fall, static_cast<size_t>(slot) * n_strips + s));
     }
-    wave_reduce_row(sr);
-    wave_reduce_row(sf);
-    if (lane == 0) {
+    sr = block_reduce_row<kRowThreads>(sr, red);
+    __syncthreads();
+    sf = block_reduce_row<kRowThreads>(sf, red);
+    if (threadIdx.x == 0) {
         const int b = ws.list[slot];
         next_token[b] = (sr.pert > -INFINITY) ? sr.idx : sf.idx;
     }
@@ -336,6 +385,8 @@ void launch_residual_valu(const VerifyArgs& a, const VerifyWs& ws, int n_strips)
                        a.V, a.r, ws, n_strips);
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 }  // namespace
 
 size_t verify_workspace_bytes(int B, int K, int V, int r) {
@@ -359,38 +410,47 @@ hipError_t launch_verify(const VerifyArgs& a) {
 
     hipLaunchKernelGGL(fill_i32, dim3(1), dim3(64), 0, a.stream, ws.count, 1, 0);
     const dim3 rows_grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * (a.K + 1)));
+    const bool vec_ok = aligned16(a.target);
     if (a.logit_dt == DSPARK_BF16) {
         hipLaunchKernelGGL(verify_rows<bf16_t>, rows_grid, dim3(kRowThreads), 0, a.stream,
                            static_cast<const bf16_t*>(a.target), a.row_off, a.lengths, a.tokens,
-                           a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, a.row_lse_t,
-                           a.row_logratio, ws);
+                           a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
+                           a.row_lse_t, a.row_logratio, ws);
     } else {
         hipLaunchKernelGGL(verify_rows<float>, rows_grid, dim3(kRowThreads), 0, a.stream,
                            static_cast<const float*>(a.target), a.row_off, a.lengths, a.tokens,
-                           a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, a.row_lse_t,
-                           a.row_logratio, ws);
+                           a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
+                           a.row_lse_t, a.row_logratio, ws);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(verify_resolve, dim3(static_cast<unsigned>(ceil_div(a.B, 256))), dim3(256),
                        0, a.stream, a.B, a.K, a.n_rows, a.row_off, a.lengths, a.temperature, ws,
-                       a.accepted,
-                       a.next_token);
+                       a.accepted, a.next_token);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_strips = static_cast<int>(ceil_div(a.V, kValuStrip));
-    if (a.logit_dt == DSPARK_BF16 && a.factor_dt == DSPARK_BF16)
-        launch_residual_valu<bf16_t, bf16_t>(a, ws, n_strips);
-    else if (a.logit_dt == DSPARK_BF16)
-        launch_residual_valu<bf16_t, float>(a, ws, n_strips);
-    else if (a.factor_dt == DSPARK_BF16)
-        launch_residual_valu<float, bf16_t>(a, ws, n_strips);
-    else
-        launch_residual_valu<float, float>(a, ws, n_strips);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(verify_residual_combine, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0,
-                       a.stream, ws, n_strips, a.next_token);
+    if (a.K == 0) return hipSuccess;  // no draft rows: every next token is a bonus draw
+    int n_strips;
+    if (residual_mfma_supported(a)) {
+        n_strips = static_cast<int>(ceil_div(a.V, kMfmaStrip));
+        ResidualArgs ra{&a, ws.list, ws.count, ws.lse, ws.res, ws.fall, n_strips};
+        e = launch_residual_mfma(ra);
+        if (e != hipSuccess) return e;
+    } else {
+        n_strips = static_cast<int>(ceil_div(a.V, kValuStrip));
+        if (a.logit_dt == DSPARK_BF16 && a.factor_dt == DSPARK_BF16)
+            launch_residual_valu<bf16_t, bf16_t>(a, ws, n_strips);
+        else if (a.logit_dt == DSPARK_BF16)
+            launch_residual_valu<bf16_t, float>(a, ws, n_strips);
+        else if (a.factor_dt == DSPARK_BF16)
+            launch_residual_valu<float, bf16_t>(a, ws, n_strips);
+        else
+            launch_residual_valu<float, float>(a, ws, n_strips);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(verify_residual_combine, dim3(static_cast<unsigned>(a.B)),
+                       dim3(kRowThreads), 0, a.stream, ws, n_strips, a.next_token);
     return hipGetLastError();
 }
 
