@@ -11,11 +11,14 @@
 // Workgroup = NWAVES wavefronts = one 128-entry vocabulary strip x 32*NWAVES
 // requests.  The strip of W (r x 128 bf16) is staged once in LDS and shared by
 // the waves; each wave owns 32 requests (one MFMA column tile) and all four
-// 32-row tiles of the strip.  Tile rows map to vocabulary entries so that each
-// lane's accumulators cover 64 consecutive entries of one request
-// (v = strip start + 64 * (lane / 32) + 4 * i + t for accumulator i of tile t):
-// the epilogue reduces in registers, one Philox block serves 4 consecutive
-// entries, and a lane's logits are 128 contiguous bytes.
+// 32-row tiles of the strip.  Row m of tile t is entry v = strip start + 4 m + t:
+//   - an A-operand lane (row m) reads 4 consecutive entries of 8 rank rows
+//     with one 8-byte LDS read per row, and the 16 lanes of an LDS pass read
+//     128 consecutive bytes (no bank conflicts);
+//   - output lane l holds rows 8 (i / 4) + 4 (l / 32) + i % 4 of every tile, so
+//     its accumulator i covers the 4 consecutive entries
+//     v = start + 32 (i / 4) + 16 (l / 32) + 4 (i % 4) + t, t = 0..3: exactly
+//     one Philox block, and the lane's 64 entries are four runs of 16.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,25 +32,43 @@ constexpr int kStripV = kMfmaStrip;  // 128 vocabulary entries per strip
 constexpr int kPitch = kStripV + 8;  // LDS row pitch in bf16 elements (272 bytes)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8, q); }
-__device__ __forceinline__ float bf_lo(uint32_t d) { return __uint_as_float(d << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 __device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
     return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
 }
-// element e (0..63) of 64 bf16 values held as 8 x uint4
-__device__ __forceinline__ float bf_elem(const uint4 (&q)[8], int e) {
-    const uint32_t dw = dword_of(q[e >> 3], (e & 7) >> 1);
-    return (e & 1) ? bf_hi(dw) : bf_lo(dw);
+
+// Entry offset of accumulator i, tile t within a lane's strip half.
+__device__ __forceinline__ constexpr int entry_of(int i, int t) {
+    return 32 * (i >> 2) + 4 * (i & 3) + t;
 }
 
-// 64 bf16 logits of one row starting at entry v (row points at entry 0).
-// Chunks past the end of the row are read from its last chunk instead (V >= 8
-// and V % 8 == 0), so every load is in bounds and unconditional; callers mask
-// the entries past V.
-__device__ __forceinline__ void load64(uint4 (&q)[8], const uint16_t* row, int v, int V) {
+// The lane's 64 bf16 logits of one row: runs a = 0..3 of 16 entries at
+// row[vh + 32 a], two 16-byte loads each.  Every load is in bounds and
+// unconditional (chunks past the end of the row are read from its last chunk;
+// V % 8 == 0, V >= 8).  In a strip that crosses V (tail != 0) those chunks are
+// then replaced by bf16 -inf, so entries past V carry the logit -inf and need
+// no mask downstream.
+__device__ __forceinline__ void load_lane_logits(uint4 (&q)[8], const uint16_t* row, int vh,
+                                                 int V, bool tail) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        q[i] = *reinterpret_cast<const uint4*>(row + min(v + 8 * i, V - 8));
+    for (int c = 0; c < 8; ++c) {
+        const int v = vh + 32 * (c >> 1) + 8 * (c & 1);
+        q[c] = *reinterpret_cast<const uint4*>(row + min(v, V - 8));
+    }
+    if (tail) {
+        const uint32_t ninf2 = 0xFF80FF80u;  // two bf16 -inf
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int v = vh + 32 * (c >> 1) + 8 * (c & 1);
+            if (v >= V) q[c] = make_uint4(ninf2, ninf2, ninf2, ninf2);
+        }
+    }
+}
+
+// Logit of accumulator i, tile t from load_lane_logits' registers.
+__device__ __forceinline__ float logit_at(const uint4 (&q)[8], int i, int t) {
+    const int o = 4 * (i & 3) + t;  // offset inside the 16-entry run i / 4
+    const uint32_t dw = dword_of(q[2 * (i >> 2) + (o >> 3)], (o & 7) >> 1);
+    return __uint_as_float((o & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
 }
 
 // Stage W[0:r, v0:v0+128] in LDS.  V % 8 == 0, so each 16-byte chunk is either
@@ -66,51 +87,130 @@ __device__ __forceinline__ void stage_w(uint16_t* w_sh, const uint16_t* __restri
 }
 
 // acc[t] = (W^T tile t of the strip) x (factor row arow); arow points at the
-// lane's 8-element rank slice (A row + 8 * (lane / 32)).
+// lane's 8-element rank slice (A row + 8 * (lane / 32)).  The factor fragment of
+// the next rank step is fetched one step ahead.
 __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_sh,
                                            const uint16_t* arow, int r, int lane) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
-    const int m = lane & 31;
-    const int colm = 64 * ((m >> 2) & 1) + 16 * (m >> 3) + 4 * (m & 3);
-    const uint16_t* wl = w_sh + (8 * (lane >> 5)) * kPitch + colm;
-    for (int kk = 0; kk < r / 16; ++kk) {
-        const uint4 bq = *reinterpret_cast<const uint4*>(arow + kk * 16);
+    const uint16_t* wl = w_sh + (8 * (lane >> 5)) * kPitch + 4 * (lane & 31);
+    const int ksteps = r / 16;
+    uint4 bq = *reinterpret_cast<const uint4*>(arow);
+    for (int kk = 0; kk < ksteps; ++kk) {
+        const uint4 bq_next =
+            *reinterpret_cast<const uint4*>(arow + 16 * min(kk + 1, ksteps - 1));
         uint2 d[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             d[j] = *reinterpret_cast<const uint2*>(wl + (kk * 16 + j) * kPitch);
         // 8 rank rows x 4 entries -> four vectors of 8 rank values
-        uint4 a0, a1, a2, a3;
-        a0.x = __builtin_amdgcn_perm(d[1].x, d[0].x, 0x05040100u);
-        a0.y = __builtin_amdgcn_perm(d[3].x, d[2].x, 0x05040100u);
-        a0.z = __builtin_amdgcn_perm(d[5].x, d[4].x, 0x05040100u);
-        a0.w = __builtin_amdgcn_perm(d[7].x, d[6].x, 0x05040100u);
-        a1.x = __builtin_amdgcn_perm(d[1].x, d[0].x, 0x07060302u);
-        a1.y = __builtin_amdgcn_perm(d[3].x, d[2].x, 0x07060302u);
-        a1.z = __builtin_amdgcn_perm(d[5].x, d[4].x, 0x07060302u);
-        a1.w = __builtin_amdgcn_perm(d[7].x, d[6].x, 0x07060302u);
-        a2.x = __builtin_amdgcn_perm(d[1].y, d[0].y, 0x05040100u);
-        a2.y = __builtin_amdgcn_perm(d[3].y, d[2].y, 0x05040100u);
-        a2.z = __builtin_amdgcn_perm(d[5].y, d[4].y, 0x05040100u);
-        a2.w = __builtin_amdgcn_perm(d[7].y, d[6].y, 0x05040100u);
-        a3.x = __builtin_amdgcn_perm(d[1].y, d[0].y, 0x07060302u);
-        a3.y = __builtin_amdgcn_perm(d[3].y, d[2].y, 0x07060302u);
-        a3.z = __builtin_amdgcn_perm(d[5].y, d[4].y, 0x07060302u);
-        a3.w = __builtin_amdgcn_perm(d[7].y, d[6].y, 0x07060302u);
         const bf16x8 bv = as_bf16x8(bq);
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), bv, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), bv, acc[1], 0, 0, 0);
-        acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a2), bv, acc[2], 0, 0, 0);
-        acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a3), bv, acc[3], 0, 0, 0);
+        uint4 a;
+        a = make_uint4(__builtin_amdgcn_perm(d[1].x, d[0].x, 0x05040100u),
+                       __builtin_amdgcn_perm(d[3].x, d[2].x, 0x05040100u),
+                       __builtin_amdgcn_perm(d[5].x, d[4].x, 0x05040100u),
+                       __builtin_amdgcn_perm(d[7].x, d[6].x, 0x05040100u));
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[0], 0, 0, 0);
+        a = make_uint4(__builtin_amdgcn_perm(d[1].x, d[0].x, 0x07060302u),
+                       __builtin_amdgcn_perm(d[3].x, d[2].x, 0x07060302u),
+                       __builtin_amdgcn_perm(d[5].x, d[4].x, 0x07060302u),
+                       __builtin_amdgcn_perm(d[7].x, d[6].x, 0x07060302u));
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[1], 0, 0, 0);
+        a = make_uint4(__builtin_amdgcn_perm(d[1].y, d[0].y, 0x05040100u),
+                       __builtin_amdgcn_perm(d[3].y, d[2].y, 0x05040100u),
+                       __builtin_amdgcn_perm(d[5].y, d[4].y, 0x05040100u),
+                       __builtin_amdgcn_perm(d[7].y, d[6].y, 0x05040100u));
+        acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[2], 0, 0, 0);
+        a = make_uint4(__builtin_amdgcn_perm(d[1].y, d[0].y, 0x07060302u),
+                       __builtin_amdgcn_perm(d[3].y, d[2].y, 0x07060302u),
+                       __builtin_amdgcn_perm(d[5].y, d[4].y, 0x07060302u),
+                       __builtin_amdgcn_perm(d[7].y, d[6].y, 0x07060302u));
+        acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[3], 0, 0, 0);
+        bq = bq_next;
     }
 }
 
 // ------------------------------------------------------------------ draft
+// Epilogue of one lane (one request, 64 entries vh + entry_of(i, t)): the
+// accumulators become s = base + bias (-inf past V); for T > 0 the lane's
+// softmax partial (max and sum of exp((s - max) / T), on the z = s / T scale)
+// and Gumbel-max winner; for T == 0 the argmax of s.
+// The Gumbel-max compares key = (s - m) c - log2(-log2 u) with c = log2(e) / T
+// and m the lane maximum of s: key is log2(e) (z + G) shifted by a per-lane
+// constant, and its first term is the exponent argument of the softmax sum.
+// Entries are visited in increasing v, so a strict comparison keeps the
+// smallest index among equal keys.  The winner's z + G is then formed once
+// for the comparison with other lanes and strips.
+__device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4 (&bl)[8], int vh,
+                                                   float T, uint64_t seed, int b, uint32_t pos) {
+    const bool greedy = !(T > 0.0f);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float sv = logit_at(bl, i, t) + acc[t][i];
+            acc[t][i] = sv;
+            mx = fmaxf(mx, sv);
+        }
+    }
+    RowState st = row_empty();
+    float best = -INFINITY, best_s = -INFINITY;
+    int be = 0;
+    if (!greedy) {
+        const float it = inv_temperature(T);
+        const float c2 = it * kLog2e;
+        // a lane of the tail strip may hold no entry below V (mx = -inf)
+        const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e0 = entry_of(i, 0);
+            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh + e0) >> 2);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float arg = fmaf(acc[t][i], c2, -mc);
+                sum += __builtin_amdgcn_exp2f(arg);
+                const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, t)));
+                const float key = arg - __builtin_amdgcn_logf(-l1);
+                if (key > best) {
+                    best = key;
+                    best_s = acc[t][i];
+                    be = e0 + t;
+                }
+            }
+            // finish one Philox block before the next: bounds live registers
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int vw = vh + be;
+        const u32x4 rw = philox_block(seed, b, pos, kTagDraft, vw >> 2);
+        st.m = mx * it;
+        st.s = sum;
+        st.zb = best_s * it;
+        st.pert = st.zb + gumbel_fast(pick(rw, vw & 3));
+        st.idx = vw;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (acc[t][i] > best) {
+                    best = acc[t][i];
+                    be = entry_of(i, t);
+                }
+            }
+        }
+        st.pert = best;
+        st.zb = best;
+        st.idx = vh + be;
+    }
+    return st;
+}
+
 template <int NWAVES>
-__global__ __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * NWAVES)
 void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
                       const uint16_t* __restrict__ W, const int32_t* __restrict__ prev,
                       int prev_stride, const float* __restrict__ temperature,
@@ -132,73 +232,11 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
     bias_tiles(acc, w_sh, A + static_cast<size_t>(p) * r + 8 * kh, r, lane);
     if (!active) return;
 
-    const int vl = v0 + 64 * kh;  // entry e = 4 i + t of this lane is v = vl + e
+    const int vh = v0 + 16 * kh;  // this lane's entries: vh + entry_of(i, t)
     uint4 bl[8];
-    load64(bl, base + (static_cast<size_t>(b) * K + k) * V, vl, V);
-    const bool full = vl + 64 <= V;
-    const float T = temperature[b];
-    const bool greedy = !(T > 0.0f);
-    const float it = greedy ? 1.0f : inv_temperature(T);
-    // The accumulators become the draft logits z = (base + bias) / T (for
-    // T == 0 the unscaled s = base + bias).  Entries past V become -inf.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int e = 4 * i + t;
-            float zz = (bf_elem(bl, e) + acc[t][i]) * it;
-            if (!full && vl + e >= V) zz = -INFINITY;
-            acc[t][i] = zz;
-            mx = fmaxf(mx, zz);
-        }
-    }
-    RowState st = row_empty();
-    float best = -INFINITY, bz = -INFINITY;
-    int bi = 0x7fffffff;
-    if (!greedy) {
-        const float mc = mx * kLog2e;
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], kLog2e, -mc));
-        st.m = mx;
-        st.s = sum;
-        // Gumbel-max; entries are visited in increasing v, so a tie never
-        // replaces the earlier (smaller) index.
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const u32x4 rnd = philox_block(seed, b, k + 1, kTagDraft, (vl + 4 * i) >> 2);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float pv = acc[t][i] + gumbel_fast(pick(rnd, t));
-                if (pv > best) {
-                    best = pv;
-                    bz = acc[t][i];
-                    bi = vl + 4 * i + t;
-                }
-            }
-            // one Philox block at a time keeps the register footprint small
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (acc[t][i] > best) {
-                    best = acc[t][i];
-                    bz = best;
-                    bi = vl + 4 * i + t;
-                }
-            }
-        }
-    }
-    st.pert = best;
-    st.zb = bz;
-    st.idx = bi;
+    load_lane_logits(bl, base + (static_cast<size_t>(b) * K + k) * V, vh, V,
+                     v0 + kStripV > V);
+    RowState st = draft_epilogue(acc, bl, vh, temperature[b], seed, b, k + 1);
     // lanes l and l + 32 hold the two halves of the strip for one request
     row_merge(st, shfl_xor_row(st, 32));
     if (kh == 0) store_partial(part, static_cast<size_t>(b) * n_strips + strip, st);
@@ -212,15 +250,15 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
 // of y with the same draws is kept as the fallback for a residual without
 // positive mass.  Rejected requests are listed in `list` (count entries).
 template <int NWAVES>
-__global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
-                         const uint16_t* __restrict__ W, const uint16_t* __restrict__ target,
-                         const int64_t* __restrict__ row_off, const int32_t* __restrict__ tokens,
-                         const int32_t* __restrict__ prev_token,
-                         const float* __restrict__ draft_lse, const float* __restrict__ temperature,
-                         const int32_t* __restrict__ accepted, const int32_t* __restrict__ list,
-                         const int32_t* __restrict__ count_ptr, const float* __restrict__ lse_tab,
-                         uint64_t seed, int K, int V, int r, PartialBuf res, PartialBuf fall,
-                         int n_strips) {
+__global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
+    const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ W, const uint16_t* __restrict__ target,
+    const int64_t* __restrict__ row_off, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ prev_token, const float* __restrict__ draft_lse,
+    const float* __restrict__ temperature, const int32_t* __restrict__ accepted,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ count_ptr,
+    const float* __restrict__ lse_tab, uint64_t seed, int K, int V, int r, PartialBuf res,
+    PartialBuf fall, int n_strips) {
     extern __shared__ uint16_t w_sh[];
     const int count = *count_ptr;
     const int slot0 = blockIdx.y * NWAVES * 32;
@@ -244,10 +282,11 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(const uint16_
     bias_tiles(acc, w_sh, A + static_cast<size_t>(p) * r + 8 * kh, r, lane);
     if (!active) return;
 
-    const int vl = v0 + 64 * kh;
+    const int vh = v0 + 16 * kh;
     uint4 bl[8], tl[8];
-    load64(bl, base + (static_cast<size_t>(b) * K + js - 1) * V, vl, V);
-    load64(tl, target + (row_off[b] + js - 1) * static_cast<int64_t>(V), vl, V);
+    const bool tail = v0 + kStripV > V;
+    load_lane_logits(bl, base + (static_cast<size_t>(b) * K + js - 1) * V, vh, V, tail);
+    load_lane_logits(tl, target + (row_off[b] + js - 1) * static_cast<int64_t>(V), vh, V, tail);
     const float it = inv_temperature(temperature[b]);
     const float lse_d = draft_lse[static_cast<size_t>(b) * K + js - 1];
     const float lse_t = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1];
@@ -255,26 +294,27 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(const uint16_
     int ir = 0x7fffffff, jf = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vl + 4 * i) >> 2);
+        const int e0 = entry_of(i, 0);
+        const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vh + e0) >> 2);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int e = 4 * i + t;
-            if (vl + e >= V) continue;
-            const float z = (bf_elem(bl, e) + acc[t][i]) * it;
-            const float y = bf_elem(tl, e) * it;
+            const int v = vh + e0 + t;
+            if (v >= V) continue;
+            const float z = (logit_at(bl, i, t) + acc[t][i]) * it;
+            const float y = logit_at(tl, i, t) * it;
             const float g = gumbel_fast(pick(rnd, t));
             const float rv = expf(y - lse_t) - expf(z - lse_d);
             if (rv > 0.0f) {
                 const float pr = logf(rv) + g;
                 if (pr > br) {
                     br = pr;
-                    ir = vl + e;
+                    ir = v;
                 }
             }
             const float pf = y + g;
             if (pf > bf) {
                 bf = pf;
-                jf = vl + e;
+                jf = v;
             }
         }
         __builtin_amdgcn_sched_barrier(0);
