@@ -21,8 +21,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+METRIC = "draft+verify tokens/s at B=256,K=16,V=151936; % of HBM / MFMA roofline"
+# Files whose contents define the dominant kernel; the stored PMC traffic figure
+# is only reported while their hash matches the one it was measured with.
+DOMINANT_SOURCES = ("draft_mfma.hip", "common.hpp", "kernels.hpp")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "draft_strip_mfma_long_draft_pmc.md")
 
 
 def parse():
@@ -33,7 +38,49 @@ def parse():
     ap.add_argument("--workload", default="long_draft")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=24)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain copy kernel (torch.neg, fp32) of this many MiB before "
+                         "warmup, as the reference for HBM counter scaling")
     return ap.parse_args()
+
+
+def dominant_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in DOMINANT_SOURCES:
+        with open(os.path.join(ROOT, "draft_sampling_verification_04_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """Per-launch HBM bytes of the dominant kernel from the committed PMC summary,
+    or None when the kernel's sources changed since the counters were taken."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            fields = dict(l.split(":", 1) for l in f.read().splitlines()
+                          if l.startswith(("source_hash:", "traffic_bytes_per_launch:")))
+    except (OSError, ValueError):
+        return None
+    if fields.get("source_hash", "").strip() != dominant_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
 
 
 def cpu_baseline(w, inp, seed, n_req):
@@ -58,18 +105,20 @@ def cpu_baseline(w, inp, seed, n_req):
         orc.verify_request(tok, int(prev[b]), base, A, W, rows, w.K, float(temp[b]), seed, b)
         t_total += time.perf_counter() - t0
     tokens = n_req * w.K
-    return dict(value=tokens / t_total, unit="tokens/s", cores=1, kind="oracle",
+    model, ncpu = host_cpu()
+    return dict(value=round(tokens / t_total, 2), unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{n_req} request(s) of {w.name} (K={w.K}, V={w.V}, r={w.r}), full draft + "
-                       f"verify of K tokens, T>0 first; {t_total:.2f} s; requests are independent, "
-                       f"so the rate scales linearly with B")
+                       f"verify of K tokens each, T>0 requests first; {t_total:.2f} s on one "
+                       f"thread of {model} ({ncpu} logical CPUs); requests are independent, so "
+                       f"the rate does not depend on B")
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards over requests without communication, see DESIGN.md",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): requests are "
+              "independent, so more GPUs would each run this same path on their own share of "
+              "the batch, and no multi-GPU figure is produced", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -106,6 +155,15 @@ def main():
     ws_v = torch.empty(d.dspark_verify_workspace_bytes(B, K, V, r), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    if args.copy_probe_mib > 0:
+        # reference kernel for counter scaling: reads and writes exactly N MiB
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     def step(events=None):
         if events:
             events[0].record(stream)
@@ -127,31 +185,75 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Timed region.  The library brackets each launch of the dominant kernel
+    # (the draft strip kernel, K launches per step) with HIP events on the
+    # stream it is launched on.
     phase_events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
                     for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    d.dspark_profile_begin(("draft_strip",), max_launches=K * args.steps + 16)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
         step(phase_events[i])
     t_end.record(stream)
     torch.cuda.synchronize()
+    prof = d.dspark_profile_end()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     draft_ms = sum(e[0].elapsed_time(e[1]) for e in phase_events) / args.steps
     sched_ms = sum(e[1].elapsed_time(e[2]) for e in phase_events) / args.steps
     verify_ms = sum(e[2].elapsed_time(e[3]) for e in phase_events) / args.steps
+    strip_ms, _, strip_timed = prof["draft_strip"]
+    strip_avg_s = strip_ms / max(strip_timed, 1) / 1e3
+
+    # One more (untimed) pass over a few steps with every kernel bracketed,
+    # for the per-kernel table.
+    d.dspark_profile_begin(d.KERNELS, max_launches=64 * max(1, min(args.steps, 5)))
+    for _ in range(max(1, min(args.steps, 5))):
+        step()
+    torch.cuda.synchronize()
+    per_kernel = d.dspark_profile_end()
+
     verified = int(L.sum())
     emitted = int(acc.sum()) + B
     tokens_per_s = B * K / (ms_step / 1e3)
 
     es = 2 if w.dtype == torch.bfloat16 else 4
-    draft_bytes = es * (B * K * V + r * V)  # base once + W once
-    verify_bytes = es * ((verified + B) * V + r * V)
-    draft_flops = 2.0 * B * r * V * K
+    # algorithmic bytes and flops per launch of the draft strip kernel (one
+    # draft step): the base-logit slice of every request plus all of W (every
+    # step multiplies by the whole of W), plus the gathered rows of A
+    strip_bytes = es * (B * V + r * V + B * r)
+    strip_flops = 2.0 * B * r * V
+    achieved_gbs = strip_bytes / strip_avg_s / 1e9
+    traffic = stored_traffic()
+
+    # algorithmic bytes of the verify rows kernel per launch: every visited
+    # target row once (selected rows + the bonus row of each request)
+    rows_ms, _, rows_timed = per_kernel["verify_rows"]
+    rows_bytes = es * (verified + B) * V
+    res_ms, _, res_timed = per_kernel["residual_strip"]
+    rejected = int(((acc < L) & (inp["temp"] > 0)).sum())  # sampled rejections only
+    res_bytes = es * (2 * rejected * V + r * V + rejected * r)
+
+    def gbs(nbytes, ms, n):
+        return round(nbytes / (ms / max(n, 1) / 1e3) / 1e9, 1) if n else None
+
+    kernels = {}
+    for k, (ms, n, nt) in per_kernel.items():
+        kernels[k] = {"launches_per_step": round(n / max(1, min(args.steps, 5)), 2),
+                      "avg_launch_us": round(1e3 * ms / nt, 2) if nt else None}
+    kernels["draft_strip"].update(
+        hbm_gbs=gbs(strip_bytes, *per_kernel["draft_strip"][::2]),
+        mfma_tflops=round(strip_flops / (per_kernel["draft_strip"][0] /
+                                         max(per_kernel["draft_strip"][2], 1) / 1e3) / 1e12, 1))
+    kernels["verify_rows"].update(hbm_gbs=gbs(rows_bytes, rows_ms, rows_timed))
+    kernels["residual_strip"].update(hbm_gbs=gbs(res_bytes, res_ms, res_timed))
+
+    model, ncpu = host_cpu()
     out = {
-        "metric": "draft+verify tokens/s at B=256,K=16,V=151936",
+        "metric": METRIC,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -165,14 +267,27 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "K": K, "V": V, "r": r,
                    "temperatures": list(w.temps), "budget_tokens": budget,
-                   "parallelism": "single GPU"},
+                   "verify": "every drafted token", "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "draft_strip_mfma",
+            "algorithmic_bytes_per_launch": strip_bytes,
+            "avg_launch_us": round(strip_avg_s * 1e6, 2),
+            "launches_timed": strip_timed,
+            "mfma_tflops": round(strip_flops / strip_avg_s / 1e12, 1),
+            "mfma_frac": round(strip_flops / strip_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
         "phases_ms": {"draft": round(draft_ms, 4), "schedule": round(sched_ms, 4),
                       "verify": round(verify_ms, 4)},
+        "kernels": kernels,
         "emitted_tokens_per_s": round(emitted / (ms_step / 1e3), 1),
         "vocab_logits_per_s": round((B * K * V + (verified + B) * V) / (ms_step / 1e3), 1),
-        "draft_call_hbm_gbs": round(draft_bytes / (draft_ms / 1e3) / 1e9, 1),
-        "verify_call_hbm_gbs": round(verify_bytes / (verify_ms / 1e3) / 1e9, 1),
-        "draft_call_tflops": round(draft_flops / (draft_ms / 1e3) / 1e12, 2),
+        "host_cpu": f"{model} x{ncpu}",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, seed, args.cpu_requests)

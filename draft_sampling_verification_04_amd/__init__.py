@@ -7,10 +7,13 @@ synthetic workload generators.
 from .binding import (  # noqa: F401
     DSPARK_BF16,
     DSPARK_F32,
+    KERNELS,
     DsparkError,
     LIB_PATH,
     dspark_draft_sample,
     dspark_draft_workspace_bytes,
+    dspark_profile_begin,
+    dspark_profile_end,
     dspark_schedule,
     dspark_schedule_workspace_bytes,
     dspark_verify,

@@ -26,6 +26,10 @@ DSPARK_ERR_HIP = 4
 
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
+
+# dspark_kernel ids (bit positions of the profiling mask)
+KERNELS = ("draft_strip", "draft_combine", "verify_rows", "verify_resolve", "residual_strip",
+           "residual_combine", "schedule")
 _DT = {torch.float32: DSPARK_F32, torch.bfloat16: DSPARK_BF16}
 
 
@@ -70,6 +74,10 @@ def lib():
         L.dspark_verify.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P,
                                     _I64, _P, _P, _P, _U64, _I32, _I32, _I32, _I32, _P, _P, _P,
                                     _P, _P, _SZ, _P]
+        L.dspark_profile_begin.restype = ctypes.c_int
+        L.dspark_profile_begin.argtypes = [ctypes.c_uint32, _I32]
+        L.dspark_profile_end.restype = ctypes.c_int
+        L.dspark_profile_end.argtypes = [_P, _P, _P]
         _lib = L
     return _lib
 
@@ -233,3 +241,22 @@ def dspark_verify(draft_tokens, prev_token, draft_logp, draft_lse, base_logits, 
         _ptr(next_token), _ptr(row_lse_t), _ptr(row_logratio), _ptr(workspace),
         workspace.numel(), _stream(stream, dev)))
     return accepted, next_token, row_lse_t, row_logratio
+
+
+def dspark_profile_begin(kernels=KERNELS, max_launches=4096):
+    """Open a per-kernel event-timing session for the named kernels."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << KERNELS.index(k)
+    _check(lib().dspark_profile_begin(mask, max_launches))
+
+
+def dspark_profile_end():
+    """Close the session; returns {kernel: (total_ms, launches, timed_launches)}."""
+    n = len(KERNELS)
+    ms = (ctypes.c_double * n)()
+    launches = (ctypes.c_int64 * n)()
+    timed = (ctypes.c_int64 * n)()
+    _check(lib().dspark_profile_end(ctypes.cast(ms, _P), ctypes.cast(launches, _P),
+                                    ctypes.cast(timed, _P)))
+    return {k: (ms[i], launches[i], timed[i]) for i, k in enumerate(KERNELS)}

@@ -167,4 +167,18 @@ dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_tok
     return hip_status(dspark::launch_verify(a), "verify");
 }
 
+dspark_status dspark_profile_begin(uint32_t kernel_mask, int32_t max_launches) {
+    if (kernel_mask == 0 || max_launches < 1 || max_launches > (1 << 20))
+        return fail(DSPARK_ERR_INVALID_ARG, "profile: mask=0x%x max_launches=%d", kernel_mask,
+                    max_launches);
+    hipError_t e = dspark::profile_open(kernel_mask, max_launches);
+    if (e == hipErrorInvalidValue)
+        return fail(DSPARK_ERR_INVALID_ARG, "profile: a session is already open");
+    return hip_status(e, "profile_begin");
+}
+
+dspark_status dspark_profile_end(double* total_ms, int64_t* launches, int64_t* timed) {
+    return hip_status(dspark::profile_close(total_ms, launches, timed), "profile_end");
+}
+
 }  // extern "C"

@@ -218,6 +218,7 @@ hipError_t launch_draft(const DraftArgs& a) {
     for (int k = 0; k < a.K; ++k) {
         const int32_t* prev = (k == 0) ? a.prev_token : a.tokens + (k - 1);
         const int prev_stride = (k == 0) ? 1 : a.K;
+        ProfScope strip_scope(DSPARK_KERNEL_DRAFT_STRIP, a.stream);
         if (mfma) {
             hipError_t e = launch_draft_mfma_step(a, prev, prev_stride, k, ws.order, ws.part,
                                                   n_strips);
@@ -233,6 +234,9 @@ hipError_t launch_draft(const DraftArgs& a) {
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        prof_end(strip_scope.slot, a.stream);
+        strip_scope.slot = -1;
+        ProfScope combine_scope(DSPARK_KERNEL_DRAFT_COMBINE, a.stream);
         hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)), dim3(kCombineThreads), 0,
                            a.stream, ws.part, n_strips, a.temperature, a.K, k, a.tokens, a.logp,
                            a.lse);

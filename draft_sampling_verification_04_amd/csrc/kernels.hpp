@@ -20,6 +20,20 @@ struct PartialBuf {
     int32_t* idx;
 };
 
+// Event timing hooks (profile.hip): prof_begin returns a slot (or -1 when the
+// kernel is not being timed) to hand to prof_end after the launch.
+int prof_begin(int kernel, hipStream_t stream);
+void prof_end(int slot, hipStream_t stream);
+hipError_t profile_open(uint32_t mask, int32_t capacity);
+hipError_t profile_close(double* total_ms, int64_t* launches, int64_t* timed);
+
+struct ProfScope {
+    int slot;
+    hipStream_t stream;
+    ProfScope(int kernel, hipStream_t s) : slot(prof_begin(kernel, s)), stream(s) {}
+    ~ProfScope() { prof_end(slot, stream); }
+};
+
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -265,6 +265,7 @@ hipError_t launch_schedule(const ScheduleArgs& a) {
         c.cn[i] = i < a.n_points ? a.curve_n[i] : 0.0;
         c.ct[i] = i < a.n_points ? a.curve_tau[i] : 0.0;
     }
+    ProfScope scope(DSPARK_KERNEL_SCHEDULE, a.stream);
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, a.stream, a.conf, a.B, a.K,
                        static_cast<long long>(a.budget), c, a.lengths, a.row_offsets, a.survival,
                        keys, sorted, static_cast<int>(npow));

@@ -411,6 +411,7 @@ hipError_t launch_verify(const VerifyArgs& a) {
     hipLaunchKernelGGL(fill_i32, dim3(1), dim3(64), 0, a.stream, ws.count, 1, 0);
     const dim3 rows_grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * (a.K + 1)));
     const bool vec_ok = aligned16(a.target);
+    ProfScope rows_scope(DSPARK_KERNEL_VERIFY_ROWS, a.stream);
     if (a.logit_dt == DSPARK_BF16) {
         hipLaunchKernelGGL(verify_rows<bf16_t>, rows_grid, dim3(kRowThreads), 0, a.stream,
                            static_cast<const bf16_t*>(a.target), a.row_off, a.lengths, a.tokens,
@@ -424,13 +425,19 @@ hipError_t launch_verify(const VerifyArgs& a) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(verify_resolve, dim3(static_cast<unsigned>(ceil_div(a.B, 256))), dim3(256),
-                       0, a.stream, a.B, a.K, a.n_rows, a.row_off, a.lengths, a.temperature, ws,
-                       a.accepted, a.next_token);
+    prof_end(rows_scope.slot, a.stream);
+    rows_scope.slot = -1;
+    {
+        ProfScope resolve_scope(DSPARK_KERNEL_VERIFY_RESOLVE, a.stream);
+        hipLaunchKernelGGL(verify_resolve, dim3(static_cast<unsigned>(ceil_div(a.B, 256))), dim3(256),
+                           0, a.stream, a.B, a.K, a.n_rows, a.row_off, a.lengths, a.temperature,
+                           ws, a.accepted, a.next_token);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.K == 0) return hipSuccess;  // no draft rows: every next token is a bonus draw
     int n_strips;
+    ProfScope res_scope(DSPARK_KERNEL_RESIDUAL_STRIP, a.stream);
     if (residual_mfma_supported(a)) {
         n_strips = static_cast<int>(ceil_div(a.V, kMfmaStrip));
         ResidualArgs ra{&a, ws.list, ws.count, ws.lse, ws.res, ws.fall, n_strips};
@@ -449,6 +456,9 @@ hipError_t launch_verify(const VerifyArgs& a) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    prof_end(res_scope.slot, a.stream);
+    res_scope.slot = -1;
+    ProfScope combine_scope(DSPARK_KERNEL_RESIDUAL_COMBINE, a.stream);
     hipLaunchKernelGGL(verify_residual_combine, dim3(static_cast<unsigned>(a.B)),
                        dim3(kRowThreads), 0, a.stream, ws, n_strips, a.next_token);
     return hipGetLastError();

@@ -169,6 +169,38 @@ dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_tok
                             float* row_lse_t, float* row_logratio, void* workspace,
                             size_t ws_bytes, void* stream);
 
+/* -------------------------------------------------------------- profiling */
+/*
+ * Per-kernel timing with HIP events, a measurement aid beside the three calls
+ * above (no page defines it).  While a session is open, each launch of a
+ * kernel whose bit (1 << dspark_kernel) is in kernel_mask is bracketed by two
+ * events recorded on its launch stream; the time between them is the launch's
+ * duration on that stream.  The session is process-wide: one at a time, from
+ * any thread.
+ */
+typedef enum dspark_kernel {
+    DSPARK_KERNEL_DRAFT_STRIP = 0,       /* draft: bias GEMM + logits + Gumbel over a vocab strip */
+    DSPARK_KERNEL_DRAFT_COMBINE = 1,     /* draft: merge of the per-strip partials of one step */
+    DSPARK_KERNEL_VERIFY_ROWS = 2,       /* verify: target normaliser and accept test per row */
+    DSPARK_KERNEL_VERIFY_RESOLVE = 3,    /* verify: strict-prefix resolution per request */
+    DSPARK_KERNEL_RESIDUAL_STRIP = 4,    /* verify: residual / fallback Gumbel over a vocab strip */
+    DSPARK_KERNEL_RESIDUAL_COMBINE = 5,  /* verify: merge of the residual partials */
+    DSPARK_KERNEL_SCHEDULE = 6,          /* schedule: survival, selection and row offsets */
+    DSPARK_KERNEL_COUNT = 7
+} dspark_kernel;
+
+/* Open a session timing at most max_launches launches (events are created
+ * here; later launches are counted, not timed).  ERR_INVALID_ARG if a session
+ * is already open, kernel_mask is 0 or max_launches is outside [1, 2^20];
+ * ERR_HIP if events cannot be created. */
+dspark_status dspark_profile_begin(uint32_t kernel_mask, int32_t max_launches);
+
+/* Close the session: wait for every recorded event, then write per kernel id
+ * (arrays of DSPARK_KERNEL_COUNT host entries, each nullable) the summed
+ * milliseconds of the timed launches, the launches seen and the launches
+ * timed.  Closing with no open session returns zeros. */
+dspark_status dspark_profile_end(double* total_ms, int64_t* launches, int64_t* timed);
+
 #ifdef __cplusplus
 }
 #endif

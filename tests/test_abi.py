@@ -116,3 +116,14 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(d.DsparkError):
         d.dspark_draft_sample(x, torch.zeros((8, 4)), torch.zeros((4, 8)),
                               torch.zeros(2, dtype=torch.int32), torch.ones(2), 0)
+
+
+def test_profile_session_without_gpu_work(L):
+    # an empty mask and a bad capacity are rejected before any HIP call
+    assert L.dspark_profile_begin(0, 16) == bd.DSPARK_ERR_INVALID_ARG
+    assert L.dspark_profile_begin(1, 0) == bd.DSPARK_ERR_INVALID_ARG
+    assert L.dspark_profile_begin(1, (1 << 20) + 1) == bd.DSPARK_ERR_INVALID_ARG
+    # closing with no session open returns zeros
+    res = d.dspark_profile_end()
+    assert set(res) == set(d.KERNELS)
+    assert all(v == (0.0, 0, 0) for v in res.values())
