@@ -171,10 +171,12 @@ void launch_valu_strip(const DraftArgs& a, const int32_t* prev, int prev_stride,
 
 // Implemented in draft_mfma.hip.
 bool mfma_supported(const DraftArgs& a);
+int mfma_draft_strip();
 hipError_t launch_temperature_order(const float* temperature, int B, int32_t* order,
                                     hipStream_t stream);
 hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
-                                  const int32_t* order, PartialBuf part, int n_strips);
+                                  const int32_t* order, PartialBuf part, int n_strips,
+                                  int* n_parts);
 
 namespace {
 
@@ -184,7 +186,7 @@ struct DraftWs {
 };
 
 DraftWs draft_ws(void* ws, int B, int V) {
-    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMfmaStrip);  // the larger strip count
+    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMinStrip);  // the largest strip count
     char* w = static_cast<char*>(ws);
     DraftWs d;
     d.part.v = reinterpret_cast<float4*>(w);
@@ -199,7 +201,7 @@ DraftWs draft_ws(void* ws, int B, int V) {
 size_t draft_workspace_bytes(int B, int K, int V, int r) {
     (void)K;
     (void)r;
-    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMfmaStrip);
+    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMinStrip);
     return align256(n * sizeof(float4)) + align256(n * sizeof(int32_t)) +
            align256(static_cast<size_t>(B) * sizeof(int32_t));
 }
@@ -209,7 +211,7 @@ bool draft_uses_mfma(const DraftArgs& a) { return mfma_supported(a); }
 hipError_t launch_draft(const DraftArgs& a) {
     if (a.B == 0 || a.K == 0) return hipSuccess;
     const bool mfma = draft_uses_mfma(a);
-    const int n_strips = static_cast<int>(ceil_div(a.V, mfma ? kMfmaStrip : kValuStrip));
+    const int n_strips = static_cast<int>(ceil_div(a.V, mfma ? mfma_draft_strip() : kValuStrip));
     const DraftWs ws = draft_ws(a.ws, a.B, a.V);
     if (mfma) {
         hipError_t e = launch_temperature_order(a.temperature, a.B, ws.order, a.stream);
@@ -219,9 +221,10 @@ hipError_t launch_draft(const DraftArgs& a) {
         const int32_t* prev = (k == 0) ? a.prev_token : a.tokens + (k - 1);
         const int prev_stride = (k == 0) ? 1 : a.K;
         ProfScope strip_scope(DSPARK_KERNEL_DRAFT_STRIP, a.stream);
+        int n_parts = n_strips;  // partials per request written by this step
         if (mfma) {
             hipError_t e = launch_draft_mfma_step(a, prev, prev_stride, k, ws.order, ws.part,
-                                                  n_strips);
+                                                  n_strips, &n_parts);
             if (e != hipSuccess) return e;
         } else if (a.logit_dt == DSPARK_BF16 && a.factor_dt == DSPARK_BF16) {
             launch_valu_strip<bf16_t, bf16_t>(a, prev, prev_stride, k, ws.part, n_strips);
@@ -238,7 +241,7 @@ hipError_t launch_draft(const DraftArgs& a) {
         strip_scope.slot = -1;
         ProfScope combine_scope(DSPARK_KERNEL_DRAFT_COMBINE, a.stream);
         hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)), dim3(kCombineThreads), 0,
-                           a.stream, ws.part, n_strips, a.temperature, a.K, k, a.tokens, a.logp,
+                           a.stream, ws.part, n_parts, a.temperature, a.K, k, a.tokens, a.logp,
                            a.lse);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -19,6 +19,8 @@
 //     its accumulator i covers the 4 consecutive entries
 //     v = start + 32 (i / 4) + 16 (l / 32) + 4 (i % 4) + t, t = 0..3: exactly
 //     one Philox block, and the lane's 64 entries are four runs of 16.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,7 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kStripV = kMfmaStrip;  // 128 vocabulary entries per strip
-constexpr int kPitch = kStripV + 8;  // LDS row pitch in bf16 elements (272 bytes)
+constexpr int kPitch = kStripV;  // LDS row pitch in bf16 elements (256 bytes)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8, q); }
 __device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
@@ -71,24 +73,65 @@ __device__ __forceinline__ float logit_at(const uint4 (&q)[8], int i, int t) {
     return __uint_as_float((o & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
 }
 
-// Stage W[0:r, v0:v0+128] in LDS.  V % 8 == 0, so each 16-byte chunk is either
-// inside the vocabulary or wholly past its end (then zero).
-template <int NT>
+// Stage W[0:r, v0:v0+128] in LDS (row pitch 256 bytes) with direct global->LDS
+// loads: one wave instruction moves 1 KiB, four rank rows of the strip, and
+// lane i's 16 bytes land at the instruction's LDS base + 16 i.  No VGPR holds
+// the data.  Chunks past the end of the vocabulary are read from the row's last
+// chunk (V % 8 == 0), so the bias of entries >= V is finite; their logits are
+// -inf.  The caller waits for the loads and synchronises before reading.
+template <int NWAVES>
 __device__ __forceinline__ void stage_w(uint16_t* w_sh, const uint16_t* __restrict__ W, int r,
                                         int V, int v0) {
-    for (int c = threadIdx.x; c < r * (kStripV / 8); c += NT) {
-        const int row = c >> 4;
-        const int cc = c & 15;
-        const int v = v0 + cc * 8;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (v < V) val = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(row) * V + v);
-        *reinterpret_cast<uint4*>(w_sh + row * kPitch + cc * 8) = val;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int v = min(v0 + 8 * (lane & 15), V - 8);
+    const uint16_t* src = W + static_cast<size_t>(lane >> 4) * V + v;
+    for (int j = wave; j < r / 4; j += NWAVES) {
+        __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(4 * j) * V,
+                                         w_sh + 4 * j * kPitch, 16, 0, 0);
     }
 }
 
 // acc[t] = (W^T tile t of the strip) x (factor row arow); arow points at the
-// lane's 8-element rank slice (A row + 8 * (lane / 32)).  The factor fragment of
-// the next rank step is fetched one step ahead.
+// lane's 8-element rank slice (A row + 8 * (lane / 32)).  The LDS rows and the
+// factor fragment of the next rank step are read one step ahead, so each
+// step's MFMAs do not wait on its own LDS reads.
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4], const uint2 (&d)[8], uint4 bq) {
+    // 8 rank rows x 4 entries -> four vectors of 8 rank values
+    const bf16x8 bv = as_bf16x8(bq);
+    uint4 a;
+    a = make_uint4(__builtin_amdgcn_perm(d[1].x, d[0].x, 0x05040100u),
+                   __builtin_amdgcn_perm(d[3].x, d[2].x, 0x05040100u),
+                   __builtin_amdgcn_perm(d[5].x, d[4].x, 0x05040100u),
+                   __builtin_amdgcn_perm(d[7].x, d[6].x, 0x05040100u));
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[0], 0, 0, 0);
+    a = make_uint4(__builtin_amdgcn_perm(d[1].x, d[0].x, 0x07060302u),
+                   __builtin_amdgcn_perm(d[3].x, d[2].x, 0x07060302u),
+                   __builtin_amdgcn_perm(d[5].x, d[4].x, 0x07060302u),
+                   __builtin_amdgcn_perm(d[7].x, d[6].x, 0x07060302u));
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[1], 0, 0, 0);
+    a = make_uint4(__builtin_amdgcn_perm(d[1].y, d[0].y, 0x05040100u),
+                   __builtin_amdgcn_perm(d[3].y, d[2].y, 0x05040100u),
+                   __builtin_amdgcn_perm(d[5].y, d[4].y, 0x05040100u),
+                   __builtin_amdgcn_perm(d[7].y, d[6].y, 0x05040100u));
+    acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[2], 0, 0, 0);
+    a = make_uint4(__builtin_amdgcn_perm(d[1].y, d[0].y, 0x07060302u),
+                   __builtin_amdgcn_perm(d[3].y, d[2].y, 0x07060302u),
+                   __builtin_amdgcn_perm(d[5].y, d[4].y, 0x07060302u),
+                   __builtin_amdgcn_perm(d[7].y, d[6].y, 0x07060302u));
+    acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[3], 0, 0, 0);
+}
+
+__device__ __forceinline__ void lds_rows(uint2 (&d)[8], const uint16_t* wl, int kk) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        d[j] = *reinterpret_cast<const uint2*>(wl + (kk * 16 + j) * kPitch);
+}
+
+__device__ __forceinline__ uint4 factor_frag(const uint16_t* arow, int kk, int ksteps) {
+    return *reinterpret_cast<const uint4*>(arow + 16 * min(kk, ksteps - 1));
+}
+
 __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_sh,
                                            const uint16_t* arow, int r, int lane) {
 #pragma unroll
@@ -97,39 +140,28 @@ __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_s
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
     const uint16_t* wl = w_sh + (8 * (lane >> 5)) * kPitch + 4 * (lane & 31);
     const int ksteps = r / 16;
-    uint4 bq = *reinterpret_cast<const uint4*>(arow);
-    for (int kk = 0; kk < ksteps; ++kk) {
-        const uint4 bq_next =
-            *reinterpret_cast<const uint4*>(arow + 16 * min(kk + 1, ksteps - 1));
-        uint2 d[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            d[j] = *reinterpret_cast<const uint2*>(wl + (kk * 16 + j) * kPitch);
-        // 8 rank rows x 4 entries -> four vectors of 8 rank values
-        const bf16x8 bv = as_bf16x8(bq);
-        uint4 a;
-        a = make_uint4(__builtin_amdgcn_perm(d[1].x, d[0].x, 0x05040100u),
-                       __builtin_amdgcn_perm(d[3].x, d[2].x, 0x05040100u),
-                       __builtin_amdgcn_perm(d[5].x, d[4].x, 0x05040100u),
-                       __builtin_amdgcn_perm(d[7].x, d[6].x, 0x05040100u));
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[0], 0, 0, 0);
-        a = make_uint4(__builtin_amdgcn_perm(d[1].x, d[0].x, 0x07060302u),
-                       __builtin_amdgcn_perm(d[3].x, d[2].x, 0x07060302u),
-                       __builtin_amdgcn_perm(d[5].x, d[4].x, 0x07060302u),
-                       __builtin_amdgcn_perm(d[7].x, d[6].x, 0x07060302u));
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[1], 0, 0, 0);
-        a = make_uint4(__builtin_amdgcn_perm(d[1].y, d[0].y, 0x05040100u),
-                       __builtin_amdgcn_perm(d[3].y, d[2].y, 0x05040100u),
-                       __builtin_amdgcn_perm(d[5].y, d[4].y, 0x05040100u),
-                       __builtin_amdgcn_perm(d[7].y, d[6].y, 0x05040100u));
-        acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[2], 0, 0, 0);
-        a = make_uint4(__builtin_amdgcn_perm(d[1].y, d[0].y, 0x07060302u),
-                       __builtin_amdgcn_perm(d[3].y, d[2].y, 0x07060302u),
-                       __builtin_amdgcn_perm(d[5].y, d[4].y, 0x07060302u),
-                       __builtin_amdgcn_perm(d[7].y, d[6].y, 0x07060302u));
-        acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[3], 0, 0, 0);
-        bq = bq_next;
+    // factor fragments come from L2, so they are fetched four rank steps ahead;
+    // indices past the last step are clamped (in bounds, never used)
+    uint4 q0 = factor_frag(arow, 0, ksteps), q1 = factor_frag(arow, 1, ksteps);
+    uint4 q2 = factor_frag(arow, 2, ksteps), q3 = factor_frag(arow, 3, ksteps);
+    uint2 d[8];
+    lds_rows(d, wl, 0);
+    int kk = 0;
+    for (; kk + 2 <= ksteps; kk += 2) {
+        uint2 e[8];
+        lds_rows(e, wl, kk + 1);
+        mfma_step(acc, d, q0);
+        q0 = factor_frag(arow, kk + 4, ksteps);
+        lds_rows(d, wl, min(kk + 2, ksteps - 1));
+        mfma_step(acc, e, q1);
+        q1 = factor_frag(arow, kk + 5, ksteps);
+        const uint4 t0 = q0, t1 = q1;
+        q0 = q2;
+        q1 = q3;
+        q2 = t0;
+        q3 = t1;
     }
+    if (kk < ksteps) mfma_step(acc, d, q0);
 }
 
 // ------------------------------------------------------------------ draft
@@ -209,37 +241,63 @@ __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4
     return st;
 }
 
+// One workgroup per (part, request group), persistent over the strips
+// part, part + n_parts, ...: while the waves run the bias MFMAs and the epilogue
+// of one strip, the next strip's W is already on its way into the other LDS
+// buffer and its logits into registers.  Each lane folds the strips it visits
+// into one running state, so a request gets n_parts partials per step.
 template <int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES)
 void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
                       const uint16_t* __restrict__ W, const int32_t* __restrict__ prev,
                       int prev_stride, const float* __restrict__ temperature,
                       const int32_t* __restrict__ order, uint64_t seed, int B, int K, int V,
-                      int r, int k, PartialBuf part, int n_strips) {
-    extern __shared__ uint16_t w_sh[];  // [r][kPitch]
+                      int r, int k, PartialBuf part, int n_strips, int n_parts) {
+    extern __shared__ uint16_t w_sh[];  // two buffers of [r][kPitch]
     const int lane = threadIdx.x & 63;
     const int kh = lane >> 5;
-    const int strip = blockIdx.x;
-    const int v0 = strip * kStripV;
     const int slot = (blockIdx.y * NWAVES + (threadIdx.x >> 6)) * 32 + (lane & 31);
     const bool active = slot < B;
+    // lanes past B run request 0's row (every wave takes part in the MFMAs and
+    // barriers) and store nothing
     const int b = active ? order[slot] : 0;
-    stage_w<64 * NWAVES>(w_sh, W, r, V, v0);
-    const int p = active ? clamp_token(prev[static_cast<size_t>(b) * prev_stride], V) : 0;
-    __syncthreads();
+    const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
+    const float T = temperature[b];
+    const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
+    const uint16_t* brow = base + (static_cast<size_t>(b) * K + k) * V;
+    const int buf_elems = r * kPitch;
 
-    f32x16 acc[4];
-    bias_tiles(acc, w_sh, A + static_cast<size_t>(p) * r + 8 * kh, r, lane);
-    if (!active) return;
-
-    const int vh = v0 + 16 * kh;  // this lane's entries: vh + entry_of(i, t)
+    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
+    stage_w<NWAVES>(w_sh, W, r, V, s * kStripV);
     uint4 bl[8];
-    load_lane_logits(bl, base + (static_cast<size_t>(b) * K + k) * V, vh, V,
-                     v0 + kStripV > V);
-    RowState st = draft_epilogue(acc, bl, vh, temperature[b], seed, b, k + 1);
-    // lanes l and l + 32 hold the two halves of the strip for one request
-    row_merge(st, shfl_xor_row(st, 32));
-    if (kh == 0) store_partial(part, static_cast<size_t>(b) * n_strips + strip, st);
+    load_lane_logits(bl, brow, s * kStripV + 16 * kh, V, s * kStripV + kStripV > V);
+    RowState run = row_empty();
+    int buf = 0;
+    for (;;) {
+        // this strip's W (all waves' shares) and logits have landed, and every
+        // wave is done with the other buffer
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int sn = s + n_parts;
+        const bool more = sn < n_strips;
+        if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
+        f32x16 acc[4];
+        bias_tiles(acc, w_sh + buf * buf_elems, arow, r, lane);
+        uint4 bn[8];
+        if (more)
+            load_lane_logits(bn, brow, sn * kStripV + 16 * kh, V, sn * kStripV + kStripV > V);
+        // lane entries: strip start + 16 kh + entry_of(i, t)
+        row_merge(run, draft_epilogue(acc, bl, s * kStripV + 16 * kh, T, seed, b, k + 1));
+        if (!more) break;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bl[c] = bn[c];
+        buf ^= 1;
+        s = sn;
+    }
+    // lanes l and l + 32 hold the two halves of every strip for one request
+    row_merge(run, shfl_xor_row(run, 32));
+    if (active && kh == 0)
+        store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
 }
 
 // --------------------------------------------------------------- residual
@@ -271,11 +329,12 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     const bool active = slot < count;
     const int b = active ? list[slot] : 0;
     const int js = active ? accepted[b] + 1 : 1;
-    stage_w<64 * NWAVES>(w_sh, W, r, V, v0);
+    stage_w<NWAVES>(w_sh, W, r, V, v0);
     const int p = active ? clamp_token((js == 1) ? prev_token[b]
                                                  : tokens[static_cast<size_t>(b) * K + js - 2],
                                        V)
                          : 0;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     f32x16 acc[4];
@@ -386,27 +445,51 @@ __global__ __launch_bounds__(1024) void temperature_order(const float* __restric
 
 constexpr int kMaxLds = 160 * 1024;
 
+// Let the kernel take all the LDS its static arrays leave.
 template <typename Kern>
 hipError_t allow_big_lds(Kern* kern, bool& done) {
     if (done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLds - static_cast<int>(fa.sharedSizeBytes));
     if (e == hipSuccess) done = true;
     return e;
 }
 
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int NWAVES>
 hipError_t launch_draft_strip(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
-                              const int32_t* order, PartialBuf part, int n_strips) {
+                              const int32_t* order, PartialBuf part, int n_strips,
+                              int* n_parts) {
     static bool lds_ok = false;
     hipError_t e = allow_big_lds(&draft_strip_mfma<NWAVES>, lds_ok);
     if (e != hipSuccess) return e;
-    const size_t lds = sizeof(uint16_t) * static_cast<size_t>(a.r) * kPitch;
-    dim3 grid(static_cast<unsigned>(n_strips), static_cast<unsigned>(ceil_div(a.B, 32 * NWAVES)));
+    const size_t lds = 2 * sizeof(uint16_t) * static_cast<size_t>(a.r) * kPitch;
+    // one resident workgroup per CU (the two W buffers take most of the LDS)
+    const int groups = static_cast<int>(ceil_div(a.B, 32 * NWAVES));
+    const int parts = std::max(1, std::min(n_strips, device_cus() / groups));
+    *n_parts = parts;
+    dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(groups));
     hipLaunchKernelGGL(draft_strip_mfma<NWAVES>, grid, dim3(64 * NWAVES), lds, a.stream,
                        static_cast<const uint16_t*>(a.base), static_cast<const uint16_t*>(a.A),
                        static_cast<const uint16_t*>(a.W), prev, prev_stride, a.temperature, order,
-                       a.seed, a.B, a.K, a.V, a.r, k, part, n_strips);
+                       a.seed, a.B, a.K, a.V, a.r, k, part, n_strips, parts);
     return hipGetLastError();
 }
 
@@ -431,9 +514,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+int mfma_draft_strip() { return kStripV; }
+
 bool mfma_supported(const DraftArgs& a) {
+    // two LDS buffers of r x 128 bf16 must fit in 160 KiB
     return a.factor_dt == DSPARK_BF16 && a.logit_dt == DSPARK_BF16 && a.r % 16 == 0 &&
-           a.r <= 512 && a.V % 8 == 0 && aligned16(a.base) && aligned16(a.A) && aligned16(a.W);
+           a.r <= 256 && a.V % 8 == 0 && aligned16(a.base) && aligned16(a.A) && aligned16(a.W);
 }
 
 bool residual_mfma_supported(const VerifyArgs& a) {
@@ -449,10 +535,13 @@ hipError_t launch_temperature_order(const float* temperature, int B, int32_t* or
 }
 
 hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
-                                  const int32_t* order, PartialBuf part, int n_strips) {
-    if (a.B > 128) return launch_draft_strip<8>(a, prev, prev_stride, k, order, part, n_strips);
-    if (a.B > 64) return launch_draft_strip<4>(a, prev, prev_stride, k, order, part, n_strips);
-    return launch_draft_strip<2>(a, prev, prev_stride, k, order, part, n_strips);
+                                  const int32_t* order, PartialBuf part, int n_strips,
+                                  int* n_parts) {
+    if (a.B > 128)
+        return launch_draft_strip<8>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
+    if (a.B > 64)
+        return launch_draft_strip<4>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
+    return launch_draft_strip<2>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
 }
 
 hipError_t launch_residual_mfma(const ResidualArgs& a) {

@@ -12,6 +12,7 @@ namespace dspark {
 // Vocabulary entries per partial (one workgroup strip) of the two draft paths.
 constexpr int kValuStrip = 1024;  // 256 threads x 4 entries
 constexpr int kMfmaStrip = 128;   // 4 MFMA row tiles of 32
+constexpr int kMinStrip = 64;     // narrowest strip of any draft path (sizes the partials)
 
 // Stored per-strip reduction partials: (max, sum, perturbed best, logit at the
 // best) as float4 plus the best index.
