@@ -172,6 +172,8 @@ void launch_valu_strip(const DraftArgs& a, const int32_t* prev, int prev_stride,
 // Implemented in draft_mfma.hip.
 bool mfma_supported(const DraftArgs& a);
 int mfma_draft_strip();
+hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts,
+                                    const int32_t* prev, int prev_stride, int k);
 hipError_t launch_temperature_order(const float* temperature, int B, int32_t* order,
                                     hipStream_t stream);
 hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
@@ -240,10 +242,14 @@ hipError_t launch_draft(const DraftArgs& a) {
         prof_end(strip_scope.slot, a.stream);
         strip_scope.slot = -1;
         ProfScope combine_scope(DSPARK_KERNEL_DRAFT_COMBINE, a.stream);
-        hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)), dim3(kCombineThreads), 0,
-                           a.stream, ws.part, n_parts, a.temperature, a.K, k, a.tokens, a.logp,
-                           a.lse);
-        e = hipGetLastError();
+        if (mfma) {
+            e = launch_draft_combine_mfma(a, ws.part, n_parts, prev, prev_stride, k);
+        } else {
+            hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)),
+                               dim3(kCombineThreads), 0, a.stream, ws.part, n_parts,
+                               a.temperature, a.K, k, a.tokens, a.logp, a.lse);
+            e = hipGetLastError();
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

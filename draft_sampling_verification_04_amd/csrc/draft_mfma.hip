@@ -170,11 +170,13 @@ __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_s
 // softmax partial (max and sum of exp((s - max) / T), on the z = s / T scale)
 // and Gumbel-max winner; for T == 0 the argmax of s.
 // The Gumbel-max compares key = (s - m) c - log2(-log2 u) with c = log2(e) / T
-// and m the lane maximum of s: key is log2(e) (z + G) shifted by a per-lane
-// constant, and its first term is the exponent argument of the softmax sum.
-// Entries are visited in increasing v, so a strict comparison keeps the
-// smallest index among equal keys.  The winner's z + G is then formed once
-// for the comparison with other lanes and strips.
+// and m the lane maximum of s; since -log2(-log2 u) = log2(e) (G + ln ln 2),
+// key + m c = log2(e) (z + G) + log2(e) ln ln 2 orders the entries of a row
+// exactly as z + G does, and it is what lanes and strips compare (the "pert"
+// of the partial).  The first term of key is also the exponent argument of the
+// softmax sum.  Entries are visited in increasing v, so a strict comparison
+// keeps the smallest index among equal keys.  The winner's logit is not kept:
+// the combine step recomputes it for the one winning entry of the row.
 __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4 (&bl)[8], int vh,
                                                    float T, uint64_t seed, int b, uint32_t pos) {
     const bool greedy = !(T > 0.0f);
@@ -189,7 +191,7 @@ __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4
         }
     }
     RowState st = row_empty();
-    float best = -INFINITY, best_s = -INFINITY;
+    float best = -INFINITY;
     int be = 0;
     if (!greedy) {
         const float it = inv_temperature(T);
@@ -209,20 +211,15 @@ __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4
                 const float key = arg - __builtin_amdgcn_logf(-l1);
                 if (key > best) {
                     best = key;
-                    best_s = acc[t][i];
                     be = e0 + t;
                 }
             }
-            // finish one Philox block before the next: bounds live registers
-            __builtin_amdgcn_sched_barrier(0);
         }
-        const int vw = vh + be;
-        const u32x4 rw = philox_block(seed, b, pos, kTagDraft, vw >> 2);
         st.m = mx * it;
         st.s = sum;
-        st.zb = best_s * it;
-        st.pert = st.zb + gumbel_fast(pick(rw, vw & 3));
-        st.idx = vw;
+        st.pert = best + mc;
+        st.zb = 0.0f;
+        st.idx = vh + be;
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -298,6 +295,61 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
     row_merge(run, shfl_xor_row(run, 32));
     if (active && kh == 0)
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
+}
+
+// Fold the partials of each request (one 256-thread workgroup per request) and
+// write x_k, log p_d(x_k) and lse_d.  For T > 0 the partials carry the winner's
+// index but not its logit, so the winning entry's z = (base + A[x_{k-1}] . W[:, v]) / T
+// is recomputed here (one rank-r dot product per request).
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void draft_combine_mfma(
+    PartialBuf part, int n_parts, const uint16_t* __restrict__ base,
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ prev, int prev_stride, const float* __restrict__ temperature,
+    int K, int V, int r, int k, int32_t* __restrict__ tokens, float* __restrict__ logp,
+    float* __restrict__ lse) {
+    __shared__ RowState red[kCombineThreads / kWave];
+    __shared__ float dsum[kCombineThreads / kWave];
+    __shared__ int win;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    RowState st = row_empty();
+    for (int s = tid; s < n_parts; s += kCombineThreads)
+        row_merge(st, load_partial(part, static_cast<size_t>(b) * n_parts + s));
+    st = block_reduce_row<kCombineThreads>(st, red);
+    const float T = temperature[b];
+    if (tid == 0) win = clamp_token(st.idx, V);
+    __syncthreads();
+    const size_t o = static_cast<size_t>(b) * K + k;
+    if (!(T > 0.0f)) {
+        if (tid == 0) {
+            tokens[o] = st.idx;
+            if (lse) lse[o] = st.pert;
+            if (logp) logp[o] = 0.0f;
+        }
+        return;
+    }
+    const int v = win;
+    const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
+    float d = 0.0f;
+    for (int i = tid; i < r; i += kCombineThreads)
+        d = fmaf(to_f32(bf16_t{A[static_cast<size_t>(p) * r + i]}),
+                 to_f32(bf16_t{W[static_cast<size_t>(i) * V + v]}), d);
+#pragma unroll
+    for (int m = kWave / 2; m > 0; m >>= 1) d += __shfl_xor(d, m, kWave);
+    if ((tid & 63) == 0) dsum[tid >> 6] = d;
+    __syncthreads();
+    if (tid == 0) {
+        float bias = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kCombineThreads / kWave; ++w) bias += dsum[w];
+        const float z = (to_f32(bf16_t{base[o * V + v]}) + bias) * inv_temperature(T);
+        const float l = st.m + logf(st.s);
+        tokens[o] = st.idx;
+        if (lse) lse[o] = l;
+        if (logp) logp[o] = z - l;
+    }
 }
 
 // --------------------------------------------------------------- residual
@@ -542,6 +594,15 @@ hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int p
     if (a.B > 64)
         return launch_draft_strip<4>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
     return launch_draft_strip<2>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
+}
+
+hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts,
+                                    const int32_t* prev, int prev_stride, int k) {
+    hipLaunchKernelGGL(draft_combine_mfma, dim3(static_cast<unsigned>(a.B)), dim3(kCombineThreads),
+                       0, a.stream, part, n_parts, static_cast<const uint16_t*>(a.base),
+                       static_cast<const uint16_t*>(a.A), static_cast<const uint16_t*>(a.W), prev,
+                       prev_stride, a.temperature, a.K, a.V, a.r, k, a.tokens, a.logp, a.lse);
+    return hipGetLastError();
 }
 
 hipError_t launch_residual_mfma(const ResidualArgs& a) {
