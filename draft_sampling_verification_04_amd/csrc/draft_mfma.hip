@@ -354,11 +354,19 @@ __global__ __launch_bounds__(kCombineThreads) void draft_combine_mfma(
 
 // --------------------------------------------------------------- residual
 // For every request whose first rejection is at j* = a_b + 1 (sampled, T > 0):
-// recompute the draft logits z at j* (previous token x_{j*-1}), read the target
-// row y = t / T, and draw next ~ normalise(max(0, p_t - p_d)) by Gumbel-max of
+// recompute the draft logits at j* (previous token x_{j*-1}), read the target
+// row, and draw next ~ normalise(max(0, p_t - p_d)) by Gumbel-max of
 // log(p_t - p_d) over the positive entries (tag 2, position j*).  The Gumbel-max
-// of y with the same draws is kept as the fallback for a residual without
-// positive mass.  Rejected requests are listed in `list` (count entries).
+// of the target row with the same draws is kept as the fallback for a residual
+// without positive mass.  Rejected requests are listed in `list` (count
+// entries).
+// In base 2, with c = log2(e) / T: a = log2 p_t = t c - lse_t log2(e) and
+// d = log2 p_d = s c - lse_d log2(e), so p_t > p_d iff a > d and
+// log2(p_t - p_d) = a + log2(1 - 2^(d - a)).  Keys are log2 r - log2(-log2 u)
+// (residual) and a - log2(-log2 u) (fallback), each log2(e) (log x + G) up to
+// a constant shared by the row, so they order entries as the natural-log forms.
+// Persistent like the draft kernel: one workgroup per (part, slot group) walks
+// the strips part, part + n_parts, ... with W double-buffered in LDS.
 template <int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
@@ -368,75 +376,87 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     const float* __restrict__ temperature, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ list, const int32_t* __restrict__ count_ptr,
     const float* __restrict__ lse_tab, uint64_t seed, int K, int V, int r, PartialBuf res,
-    PartialBuf fall, int n_strips) {
-    extern __shared__ uint16_t w_sh[];
+    PartialBuf fall, int n_strips, int n_parts) {
+    extern __shared__ uint16_t w_sh[];  // two buffers of [r][kPitch]
     const int count = *count_ptr;
     const int slot0 = blockIdx.y * NWAVES * 32;
     if (slot0 >= count) return;  // whole workgroup idle
     const int lane = threadIdx.x & 63;
     const int kh = lane >> 5;
-    const int strip = blockIdx.x;
-    const int v0 = strip * kStripV;
     const int slot = slot0 + (threadIdx.x >> 6) * 32 + (lane & 31);
     const bool active = slot < count;
-    const int b = active ? list[slot] : 0;
-    const int js = active ? accepted[b] + 1 : 1;
-    stage_w<NWAVES>(w_sh, W, r, V, v0);
-    const int p = active ? clamp_token((js == 1) ? prev_token[b]
-                                                 : tokens[static_cast<size_t>(b) * K + js - 2],
-                                       V)
-                         : 0;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // lanes past the list run request list[0]'s rows and store nothing
+    const int b = list[active ? slot : 0];
+    const int js = accepted[b] + 1;
+    const int p = clamp_token((js == 1) ? prev_token[b]
+                                        : tokens[static_cast<size_t>(b) * K + js - 2],
+                              V);
+    const float c2 = inv_temperature(temperature[b]) * kLog2e;
+    const float ld2 = draft_lse[static_cast<size_t>(b) * K + js - 1] * kLog2e;
+    const float lt2 = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1] * kLog2e;
+    const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
+    const uint16_t* brow = base + (static_cast<size_t>(b) * K + js - 1) * V;
+    const uint16_t* trow = target + (row_off[b] + js - 1) * static_cast<int64_t>(V);
+    const int buf_elems = r * kPitch;
 
-    f32x16 acc[4];
-    bias_tiles(acc, w_sh, A + static_cast<size_t>(p) * r + 8 * kh, r, lane);
-    if (!active) return;
-
-    const int vh = v0 + 16 * kh;
-    uint4 bl[8], tl[8];
-    const bool tail = v0 + kStripV > V;
-    load_lane_logits(bl, base + (static_cast<size_t>(b) * K + js - 1) * V, vh, V, tail);
-    load_lane_logits(tl, target + (row_off[b] + js - 1) * static_cast<int64_t>(V), vh, V, tail);
-    const float it = inv_temperature(temperature[b]);
-    const float lse_d = draft_lse[static_cast<size_t>(b) * K + js - 1];
-    const float lse_t = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1];
-    float br = -INFINITY, bf = -INFINITY;
-    int ir = 0x7fffffff, jf = 0x7fffffff;
+    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
+    stage_w<NWAVES>(w_sh, W, r, V, s * kStripV);
+    RowState sr = row_empty(), sf = row_empty();
+    int buf = 0;
+    for (;;) {
+        __builtin_amdgcn_s_waitcnt(0);  // this strip's W (all waves' shares) has landed
+        __syncthreads();
+        const int sn = s + n_parts;
+        const bool more = sn < n_strips;
+        if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
+        const int v0 = s * kStripV;
+        const int vh = v0 + 16 * kh;
+        const bool tail = v0 + kStripV > V;
+        uint4 bl[8], tl[8];
+        load_lane_logits(bl, brow, vh, V, tail);
+        load_lane_logits(tl, trow, vh, V, tail);
+        f32x16 acc[4];
+        bias_tiles(acc, w_sh + buf * buf_elems, arow, r, lane);
+        float br = -INFINITY, bf = -INFINITY;
+        int ir = 0x7fffffff, jf = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e0 = entry_of(i, 0);
-        const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vh + e0) >> 2);
+        for (int i = 0; i < 16; ++i) {
+            const int e0 = entry_of(i, 0);
+            const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vh + e0) >> 2);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int v = vh + e0 + t;
-            if (v >= V) continue;
-            const float z = (logit_at(bl, i, t) + acc[t][i]) * it;
-            const float y = logit_at(tl, i, t) * it;
-            const float g = gumbel_fast(pick(rnd, t));
-            const float rv = expf(y - lse_t) - expf(z - lse_d);
-            if (rv > 0.0f) {
-                const float pr = logf(rv) + g;
-                if (pr > br) {
-                    br = pr;
-                    ir = v;
+            for (int t = 0; t < 4; ++t) {
+                const int v = vh + e0 + t;
+                const float d = fmaf(logit_at(bl, i, t) + acc[t][i], c2, -ld2);
+                const float a = fmaf(logit_at(tl, i, t), c2, -lt2);
+                const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, t)));
+                const float g2 = __builtin_amdgcn_logf(-l1);  // log2(-log2 u)
+                // entries past V have a = -inf and take part in neither draw
+                if (a > d) {
+                    const float kr =
+                        a + __builtin_amdgcn_logf(1.0f - __builtin_amdgcn_exp2f(d - a)) - g2;
+                    if (kr > br) {
+                        br = kr;
+                        ir = v;
+                    }
+                }
+                const float kf = a - g2;
+                if (kf > bf) {
+                    bf = kf;
+                    jf = v;
                 }
             }
-            const float pf = y + g;
-            if (pf > bf) {
-                bf = pf;
-                jf = v;
-            }
         }
-        __builtin_amdgcn_sched_barrier(0);
+        row_merge(sr, RowState{-INFINITY, 0.0f, br, br, ir});
+        row_merge(sf, RowState{-INFINITY, 0.0f, bf, bf, jf});
+        if (!more) break;
+        buf ^= 1;
+        s = sn;
     }
-    RowState sr = {-INFINITY, 0.0f, br, br, ir};
-    RowState sf = {-INFINITY, 0.0f, bf, bf, jf};
     row_merge(sr, shfl_xor_row(sr, 32));
     row_merge(sf, shfl_xor_row(sf, 32));
-    if (kh == 0) {
-        store_partial(res, static_cast<size_t>(slot) * n_strips + strip, sr);
-        store_partial(fall, static_cast<size_t>(slot) * n_strips + strip, sf);
+    if (active && kh == 0) {
+        store_partial(res, static_cast<size_t>(slot) * n_parts + blockIdx.x, sr);
+        store_partial(fall, static_cast<size_t>(slot) * n_parts + blockIdx.x, sf);
     }
 }
 
@@ -546,19 +566,22 @@ hipError_t launch_draft_strip(const DraftArgs& a, const int32_t* prev, int prev_
 }
 
 template <int NWAVES>
-hipError_t launch_residual_strip(const ResidualArgs& a) {
+hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
     static bool lds_ok = false;
     hipError_t e = allow_big_lds(&residual_strip_mfma<NWAVES>, lds_ok);
     if (e != hipSuccess) return e;
     const VerifyArgs& v = *a.v;
-    const size_t lds = sizeof(uint16_t) * static_cast<size_t>(v.r) * kPitch;
-    dim3 grid(static_cast<unsigned>(a.n_strips), static_cast<unsigned>(ceil_div(v.B, 32 * NWAVES)));
+    const size_t lds = 2 * sizeof(uint16_t) * static_cast<size_t>(v.r) * kPitch;
+    const int groups = static_cast<int>(ceil_div(v.B, 32 * NWAVES));
+    const int parts = std::max(1, std::min(a.n_strips, device_cus() / groups));
+    *n_parts = parts;
+    dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(groups));
     hipLaunchKernelGGL(residual_strip_mfma<NWAVES>, grid, dim3(64 * NWAVES), lds, v.stream,
                        static_cast<const uint16_t*>(v.base), static_cast<const uint16_t*>(v.A),
                        static_cast<const uint16_t*>(v.W), static_cast<const uint16_t*>(v.target),
                        v.row_off, v.tokens, v.prev_token, v.draft_lse, v.temperature, v.accepted,
                        a.list, a.count, a.lse_tab, v.seed, v.K, v.V, v.r, a.res, a.fall,
-                       a.n_strips);
+                       a.n_strips, parts);
     return hipGetLastError();
 }
 
@@ -576,7 +599,7 @@ bool mfma_supported(const DraftArgs& a) {
 
 bool residual_mfma_supported(const VerifyArgs& a) {
     return a.factor_dt == DSPARK_BF16 && a.logit_dt == DSPARK_BF16 && a.r % 16 == 0 &&
-           a.r <= 512 && a.V % 8 == 0 && aligned16(a.base) && aligned16(a.A) &&
+           a.r <= 256 && a.V % 8 == 0 && aligned16(a.base) && aligned16(a.A) &&
            aligned16(a.W) && aligned16(a.target);
 }
 
@@ -605,10 +628,10 @@ hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_
     return hipGetLastError();
 }
 
-hipError_t launch_residual_mfma(const ResidualArgs& a) {
-    if (a.v->B > 128) return launch_residual_strip<8>(a);
-    if (a.v->B > 64) return launch_residual_strip<4>(a);
-    return launch_residual_strip<2>(a);
+hipError_t launch_residual_mfma(const ResidualArgs& a, int* n_parts) {
+    if (a.v->B > 128) return launch_residual_strip<8>(a, n_parts);
+    if (a.v->B > 64) return launch_residual_strip<4>(a, n_parts);
+    return launch_residual_strip<2>(a, n_parts);
 }
 
 }  // namespace dspark

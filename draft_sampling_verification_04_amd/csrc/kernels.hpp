@@ -99,7 +99,7 @@ struct ResidualArgs {
     int n_strips;
 };
 bool residual_mfma_supported(const VerifyArgs& a);
-hipError_t launch_residual_mfma(const ResidualArgs& a);
+hipError_t launch_residual_mfma(const ResidualArgs& a, int* n_parts);
 hipError_t launch_verify(const VerifyArgs& a);
 
 constexpr int kMaxCurvePoints = 64;

@@ -441,7 +441,7 @@ hipError_t launch_verify(const VerifyArgs& a) {
     if (residual_mfma_supported(a)) {
         n_strips = static_cast<int>(ceil_div(a.V, kMfmaStrip));
         ResidualArgs ra{&a, ws.list, ws.count, ws.lse, ws.res, ws.fall, n_strips};
-        e = launch_residual_mfma(ra);
+        e = launch_residual_mfma(ra, &n_strips);  // partials per listed request
         if (e != hipSuccess) return e;
     } else {
         n_strips = static_cast<int>(ceil_div(a.V, kValuStrip));
