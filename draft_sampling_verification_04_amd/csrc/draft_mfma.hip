@@ -277,12 +277,17 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
         __syncthreads();
         const int sn = s + n_parts;
         const bool more = sn < n_strips;
-        if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
         f32x16 acc[4];
         bias_tiles(acc, w_sh + buf * buf_elems, arow, r, lane);
+        // The next strip's W and logits are requested only now: the vector
+        // memory counter retires loads in order, so a prefetch issued before
+        // the factor-fragment loads of the MFMA loop would stall that loop
+        // until the whole prefetch had landed.
         uint4 bn[8];
-        if (more)
+        if (more) {
+            stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
             load_lane_logits(bn, brow, sn * kStripV + 16 * kh, V, sn * kStripV + kStripV > V);
+        }
         // lane entries: strip start + 16 kh + entry_of(i, t)
         row_merge(run, draft_epilogue(acc, bl, s * kStripV + 16 * kh, T, seed, b, k + 1));
         if (!more) break;
@@ -385,6 +390,8 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     const int kh = lane >> 5;
     const int slot = slot0 + (threadIdx.x >> 6) * 32 + (lane & 31);
     const bool active = slot < count;
+    // waves wholly past the list only help stage W and meet the barriers
+    const bool wave_busy = slot0 + (threadIdx.x >> 6) * 32 < count;
     // lanes past the list run request list[0]'s rows and store nothing
     const int b = list[active ? slot : 0];
     const int js = accepted[b] + 1;
@@ -408,7 +415,13 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
         __syncthreads();
         const int sn = s + n_parts;
         const bool more = sn < n_strips;
-        if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
+        if (!wave_busy) {
+            if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
+            if (!more) break;
+            buf ^= 1;
+            s = sn;
+            continue;
+        }
         const int v0 = s * kStripV;
         const int vh = v0 + 16 * kh;
         const bool tail = v0 + kStripV > V;
@@ -417,6 +430,8 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
         load_lane_logits(tl, trow, vh, V, tail);
         f32x16 acc[4];
         bias_tiles(acc, w_sh + buf * buf_elems, arow, r, lane);
+        // requested after the MFMA loop's factor loads (in-order load counter)
+        if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
         float br = -INFINITY, bf = -INFINITY;
         int ir = 0x7fffffff, jf = 0x7fffffff;
 #pragma unroll
