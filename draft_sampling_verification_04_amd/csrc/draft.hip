@@ -172,8 +172,9 @@ void launch_valu_strip(const DraftArgs& a, const int32_t* prev, int prev_stride,
 // Implemented in draft_mfma.hip.
 bool mfma_supported(const DraftArgs& a);
 int mfma_draft_strip();
-hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts,
-                                    const int32_t* prev, int prev_stride, int k);
+hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts, int k,
+                                    float* lse_ws);
+hipError_t launch_draft_logp_mfma(const DraftArgs& a, const float* lse_ws);
 hipError_t launch_temperature_order(const float* temperature, int B, int32_t* order,
                                     hipStream_t stream);
 hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
@@ -185,27 +186,32 @@ namespace {
 struct DraftWs {
     PartialBuf part;
     int32_t* order;
+    float* lse;  // [B, K] lse_d, kept for the deferred log-probabilities
 };
 
-DraftWs draft_ws(void* ws, int B, int V) {
+DraftWs draft_ws(void* ws, int B, int K, int V) {
     const size_t n = static_cast<size_t>(B) * ceil_div(V, kMinStrip);  // the largest strip count
     char* w = static_cast<char*>(ws);
     DraftWs d;
-    d.part.v = reinterpret_cast<float4*>(w);
-    d.part.idx = reinterpret_cast<int32_t*>(w + align256(n * sizeof(float4)));
-    d.order = reinterpret_cast<int32_t*>(w + align256(n * sizeof(float4)) +
-                                         align256(n * sizeof(int32_t)));
+    size_t o = 0;
+    d.part.v = reinterpret_cast<float4*>(w + o);
+    o += align256(n * sizeof(float4));
+    d.part.idx = reinterpret_cast<int32_t*>(w + o);
+    o += align256(n * sizeof(int32_t));
+    d.order = reinterpret_cast<int32_t*>(w + o);
+    o += align256(static_cast<size_t>(B) * sizeof(int32_t));
+    d.lse = reinterpret_cast<float*>(w + o);
     return d;
 }
 
 }  // namespace
 
 size_t draft_workspace_bytes(int B, int K, int V, int r) {
-    (void)K;
     (void)r;
     const size_t n = static_cast<size_t>(B) * ceil_div(V, kMinStrip);
     return align256(n * sizeof(float4)) + align256(n * sizeof(int32_t)) +
-           align256(static_cast<size_t>(B) * sizeof(int32_t));
+           align256(static_cast<size_t>(B) * sizeof(int32_t)) +
+           align256(static_cast<size_t>(B) * K * sizeof(float));
 }
 
 bool draft_uses_mfma(const DraftArgs& a) { return mfma_supported(a); }
@@ -214,7 +220,7 @@ hipError_t launch_draft(const DraftArgs& a) {
     if (a.B == 0 || a.K == 0) return hipSuccess;
     const bool mfma = draft_uses_mfma(a);
     const int n_strips = static_cast<int>(ceil_div(a.V, mfma ? mfma_draft_strip() : kValuStrip));
-    const DraftWs ws = draft_ws(a.ws, a.B, a.V);
+    const DraftWs ws = draft_ws(a.ws, a.B, a.K, a.V);
     if (mfma) {
         hipError_t e = launch_temperature_order(a.temperature, a.B, ws.order, a.stream);
         if (e != hipSuccess) return e;
@@ -243,13 +249,18 @@ hipError_t launch_draft(const DraftArgs& a) {
         strip_scope.slot = -1;
         ProfScope combine_scope(DSPARK_KERNEL_DRAFT_COMBINE, a.stream);
         if (mfma) {
-            e = launch_draft_combine_mfma(a, ws.part, n_parts, prev, prev_stride, k);
+            e = launch_draft_combine_mfma(a, ws.part, n_parts, k, ws.lse);
         } else {
             hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)),
                                dim3(kCombineThreads), 0, a.stream, ws.part, n_parts,
                                a.temperature, a.K, k, a.tokens, a.logp, a.lse);
             e = hipGetLastError();
         }
+        if (e != hipSuccess) return e;
+    }
+    if (mfma && a.logp) {
+        ProfScope logp_scope(DSPARK_KERNEL_DRAFT_LOGP, a.stream);
+        hipError_t e = launch_draft_logp_mfma(a, ws.lse);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -302,58 +302,57 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
 }
 
-// Fold the partials of each request (one 256-thread workgroup per request) and
-// write x_k, log p_d(x_k) and lse_d.  For T > 0 the partials carry the winner's
-// index but not its logit, so the winning entry's z = (base + A[x_{k-1}] . W[:, v]) / T
-// is recomputed here (one rank-r dot product per request).
-constexpr int kCombineThreads = 256;
-
-__global__ __launch_bounds__(kCombineThreads) void draft_combine_mfma(
-    PartialBuf part, int n_parts, const uint16_t* __restrict__ base,
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ prev, int prev_stride, const float* __restrict__ temperature,
-    int K, int V, int r, int k, int32_t* __restrict__ tokens, float* __restrict__ logp,
-    float* __restrict__ lse) {
-    __shared__ RowState red[kCombineThreads / kWave];
-    __shared__ float dsum[kCombineThreads / kWave];
-    __shared__ int win;
+// Fold the partials of each request (one wavefront per request) and write x_k
+// and lse_d (the row maximum for T == 0) for step k.  The winner's logit is
+// not in the partials; log p_d(x_k) is filled in after the last step by
+// draft_logp_mfma, off the sequential path.
+__global__ __launch_bounds__(kWave) void draft_combine_mfma(
+    PartialBuf part, int n_parts, const float* __restrict__ temperature, int K, int k,
+    int32_t* __restrict__ tokens, float* __restrict__ lse, float* __restrict__ lse_ws) {
     const int b = blockIdx.x;
-    const int tid = threadIdx.x;
     RowState st = row_empty();
-    for (int s = tid; s < n_parts; s += kCombineThreads)
+    for (int s = threadIdx.x; s < n_parts; s += kWave)
         row_merge(st, load_partial(part, static_cast<size_t>(b) * n_parts + s));
-    st = block_reduce_row<kCombineThreads>(st, red);
+    wave_reduce_row(st);
+    if (threadIdx.x == 0) {
+        const size_t o = static_cast<size_t>(b) * K + k;
+        const float l = (temperature[b] > 0.0f) ? st.m + logf(st.s) : st.pert;
+        tokens[o] = st.idx;
+        lse_ws[o] = l;
+        if (lse) lse[o] = l;
+    }
+}
+
+// log p_d(x_k) = z_{x_k} - lse_d for every (request, step), one wavefront each:
+// z = (base + A[x_{k-1}] . W[:, x_k]) / T, the bias recomputed as one rank-r
+// dot product; 0 for T == 0.
+__global__ __launch_bounds__(256) void draft_logp_mfma(
+    const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ W, const int32_t* __restrict__ prev_token,
+    const float* __restrict__ temperature, const int32_t* __restrict__ tokens,
+    const float* __restrict__ lse_ws, float* __restrict__ logp, int B, int K, int V, int r) {
+    const int lane = threadIdx.x & 63;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (g >= static_cast<int64_t>(B) * K) return;  // whole wavefront
+    const int b = static_cast<int>(g / K);
+    const int k = static_cast<int>(g - static_cast<int64_t>(b) * K);
     const float T = temperature[b];
-    if (tid == 0) win = clamp_token(st.idx, V);
-    __syncthreads();
-    const size_t o = static_cast<size_t>(b) * K + k;
     if (!(T > 0.0f)) {
-        if (tid == 0) {
-            tokens[o] = st.idx;
-            if (lse) lse[o] = st.pert;
-            if (logp) logp[o] = 0.0f;
-        }
+        if (lane == 0) logp[g] = 0.0f;
         return;
     }
-    const int v = win;
-    const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
+    const int v = clamp_token(tokens[g], V);
+    const int p = clamp_token((k == 0) ? prev_token[b] : tokens[g - 1], V);
     float d = 0.0f;
-    for (int i = tid; i < r; i += kCombineThreads)
+    for (int i = lane; i < r; i += kWave)
         d = fmaf(to_f32(bf16_t{A[static_cast<size_t>(p) * r + i]}),
                  to_f32(bf16_t{W[static_cast<size_t>(i) * V + v]}), d);
 #pragma unroll
     for (int m = kWave / 2; m > 0; m >>= 1) d += __shfl_xor(d, m, kWave);
-    if ((tid & 63) == 0) dsum[tid >> 6] = d;
-    __syncthreads();
-    if (tid == 0) {
-        float bias = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kCombineThreads / kWave; ++w) bias += dsum[w];
-        const float z = (to_f32(bf16_t{base[o * V + v]}) + bias) * inv_temperature(T);
-        const float l = st.m + logf(st.s);
-        tokens[o] = st.idx;
-        if (lse) lse[o] = l;
-        if (logp) logp[o] = z - l;
+    if (lane == 0) {
+        const float z = (to_f32(bf16_t{base[static_cast<size_t>(g) * V + v]}) + d) *
+                        inv_temperature(T);
+        logp[g] = z - lse_ws[g];
     }
 }
 
@@ -634,12 +633,19 @@ hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int p
     return launch_draft_strip<2>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
 }
 
-hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts,
-                                    const int32_t* prev, int prev_stride, int k) {
-    hipLaunchKernelGGL(draft_combine_mfma, dim3(static_cast<unsigned>(a.B)), dim3(kCombineThreads),
-                       0, a.stream, part, n_parts, static_cast<const uint16_t*>(a.base),
-                       static_cast<const uint16_t*>(a.A), static_cast<const uint16_t*>(a.W), prev,
-                       prev_stride, a.temperature, a.K, a.V, a.r, k, a.tokens, a.logp, a.lse);
+hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts, int k,
+                                    float* lse_ws) {
+    hipLaunchKernelGGL(draft_combine_mfma, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0,
+                       a.stream, part, n_parts, a.temperature, a.K, k, a.tokens, a.lse, lse_ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_draft_logp_mfma(const DraftArgs& a, const float* lse_ws) {
+    const int64_t n = static_cast<int64_t>(a.B) * a.K;
+    hipLaunchKernelGGL(draft_logp_mfma, dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0,
+                       a.stream, static_cast<const uint16_t*>(a.base),
+                       static_cast<const uint16_t*>(a.A), static_cast<const uint16_t*>(a.W),
+                       a.prev_token, a.temperature, a.tokens, lse_ws, a.logp, a.B, a.K, a.V, a.r);
     return hipGetLastError();
 }
 

@@ -186,7 +186,8 @@ typedef enum dspark_kernel {
     DSPARK_KERNEL_RESIDUAL_STRIP = 4,    /* verify: residual / fallback Gumbel over a vocab strip */
     DSPARK_KERNEL_RESIDUAL_COMBINE = 5,  /* verify: merge of the residual partials */
     DSPARK_KERNEL_SCHEDULE = 6,          /* schedule: survival, selection and row offsets */
-    DSPARK_KERNEL_COUNT = 7
+    DSPARK_KERNEL_DRAFT_LOGP = 7,        /* draft: log p_d of the drawn tokens, once per call */
+    DSPARK_KERNEL_COUNT = 8
 } dspark_kernel;
 
 /* Open a session timing at most max_launches launches (events are created
