@@ -75,14 +75,20 @@ __device__ __forceinline__ void load8<float>(const float* row, int v0, int V, bo
     }
 }
 
+// verify_rows: one 512-thread workgroup per visited row with two 16-byte loads
+// in flight per lane (measured best among 64 / 256 / 512 / 1024 threads and
+// one, two or four loads per lane).
+constexpr int kVRowThreads = 512;
+constexpr int kVRowUnroll = 2;
+
 template <typename LT>
-__global__ __launch_bounds__(kRowThreads) void verify_rows(
+__global__ __launch_bounds__(kVRowThreads) void verify_rows(
     const LT* __restrict__ target, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ lengths, const int32_t* __restrict__ tokens,
     const float* __restrict__ draft_logp, const float* __restrict__ temperature, uint64_t seed,
     int K, int V, int64_t n_rows, bool vec_ok, float* __restrict__ row_lse_t,
     float* __restrict__ row_logratio, VerifyWs ws) {
-    __shared__ RowState red[kRowThreads / kWave];
+    __shared__ RowState red[kVRowThreads / kWave];
     const int64_t id = blockIdx.x;
     const int b = static_cast<int>(id / (K + 1));
     const int j = static_cast<int>(id - static_cast<int64_t>(b) * (K + 1)) + 1;
@@ -100,14 +106,23 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows(
         // argmax of t, smallest index on ties (visited in increasing v per thread)
         float best = -INFINITY;
         int bi = 0x7fffffff;
-        for (int v0 = threadIdx.x * 8; v0 < V; v0 += kRowThreads * 8) {
-            float x[8];
-            load8<LT>(trow, v0, V, vec, x);
+        for (int c0 = threadIdx.x * 8; c0 < V; c0 += kVRowThreads * 8 * kVRowUnroll) {
+            float xs[kVRowUnroll][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (x[e] > best) {
-                    best = x[e];
-                    bi = v0 + e;
+            for (int u = 0; u < kVRowUnroll; ++u) {
+                const int v0 = c0 + u * kVRowThreads * 8;
+                if (v0 < V) load8<LT>(trow, v0, V, vec, xs[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kVRowUnroll; ++u) {
+                const int v0 = c0 + u * kVRowThreads * 8;
+                if (v0 >= V) break;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (xs[u][e] > best) {
+                        best = xs[u][e];
+                        bi = v0 + e;
+                    }
                 }
             }
         }
@@ -122,9 +137,18 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows(
         float m = -INFINITY, s = 0.0f;
         float best = -INFINITY, bz = -INFINITY;
         int bi = 0x7fffffff;
-        for (int v0 = threadIdx.x * 8; v0 < V; v0 += kRowThreads * 8) {
-            float x[8];
-            load8<LT>(trow, v0, V, vec, x);
+        for (int c0 = threadIdx.x * 8; c0 < V; c0 += kVRowThreads * 8 * kVRowUnroll) {
+          float xs[kVRowUnroll][8];
+#pragma unroll
+          for (int u = 0; u < kVRowUnroll; ++u) {
+            const int v0 = c0 + u * kVRowThreads * 8;
+            if (v0 < V) load8<LT>(trow, v0, V, vec, xs[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < kVRowUnroll; ++u) {
+            const int v0 = c0 + u * kVRowThreads * 8;
+            if (v0 >= V) break;
+            const float (&x)[8] = xs[u];
             float cm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             if (cm > m) {
@@ -148,6 +172,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows(
                     }
                 }
             }
+          }
         }
         // express (m, s) on the y = t / T scale for the shared merge
         st.m = m * it;
@@ -156,7 +181,7 @@ __global__ __launch_bounds__(kRowThreads) void verify_rows(
         st.zb = bz;
         st.idx = bi;
     }
-    st = block_reduce_row<kRowThreads>(st, red);
+    st = block_reduce_row<kVRowThreads>(st, red);
     if (threadIdx.x == 0) {
         const size_t slot = static_cast<size_t>(b) * (K + 1) + (j - 1);
         const float lse_t = greedy ? st.pert : st.m + logf(st.s);
@@ -413,12 +438,12 @@ hipError_t launch_verify(const VerifyArgs& a) {
     const bool vec_ok = aligned16(a.target);
     ProfScope rows_scope(DSPARK_KERNEL_VERIFY_ROWS, a.stream);
     if (a.logit_dt == DSPARK_BF16) {
-        hipLaunchKernelGGL(verify_rows<bf16_t>, rows_grid, dim3(kRowThreads), 0, a.stream,
+        hipLaunchKernelGGL(verify_rows<bf16_t>, rows_grid, dim3(kVRowThreads), 0, a.stream,
                            static_cast<const bf16_t*>(a.target), a.row_off, a.lengths, a.tokens,
                            a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
                            a.row_lse_t, a.row_logratio, ws);
     } else {
-        hipLaunchKernelGGL(verify_rows<float>, rows_grid, dim3(kRowThreads), 0, a.stream,
+        hipLaunchKernelGGL(verify_rows<float>, rows_grid, dim3(kVRowThreads), 0, a.stream,
                            static_cast<const float*>(a.target), a.row_off, a.lengths, a.tokens,
                            a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
                            a.row_lse_t, a.row_logratio, ws);
