@@ -302,6 +302,211 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
 }
 
+// ------------------------------------------------- draft: strip in two halves
+// Half h of a 128-entry strip is two 32-row tiles; row m of tile t is entry
+// v0 + 64 h + 2 m + t, so an A-operand lane reads the two entries of a rank row
+// with one 4-byte LDS read (32 lanes cover 128 contiguous bytes), and output
+// lane l's accumulator i of tile t is entry v0 + 64 h + 16 (i / 4) + 8 (l / 32)
+// + 2 (i % 4) + t: run i / 4 is 8 consecutive entries (one 16-byte logit chunk,
+// two Philox blocks).  Working on one half at a time keeps 32 accumulators
+// live, which leaves room to hold the factor fragments in registers.
+// KS = r / 16 rank steps, fixed at compile time so that the step loop is fully
+// unrolled without guards (per-step guards split it into branches that stall
+// the MFMA pipeline).
+template <int KS>
+__device__ __forceinline__ void bias_half(f32x16 (&acc)[2], const uint16_t* wl,
+                                          const uint4 (&afr)[KS]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    uint32_t d[2][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[0][j] = *reinterpret_cast<const uint32_t*>(wl + j * kPitch);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        {
+            if (kk + 1 < KS) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    d[(kk + 1) & 1][j] =
+                        *reinterpret_cast<const uint32_t*>(wl + ((kk + 1) * 16 + j) * kPitch);
+            }
+            const uint32_t (&c)[8] = d[kk & 1];
+            const bf16x8 bv = as_bf16x8(afr[kk]);
+            uint4 a;
+            a = make_uint4(__builtin_amdgcn_perm(c[1], c[0], 0x05040100u),
+                           __builtin_amdgcn_perm(c[3], c[2], 0x05040100u),
+                           __builtin_amdgcn_perm(c[5], c[4], 0x05040100u),
+                           __builtin_amdgcn_perm(c[7], c[6], 0x05040100u));
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[0], 0, 0, 0);
+            a = make_uint4(__builtin_amdgcn_perm(c[1], c[0], 0x07060302u),
+                           __builtin_amdgcn_perm(c[3], c[2], 0x07060302u),
+                           __builtin_amdgcn_perm(c[5], c[4], 0x07060302u),
+                           __builtin_amdgcn_perm(c[7], c[6], 0x07060302u));
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[1], 0, 0, 0);
+        }
+    }
+}
+
+// The lane's 64 logits of one strip: chunk 4 h + a holds entries
+// v0 + 64 h + 16 a + 8 kh .. + 7.  Loads are in bounds (the last chunk of the
+// row stands in past V) and chunks past V become bf16 -inf.
+__device__ __forceinline__ void load_strip_logits(uint4 (&q)[8], const uint16_t* row, int v0,
+                                                  int kh, int V) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int v = v0 + 64 * (c >> 2) + 16 * (c & 3) + 8 * kh;
+        q[c] = *reinterpret_cast<const uint4*>(row + min(v, V - 8));
+    }
+    if (v0 + kStripV > V) {
+        const uint32_t ninf2 = 0xFF80FF80u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int v = v0 + 64 * (c >> 2) + 16 * (c & 3) + 8 * kh;
+            if (v >= V) q[c] = make_uint4(ninf2, ninf2, ninf2, ninf2);
+        }
+    }
+}
+
+// Running state of a lane over the halves and strips it visits (sampled or
+// greedy; see draft_epilogue for the key).
+__device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], const uint4 (&bl)[8],
+                                              int h, int vh, float T, uint64_t seed, int b,
+                                              uint32_t pos) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t dw = dword_of(bl[4 * h + (i >> 2)], i & 3);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float lg = __uint_as_float(t ? (dw & 0xFFFF0000u) : (dw << 16));
+            const float sv = lg + acc[t][i];
+            acc[t][i] = sv;
+            mx = fmaxf(mx, sv);
+        }
+    }
+    RowState st = row_empty();
+    float best = -INFINITY;
+    int be = 0;
+    if (T > 0.0f) {
+        const float it = inv_temperature(T);
+        const float c2 = it * kLog2e;
+        const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
+        float sum = 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            const int i0 = 4 * (blk >> 1) + 2 * (blk & 1);    // accumulators i0, i0 + 1
+            const int e0 = 16 * (blk >> 1) + 4 * (blk & 1);  // lane entry offset of the block
+            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh + e0) >> 2);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int i = i0 + (w >> 1);
+                const int t = w & 1;
+                const float arg = fmaf(acc[t][i], c2, -mc);
+                sum += __builtin_amdgcn_exp2f(arg);
+                const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, w)));
+                const float key = arg - __builtin_amdgcn_logf(-l1);
+                if (key > best) {
+                    best = key;
+                    be = e0 + w;
+                }
+            }
+        }
+        st.m = mx * it;
+        st.s = sum;
+        st.pert = best + mc;
+        st.zb = 0.0f;
+        st.idx = vh + be;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (acc[t][i] > best) {
+                    best = acc[t][i];
+                    be = 16 * (i >> 2) + 2 * (i & 3) + t;
+                }
+            }
+        }
+        st.pert = best;
+        st.zb = best;
+        st.idx = vh + be;
+    }
+    row_merge(run, st);
+}
+
+// One workgroup per (part, request group), persistent over the strips part,
+// part + n_parts, ...: the factor fragments of each lane's request are loaded
+// once and stay in registers, so the MFMA loops issue no vector-memory loads
+// and the next strip's W (into the other LDS buffer) and logits (into
+// registers) are requested as soon as a strip starts.  Each lane folds the
+// halves and strips it visits into one running state, so a request gets
+// n_parts partials per step.
+template <int NWAVES, int KS>
+__global__ __launch_bounds__(64 * NWAVES)
+void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
+                      const uint16_t* __restrict__ W, const int32_t* __restrict__ prev,
+                      int prev_stride, const float* __restrict__ temperature,
+                      const int32_t* __restrict__ order, uint64_t seed, int B, int K, int V,
+                      int r, int k, PartialBuf part, int n_strips, int n_parts) {
+    extern __shared__ uint16_t w_sh[];  // two buffers of [r][kPitch]
+    const int lane = threadIdx.x & 63;
+    const int kh = lane >> 5;
+    const int slot = (blockIdx.y * NWAVES + (threadIdx.x >> 6)) * 32 + (lane & 31);
+    const bool active = slot < B;
+    // lanes past B run request 0's row (every wave takes part in the MFMAs and
+    // barriers) and store nothing
+    const int b = active ? order[slot] : 0;
+    const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
+    const float T = temperature[b];
+    const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
+    const uint16_t* brow = base + (static_cast<size_t>(b) * K + k) * V;
+    const int buf_elems = r * kPitch;
+    uint4 afr[KS];  // r == 16 KS
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
+    const int wl_off = (8 * kh) * kPitch + 2 * (lane & 31);
+
+    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
+    stage_w<NWAVES>(w_sh, W, r, V, s * kStripV);
+    uint4 bl[8];
+    load_strip_logits(bl, brow, s * kStripV, kh, V);
+    RowState run = row_empty();
+    int buf = 0;
+    for (;;) {
+        // this strip's W (all waves' shares) and logits have landed, and every
+        // wave is done with the other buffer
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int sn = s + n_parts;
+        const bool more = sn < n_strips;
+        // the MFMA loops issue no vector-memory loads, so the next strip's data
+        // can be requested at once
+        uint4 bn[8];
+        if (more) {
+            stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
+            load_strip_logits(bn, brow, sn * kStripV, kh, V);
+        }
+        const uint16_t* wl = w_sh + buf * buf_elems + wl_off;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x16 acc[2];
+            bias_half<KS>(acc, wl + 64 * h, afr);
+            epilogue_half(run, acc, bl, h, s * kStripV + 64 * h + 8 * kh, T, seed, b, k + 1);
+        }
+        if (!more) break;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bl[c] = bn[c];
+        buf ^= 1;
+        s = sn;
+    }
+    // lanes l and l + 32 hold the two halves of every strip for one request
+    row_merge(run, shfl_xor_row(run, 32));
+    if (active && kh == 0)
+        store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
+}
+
 // Fold the partials of each request (one wavefront per request) and write x_k
 // and lse_d (the row maximum for T == 0) for step k.  The winner's logit is
 // not in the partials; log p_d(x_k) is filled in after the last step by
@@ -559,12 +764,11 @@ int device_cus() {
     return cus[dev];
 }
 
-template <int NWAVES>
-hipError_t launch_draft_strip(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
-                              const int32_t* order, PartialBuf part, int n_strips,
-                              int* n_parts) {
-    static bool lds_ok = false;
-    hipError_t e = allow_big_lds(&draft_strip_mfma<NWAVES>, lds_ok);
+template <int NWAVES, typename Kern>
+hipError_t launch_draft_strip(Kern* kern, bool& lds_ok, const DraftArgs& a, const int32_t* prev,
+                              int prev_stride, int k, const int32_t* order, PartialBuf part,
+                              int n_strips, int* n_parts) {
+    hipError_t e = allow_big_lds(kern, lds_ok);
     if (e != hipSuccess) return e;
     const size_t lds = 2 * sizeof(uint16_t) * static_cast<size_t>(a.r) * kPitch;
     // one resident workgroup per CU (the two W buffers take most of the LDS)
@@ -572,11 +776,26 @@ hipError_t launch_draft_strip(const DraftArgs& a, const int32_t* prev, int prev_
     const int parts = std::max(1, std::min(n_strips, device_cus() / groups));
     *n_parts = parts;
     dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(groups));
-    hipLaunchKernelGGL(draft_strip_mfma<NWAVES>, grid, dim3(64 * NWAVES), lds, a.stream,
+    hipLaunchKernelGGL(kern, grid, dim3(64 * NWAVES), lds, a.stream,
                        static_cast<const uint16_t*>(a.base), static_cast<const uint16_t*>(a.A),
                        static_cast<const uint16_t*>(a.W), prev, prev_stride, a.temperature, order,
                        a.seed, a.B, a.K, a.V, a.r, k, part, n_strips, parts);
     return hipGetLastError();
+}
+
+// Rank 256 takes the register-factor kernel; other ranks the runtime-rank one.
+template <int NWAVES>
+hipError_t launch_draft_step_nw(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
+                                const int32_t* order, PartialBuf part, int n_strips,
+                                int* n_parts) {
+    if (a.r == 256) {
+        static bool lds_ok = false;
+        return launch_draft_strip<NWAVES>(&draft_strip_mfma_rk<NWAVES, 16>, lds_ok, a, prev,
+                                          prev_stride, k, order, part, n_strips, n_parts);
+    }
+    static bool lds_ok = false;
+    return launch_draft_strip<NWAVES>(&draft_strip_mfma<NWAVES>, lds_ok, a, prev, prev_stride, k,
+                                      order, part, n_strips, n_parts);
 }
 
 template <int NWAVES>
@@ -627,10 +846,10 @@ hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int p
                                   const int32_t* order, PartialBuf part, int n_strips,
                                   int* n_parts) {
     if (a.B > 128)
-        return launch_draft_strip<8>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
+        return launch_draft_step_nw<8>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
     if (a.B > 64)
-        return launch_draft_strip<4>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
-    return launch_draft_strip<2>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
+        return launch_draft_step_nw<4>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
+    return launch_draft_step_nw<2>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
 }
 
 hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts, int k,

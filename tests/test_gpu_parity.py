@@ -86,6 +86,10 @@ def test_tiny_full_parity(dsp, orc, inputs):
     (5, 16, 4, 4, torch.bfloat16, torch.float32),
     (1, 16, 2, 2, torch.float32, torch.float32),
     (4099, 48, 5, 9, torch.float32, torch.float32),
+    # rank 256 takes the register-factor kernel: a ragged last strip, a request
+    # count that leaves lanes idle, and a one-chunk vocabulary
+    (1000, 256, 3, 40, torch.bfloat16, torch.bfloat16),
+    (8, 256, 2, 3, torch.bfloat16, torch.bfloat16),
 ])
 def test_small_shapes_parity(dsp, orc, inputs, V, r, K, B, ldt, fdt):
     w = inputs.resized(inputs.WORKLOADS["long_draft"], B=B, K=K, V=V, r=r, dtype=ldt)
