@@ -1,0 +1,176 @@
+"""GPU edge cases through the C ABI: exact ties (smallest index wins on every
+path and across strips and lanes), the smallest batch and draft length,
+extreme temperatures, a flat distribution, and degenerate schedules.  Where a
+result has a closed form it is checked directly; elsewhere against the oracle
+with the near-tie rule of tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+# (V, r, logit dtype, factor dtype): the rank-256 register-factor kernel, the
+# runtime-rank MFMA kernel, the VALU path (fp32), and a vocabulary that is not a
+# multiple of 8 (VALU path for bf16)
+PATHS = [
+    (2000, 256, torch.bfloat16, torch.bfloat16),
+    (2000, 32, torch.bfloat16, torch.bfloat16),
+    (2000, 16, torch.float32, torch.float32),
+    (2003, 16, torch.bfloat16, torch.bfloat16),
+]
+
+
+@pytest.fixture(scope="module")
+def dsp():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import draft_sampling_verification_04_amd as d
+
+    d.lib()
+    return d
+
+
+def _zeros(B, K, V, r, ldt, fdt):
+    dev = "cuda"
+    return dict(base=torch.zeros((B, K, V), dtype=ldt, device=dev),
+                A=torch.zeros((V, r), dtype=fdt, device=dev),
+                W=torch.zeros((r, V), dtype=fdt, device=dev),
+                prev=torch.arange(B, dtype=torch.int32, device=dev) % V,
+                temp=torch.zeros(B, dtype=torch.float32, device=dev))
+
+
+@pytest.mark.parametrize("V,r,ldt,fdt", PATHS)
+def test_greedy_ties_take_the_smallest_index(dsp, V, r, ldt, fdt):
+    B, K = 37, 3
+    inp = _zeros(B, K, V, r, ldt, fdt)
+    # every entry ties at 0: token 0 at every step
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], 1)
+    torch.cuda.synchronize()
+    assert (tok == 0).all()
+    assert (logp == 0).all() and (lse == 0).all()
+    # two maxima, in different strips, lanes and (for 777 / 1500) MFMA tiles
+    inp["base"][:, :, 1500] = 5.0
+    inp["base"][:, :, 777] = 5.0
+    inp["base"][:, 1, 3] = 5.0  # step 2: an earlier tie
+    tok, _, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                          inp["temp"], 1)
+    torch.cuda.synchronize()
+    assert (tok[:, 0] == 777).all() and (tok[:, 1] == 3).all() and (tok[:, 2] == 777).all()
+    assert torch.allclose(lse, torch.full_like(lse, 5.0))
+    # verify at T = 0: accept iff the draft token is the target argmax (ties to
+    # the smallest index); request 0's first row has its maximum at 5 and 9
+    target = torch.zeros((B * (K + 1), V), dtype=ldt, device="cuda")
+    target[:, 777] = 2.0
+    target[1:, 3] = 2.0  # every row but request 0's first: tie between 3 and 777
+    target[0, 5] = 3.0
+    target[0, 9] = 3.0
+    offs = torch.arange(B, dtype=torch.int64, device="cuda") * (K + 1)
+    acc, nxt, rl, rr = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                         inp["W"], target, offs, inp["temp"], 1)
+    torch.cuda.synchronize()
+    # request 0: row 1 argmax 5 != 777 -> reject at once, next = 5
+    assert int(acc[0]) == 0 and int(nxt[0]) == 5
+    # others: row 1 argmax is 3 (tie 3 / 777) != 777 -> reject at once, next = 3
+    assert (acc[1:] == 0).all() and (nxt[1:] == 3).all()
+    assert rr[0] == float("-inf")
+
+
+@pytest.mark.parametrize("V,r,ldt,fdt", PATHS)
+def test_single_request_single_step(dsp, orc, V, r, ldt, fdt):
+    from draft_sampling_verification_04_amd import inputs
+
+    w = inputs.resized(inputs.WORKLOADS["qwen3_4b"], B=1, K=1, V=V, r=r, dtype=ldt,
+                       temps=(0.7,))
+    inp = inputs.make_inputs(w, "cuda", seed=V + r)
+    inp["A"] = inp["A"].to(fdt)
+    inp["W"] = inp["W"].to(fdt)
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], 9)
+    torch.cuda.synchronize()
+    ora = P.oracle_draft(orc, inp, [0], 9)
+    tally = P.Tally()
+    P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
+                    inp["temp"].cpu().numpy(), P.tol_for(ldt), tally)
+    assert tally.compared + tally.near_ties == 1
+
+
+@pytest.mark.parametrize("T", [0.05, 5.0])
+def test_extreme_temperatures(dsp, orc, T):
+    from draft_sampling_verification_04_amd import inputs
+
+    w = inputs.resized(inputs.WORKLOADS["qwen3_4b"], B=40, K=3, V=3000, r=256, temps=(T,))
+    inp = inputs.make_inputs(w, "cuda", seed=int(T * 100))
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], 21)
+    torch.cuda.synchronize()
+    idx = [0, 7, 33, 39]
+    ora = P.oracle_draft(orc, inp, idx, 21)
+    tally = P.Tally()
+    P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
+                    inp["temp"].cpu().numpy(), P.tol_for(torch.bfloat16), tally)
+    assert tally.compared >= 3 * len(idx) - 3
+    # verify the same rows against the oracle
+    V, K = w.V, w.K
+    target = inp["target"].reshape(-1, V)
+    for b in idx:
+        tok[b] = torch.from_numpy(ora[b][0]).to(tok.device)
+        logp[b] = torch.from_numpy(ora[b][1]).to(tok.device)
+        lse[b] = torch.from_numpy(ora[b][2]).to(tok.device)
+    offs = torch.arange(w.B, dtype=torch.int64, device="cuda") * (K + 1)
+    acc, nxt, rl, rr = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                         inp["W"], target, offs, inp["temp"], 21)
+    torch.cuda.synchronize()
+    rows = {b: P.np32(target[b * (K + 1):(b + 1) * (K + 1)]) for b in idx}
+    orv = P.oracle_verify(orc, inp, idx, {b: ora[b][0] for b in idx}, rows, {b: K for b in idx},
+                          21)
+    P.compare_verify(acc.cpu().numpy(), nxt.cpu().numpy(), rl.cpu().numpy(), rr.cpu().numpy(),
+                     offs.cpu().numpy(), orv, P.tol_for(torch.bfloat16), tally)
+    print(tally)
+
+
+def test_flat_distribution_is_decided_by_the_draws(dsp, orc):
+    """Equal logits and no bias: every token is the Gumbel-argmax of the draws
+    alone, so the GPU and the oracle must pick the same index."""
+    B, K, V, r = 12, 4, 1024, 256
+    inp = _zeros(B, K, V, r, torch.bfloat16, torch.bfloat16)
+    inp["temp"].fill_(1.0)
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], 31)
+    torch.cuda.synchronize()
+    ora = P.oracle_draft(orc, inp, list(range(B)), 31)
+    tally = P.Tally()
+    P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
+                    inp["temp"].cpu().numpy(), P.tol_for(torch.bfloat16), tally)
+    assert tally.compared >= B * K - 2
+    # lse of a flat row is log V, log p_d = -log V
+    assert torch.allclose(lse, torch.full_like(lse, float(np.log(V))), rtol=1e-5)
+    assert torch.allclose(logp, torch.full_like(logp, -float(np.log(V))), rtol=1e-5)
+
+
+def test_degenerate_schedules(dsp):
+    B, K = 50, 6
+    conf = torch.rand((B, K), generator=torch.Generator().manual_seed(4)).to("cuda")
+    # a budget that only covers the root tokens selects nothing
+    L, offs, _ = dsp.dspark_schedule(conf, B)
+    torch.cuda.synchronize()
+    assert (L == 0).all()
+    assert torch.equal(offs, torch.arange(B + 1, dtype=torch.int64, device="cuda"))
+    L, offs, _ = dsp.dspark_schedule(conf, 3)  # budget below B
+    torch.cuda.synchronize()
+    assert (L == 0).all()
+    # a budget past every item selects every position with S > 0
+    conf[7, 2] = 0.0  # request 7 stops after its second position
+    L, offs, surv = dsp.dspark_schedule(conf, 10 * B * K)
+    torch.cuda.synchronize()
+    expect = torch.full((B,), K, dtype=torch.int32, device="cuda")
+    expect[7] = 2
+    assert torch.equal(L, expect)
+    assert int(offs[B]) == int((L + 1).sum())
+    # a one-point curve is constant latency: the objective rises with every
+    # positive item, so the result equals the plain budget rule
+    L1, _, _ = dsp.dspark_schedule(conf, B + 40, [float(B + 40)], [1.0])
+    L0, _, _ = dsp.dspark_schedule(conf, B + 40)
+    torch.cuda.synchronize()
+    assert torch.equal(L1, L0) and int(L0.sum()) == 40
