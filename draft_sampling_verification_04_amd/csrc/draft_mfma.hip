@@ -568,7 +568,8 @@ __global__ __launch_bounds__(256) void draft_logp_mfma(
 // log(p_t - p_d) over the positive entries (tag 2, position j*).  The Gumbel-max
 // of the target row with the same draws is kept as the fallback for a residual
 // without positive mass.  Rejected requests are listed in `list` (count
-// entries).
+// entries), and so are sampled requests that accepted every drafted token:
+// their bonus token is exactly that fallback draw over row L_b + 1.
 // In base 2, with c = log2(e) / T: a = log2 p_t = t c - lse_t log2(e) and
 // d = log2 p_d = s c - lse_d log2(e), so p_t > p_d iff a > d and
 // log2(p_t - p_d) = a + log2(1 - 2^(d - a)).  Keys are log2 r - log2(-log2 u)
@@ -584,8 +585,8 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     const int32_t* __restrict__ prev_token, const float* __restrict__ draft_lse,
     const float* __restrict__ temperature, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ list, const int32_t* __restrict__ count_ptr,
-    const float* __restrict__ lse_tab, uint64_t seed, int K, int V, int r, PartialBuf res,
-    PartialBuf fall, int n_strips, int n_parts) {
+    const int32_t* __restrict__ lengths, const float* __restrict__ lse_tab, uint64_t seed, int K,
+    int V, int r, PartialBuf res, PartialBuf fall, int n_strips, int n_parts) {
     extern __shared__ uint16_t w_sh[];  // two buffers of [r][kPitch]
     const int count = *count_ptr;
     const int slot0 = blockIdx.y * NWAVES * 32;
@@ -599,14 +600,19 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     // lanes past the list run request list[0]'s rows and store nothing
     const int b = list[active ? slot : 0];
     const int js = accepted[b] + 1;
-    const int p = clamp_token((js == 1) ? prev_token[b]
-                                        : tokens[static_cast<size_t>(b) * K + js - 2],
+    // js > L_b: a full acceptance listed for its bonus, which is this kernel's
+    // fallback draw over row L_b + 1; it takes no residual draw, and its draft
+    // side reads row 1 as an in-range stand-in
+    const bool bonus = js > (lengths ? clamp_len(lengths[b], K) : K);
+    const int jd = bonus ? 1 : js;
+    const int p = clamp_token((jd == 1) ? prev_token[b]
+                                        : tokens[static_cast<size_t>(b) * K + jd - 2],
                               V);
     const float c2 = inv_temperature(temperature[b]) * kLog2e;
-    const float ld2 = draft_lse[static_cast<size_t>(b) * K + js - 1] * kLog2e;
+    const float ld2 = draft_lse[static_cast<size_t>(b) * K + jd - 1] * kLog2e;
     const float lt2 = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1] * kLog2e;
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
-    const uint16_t* brow = base + (static_cast<size_t>(b) * K + js - 1) * V;
+    const uint16_t* brow = base + (static_cast<size_t>(b) * K + jd - 1) * V;
     const uint16_t* trow = target + (row_off[b] + js - 1) * static_cast<int64_t>(V);
     const int buf_elems = r * kPitch;
 
@@ -650,7 +656,7 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
                 const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, t)));
                 const float g2 = __builtin_amdgcn_logf(-l1);  // log2(-log2 u)
                 // entries past V have a = -inf and take part in neither draw
-                if (a > d) {
+                if (!bonus && a > d) {
                     const float kr =
                         a + __builtin_amdgcn_logf(1.0f - __builtin_amdgcn_exp2f(d - a)) - g2;
                     if (kr > br) {
@@ -813,7 +819,7 @@ hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
                        static_cast<const uint16_t*>(v.base), static_cast<const uint16_t*>(v.A),
                        static_cast<const uint16_t*>(v.W), static_cast<const uint16_t*>(v.target),
                        v.row_off, v.tokens, v.prev_token, v.draft_lse, v.temperature, v.accepted,
-                       a.list, a.count, a.lse_tab, v.seed, v.K, v.V, v.r, a.res, a.fall,
+                       a.list, a.count, v.lengths, a.lse_tab, v.seed, v.K, v.V, v.r, a.res, a.fall,
                        a.n_strips, parts);
     return hipGetLastError();
 }

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
     const LT* __restrict__ target, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ lengths, const int32_t* __restrict__ tokens,
     const float* __restrict__ draft_logp, const float* __restrict__ temperature, uint64_t seed,
-    int K, int V, int64_t n_rows, bool vec_ok, float* __restrict__ row_lse_t,
+    int K, int V, int64_t n_rows, bool vec_ok, bool bonus_draw, float* __restrict__ row_lse_t,
     float* __restrict__ row_logratio, VerifyWs ws) {
     __shared__ RowState red[kVRowThreads / kWave];
     const int64_t id = blockIdx.x;
@@ -99,6 +99,9 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
     const float T = temperature[b];
     const bool greedy = !(T > 0.0f);
     const bool bonus = (j == L + 1);
+    // the sampled bonus draw is made here only when the residual kernel does
+    // not make it (bonus_draw); the normaliser is always computed
+    const bool draw = bonus && bonus_draw;
     const LT* trow = target + row * static_cast<int64_t>(V);
     const bool vec = vec_ok && (V % 8 == 0);
     RowState st = row_empty();
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
             const float mc = m * c;
 #pragma unroll
             for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
-            if (bonus) {
+            if (draw) {
                 const u32x4 r0 = philox_block(seed, b, j, kTagResample, v0 >> 2);
                 const u32x4 r1 = philox_block(seed, b, j, kTagResample, (v0 >> 2) + 1);
 #pragma unroll
@@ -219,7 +222,8 @@ __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_ro
                                                      const int64_t* __restrict__ row_off,
                                                      const int32_t* __restrict__ lengths,
                                                      const float* __restrict__ temperature,
-                                                     VerifyWs ws, int32_t* __restrict__ accepted,
+                                                     bool bonus_in_list, VerifyWs ws,
+                                                     int32_t* __restrict__ accepted,
                                                      int32_t* __restrict__ next_token) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
@@ -233,11 +237,14 @@ __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_ro
     int a = 0;
     while (a < L && acc[a]) ++a;
     accepted[b] = a;
-    if (a == L) {
+    const bool sampled = temperature[b] > 0.0f;
+    if (a == L && !(sampled && bonus_in_list)) {
         next_token[b] = ws.bonus[b];
-    } else if (!(temperature[b] > 0.0f)) {
+    } else if (!sampled) {
         next_token[b] = ws.arg[static_cast<size_t>(b) * (K + 1) + a];
     } else {
+        // a sampled first rejection, or (bonus_in_list) a sampled full
+        // acceptance whose bonus the residual kernel draws as its fallback
         const int slot = atomicAdd(ws.count, 1);
         ws.list[slot] = b;
     }
@@ -436,17 +443,21 @@ hipError_t launch_verify(const VerifyArgs& a) {
     hipLaunchKernelGGL(fill_i32, dim3(1), dim3(64), 0, a.stream, ws.count, 1, 0);
     const dim3 rows_grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * (a.K + 1)));
     const bool vec_ok = aligned16(a.target);
+    // With draft rows and the MFMA residual kernel, the sampled bonus draws are
+    // made there (its fallback draw over row L_b + 1 is the bonus draw), only
+    // for the requests that accepted every drafted token.
+    const bool bonus_in_residual = a.K > 0 && residual_mfma_supported(a);
     ProfScope rows_scope(DSPARK_KERNEL_VERIFY_ROWS, a.stream);
     if (a.logit_dt == DSPARK_BF16) {
         hipLaunchKernelGGL(verify_rows<bf16_t>, rows_grid, dim3(kVRowThreads), 0, a.stream,
                            static_cast<const bf16_t*>(a.target), a.row_off, a.lengths, a.tokens,
                            a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
-                           a.row_lse_t, a.row_logratio, ws);
+                           !bonus_in_residual, a.row_lse_t, a.row_logratio, ws);
     } else {
         hipLaunchKernelGGL(verify_rows<float>, rows_grid, dim3(kVRowThreads), 0, a.stream,
                            static_cast<const float*>(a.target), a.row_off, a.lengths, a.tokens,
                            a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
-                           a.row_lse_t, a.row_logratio, ws);
+                           !bonus_in_residual, a.row_lse_t, a.row_logratio, ws);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -456,7 +467,7 @@ hipError_t launch_verify(const VerifyArgs& a) {
         ProfScope resolve_scope(DSPARK_KERNEL_VERIFY_RESOLVE, a.stream);
         hipLaunchKernelGGL(verify_resolve, dim3(static_cast<unsigned>(ceil_div(a.B, 256))), dim3(256),
                            0, a.stream, a.B, a.K, a.n_rows, a.row_off, a.lengths, a.temperature,
-                           ws, a.accepted, a.next_token);
+                           bonus_in_residual, ws, a.accepted, a.next_token);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
