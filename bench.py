@@ -185,26 +185,32 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region.  The library brackets each launch of the dominant kernel
-    # (the draft strip kernel, K launches per step) with HIP events on the
-    # stream it is launched on.
+    # Timed region.  Events perturb what they time (each one recorded between
+    # two dependent kernels widens the gap between them), so only the last
+    # `inst` steps are instrumented: their phases are bracketed with events, and
+    # the library brackets each launch of the dominant kernel (the draft strip
+    # kernel, K launches per step) with HIP events on the stream it is
+    # launched on.  The other steps run as they would in production.
+    inst = min(args.steps, 2)
     phase_events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                    for _ in range(args.steps)]
+                    for _ in range(inst)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    d.dspark_profile_begin(("draft_strip",), max_launches=K * args.steps + 16)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(phase_events[i])
+        j = i - (args.steps - inst)
+        if j == 0:
+            d.dspark_profile_begin(("draft_strip",), max_launches=K * inst)
+        step(phase_events[j] if j >= 0 else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     prof = d.dspark_profile_end()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    draft_ms = sum(e[0].elapsed_time(e[1]) for e in phase_events) / args.steps
-    sched_ms = sum(e[1].elapsed_time(e[2]) for e in phase_events) / args.steps
-    verify_ms = sum(e[2].elapsed_time(e[3]) for e in phase_events) / args.steps
+    draft_ms = sum(e[0].elapsed_time(e[1]) for e in phase_events) / inst
+    sched_ms = sum(e[1].elapsed_time(e[2]) for e in phase_events) / inst
+    verify_ms = sum(e[2].elapsed_time(e[3]) for e in phase_events) / inst
     strip_ms, _, strip_timed = prof["draft_strip"]
     strip_avg_s = strip_ms / max(strip_timed, 1) / 1e3
 
@@ -279,6 +285,7 @@ def main():
             "algorithmic_bytes_per_launch": strip_bytes,
             "avg_launch_us": round(strip_avg_s * 1e6, 2),
             "launches_timed": strip_timed,
+            "timed_steps": f"last {inst} of {args.steps}",
             "mfma_tflops": round(strip_flops / strip_avg_s / 1e12, 1),
             "mfma_frac": round(strip_flops / strip_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
