@@ -281,7 +281,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "draft_strip_mfma",
+            "kernel": "draft_strip_mfma_rk<8,16>" if r == 256 else "draft_strip_mfma",
             "algorithmic_bytes_per_launch": strip_bytes,
             "avg_launch_us": round(strip_avg_s * 1e6, 2),
             "launches_timed": strip_timed,
