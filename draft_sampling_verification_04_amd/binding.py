@@ -143,16 +143,22 @@ def dspark_verify_workspace_bytes(B, K, V, r) -> int:
 
 def dspark_draft_sample(base_logits, A, W, prev_token, temperature, seed, *, draft_tokens=None,
                         draft_logp=None, draft_lse=None, workspace=None, stream=None):
-    """Markov-head draft of K tokens per request; returns (tokens, logp, lse)."""
+    """Markov-head draft of K tokens per request; returns (tokens, logp, lse).
+    A = W = None drafts without the Markov head (every position from its own
+    base logits, all in one pass)."""
     _dev(base_logits, "base_logits")
-    _dev(A, "A")
-    _dev(W, "W")
     _dev(prev_token, "prev_token")
     _dev(temperature, "temperature")
     B, K, V = base_logits.shape
-    r = A.shape[1]
-    if A.shape != (V, r) or W.shape != (r, V) or A.dtype != W.dtype:
-        raise DsparkError(DSPARK_ERR_INVALID_ARG, "A must be [V, r] and W [r, V], same dtype")
+    if A is None and W is None:
+        r, fdt = 1, _dtype(base_logits, "base_logits")
+    else:
+        _dev(A, "A")
+        _dev(W, "W")
+        r = A.shape[1]
+        if A.shape != (V, r) or W.shape != (r, V) or A.dtype != W.dtype:
+            raise DsparkError(DSPARK_ERR_INVALID_ARG, "A must be [V, r] and W [r, V], same dtype")
+        fdt = _dtype(A, "A")
     if prev_token.dtype != torch.int32 or temperature.dtype != torch.float32:
         raise DsparkError(DSPARK_ERR_INVALID_ARG, "prev_token int32, temperature float32")
     dev = base_logits.device
@@ -165,7 +171,7 @@ def dspark_draft_sample(base_logits, A, W, prev_token, temperature, seed, *, dra
     nbytes = dspark_draft_workspace_bytes(B, K, V, r)
     workspace = _workspace(workspace, nbytes, dev)
     _check(lib().dspark_draft_sample(
-        _ptr(base_logits), _dtype(base_logits, "base_logits"), _ptr(A), _ptr(W), _dtype(A, "A"),
+        _ptr(base_logits), _dtype(base_logits, "base_logits"), _ptr(A), _ptr(W), fdt,
         _ptr(prev_token), _ptr(temperature), int(seed) & (2**64 - 1), B, K, V, r,
         _ptr(draft_tokens), _ptr(draft_logp), _ptr(draft_lse), _ptr(workspace),
         workspace.numel(), _stream(stream, dev)))

@@ -58,8 +58,10 @@ dspark_status dspark_draft_sample(const void* base_logits, dspark_dtype logit_dt
     if (V < 1 || V >= (1 << 30)) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: V=%d", V);
     if (r < 1 || r > 1024) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: r=%d", r);
     if (B == 0 || K == 0) return ok();
-    if (!base_logits || !A || !W || !prev_token || !temperature || !draft_tokens)
+    if (!base_logits || !prev_token || !temperature || !draft_tokens)
         return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: NULL required pointer");
+    if ((A == nullptr) != (W == nullptr))
+        return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: A and W must both be set or both NULL");
     if (static_cast<int64_t>(B) * K > (int64_t{1} << 31))
         return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: B*K too large");
     const size_t need = dspark::draft_workspace_bytes(B, K, V, r);
@@ -72,6 +74,10 @@ dspark_status dspark_draft_sample(const void* base_logits, dspark_dtype logit_dt
                         prev_token,  temperature,  seed,      B,          K,
                         V,           r,            draft_tokens, draft_logp, draft_lse,
                         workspace,   ws_bytes,     static_cast<hipStream_t>(stream)};
+    if (!A && !dspark::parallel_supported(a))
+        return fail(DSPARK_ERR_INVALID_ARG,
+                    "draft_sample: drafting without factors needs bf16 logits, V %% 8 == 0 and a "
+                    "16-byte aligned base");
     return hip_status(dspark::launch_draft(a), "draft_sample");
 }
 

@@ -13,6 +13,8 @@
 // combine kernel that folds the strips of each request into x_k, log p_d, lse_d.
 // The strip kernel exists in two forms: a VALU form for any factor dtype and
 // rank, and an MFMA form (draft_mfma.hip) for bf16 factors.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -175,6 +177,9 @@ int mfma_draft_strip();
 hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts, int k,
                                     float* lse_ws);
 hipError_t launch_draft_logp_mfma(const DraftArgs& a, const float* lse_ws);
+bool parallel_supported(const DraftArgs& a);
+hipError_t launch_draft_parallel(const DraftArgs& a, PartialBuf part, size_t part_capacity,
+                                 const int32_t* order);
 hipError_t launch_temperature_order(const float* temperature, int B, int32_t* order,
                                     hipStream_t stream);
 hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int prev_stride, int k,
@@ -189,8 +194,14 @@ struct DraftWs {
     float* lse;  // [B, K] lse_d, kept for the deferred log-probabilities
 };
 
+// Partial records reserved: B max(ceil(V / 64), K), enough for one per
+// (request, strip) of the narrowest strip and for the parallel path's rows.
+size_t partial_capacity(int B, int K, int V) {
+    return static_cast<size_t>(B) * std::max<int64_t>(ceil_div(V, kMinStrip), K);
+}
+
 DraftWs draft_ws(void* ws, int B, int K, int V) {
-    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMinStrip);  // the largest strip count
+    const size_t n = partial_capacity(B, K, V);
     char* w = static_cast<char*>(ws);
     DraftWs d;
     size_t o = 0;
@@ -208,7 +219,7 @@ DraftWs draft_ws(void* ws, int B, int K, int V) {
 
 size_t draft_workspace_bytes(int B, int K, int V, int r) {
     (void)r;
-    const size_t n = static_cast<size_t>(B) * ceil_div(V, kMinStrip);
+    const size_t n = partial_capacity(B, K, V);
     return align256(n * sizeof(float4)) + align256(n * sizeof(int32_t)) +
            align256(static_cast<size_t>(B) * sizeof(int32_t)) +
            align256(static_cast<size_t>(B) * K * sizeof(float));
@@ -218,6 +229,13 @@ bool draft_uses_mfma(const DraftArgs& a) { return mfma_supported(a); }
 
 hipError_t launch_draft(const DraftArgs& a) {
     if (a.B == 0 || a.K == 0) return hipSuccess;
+    if (a.A == nullptr && a.W == nullptr) {  // parallel drafting: no Markov head
+        const DraftWs ws = draft_ws(a.ws, a.B, a.K, a.V);
+        hipError_t e = launch_temperature_order(a.temperature, a.B, ws.order, a.stream);
+        if (e != hipSuccess) return e;
+        ProfScope scope(DSPARK_KERNEL_DRAFT_STRIP, a.stream);
+        return launch_draft_parallel(a, ws.part, partial_capacity(a.B, a.K, a.V), ws.order);
+    }
     const bool mfma = draft_uses_mfma(a);
     const int n_strips = static_cast<int>(ceil_div(a.V, mfma ? mfma_draft_strip() : kValuStrip));
     const DraftWs ws = draft_ws(a.ws, a.B, a.K, a.V);

@@ -507,6 +507,76 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
 }
 
+// ------------------------------------------ parallel drafting (no Markov head)
+// With no transition factors the draft distribution of position k is
+// softmax(base_k / T) on its own, so all B K rows are drawn in one launch:
+// the same half-strip sampler (epilogue_half) on zero bias, lanes walking the
+// strips of their row.  Slot s is row (order[s / K], s % K); partials are
+// stored per row.
+template <int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES)
+void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restrict__ temperature,
+                         const int32_t* __restrict__ order, uint64_t seed, int B, int K, int V,
+                         PartialBuf part, int n_strips, int n_parts) {
+    const int lane = threadIdx.x & 63;
+    const int kh = lane >> 5;
+    const int rows = B * K;
+    const int slot = (blockIdx.y * NWAVES + (threadIdx.x >> 6)) * 32 + (lane & 31);
+    const bool active = slot < rows;
+    const int sl = active ? slot : 0;
+    const int b = order[sl / K];
+    const int k = sl - (sl / K) * K;
+    const int row = b * K + k;
+    const float T = temperature[b];
+    const uint16_t* brow = base + static_cast<size_t>(row) * V;
+    RowState run = row_empty();
+    for (int s = blockIdx.x; s < n_strips; s += n_parts) {
+        uint4 bl[8];
+        load_strip_logits(bl, brow, s * kStripV, kh, V);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x16 acc[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+            epilogue_half(run, acc, bl, h, s * kStripV + 64 * h + 8 * kh, T, seed, b, k + 1);
+        }
+    }
+    row_merge(run, shfl_xor_row(run, 32));
+    if (active && kh == 0) store_partial(part, static_cast<size_t>(row) * n_parts + blockIdx.x, run);
+}
+
+// Fold the partials of each row (one wavefront per row) and write x, lse_d and
+// log p_d = z_x - lse_d with z = base / T (0 for T == 0).
+__global__ __launch_bounds__(256) void draft_combine_rows(
+    PartialBuf part, int n_parts, const uint16_t* __restrict__ base,
+    const float* __restrict__ temperature, int B, int K, int V, int32_t* __restrict__ tokens,
+    float* __restrict__ logp, float* __restrict__ lse) {
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (q >= static_cast<int64_t>(B) * K) return;  // whole wavefront
+    RowState st = row_empty();
+    for (int s = threadIdx.x & 63; s < n_parts; s += kWave)
+        row_merge(st, load_partial(part, static_cast<size_t>(q) * n_parts + s));
+    wave_reduce_row(st);
+    if ((threadIdx.x & 63) == 0) {
+        const int b = static_cast<int>(q / K);
+        const float T = temperature[b];
+        tokens[q] = st.idx;
+        if (T > 0.0f) {
+            const float l = st.m + logf(st.s);
+            if (lse) lse[q] = l;
+            if (logp) {
+                const int v = clamp_token(st.idx, V);
+                logp[q] = to_f32(bf16_t{base[static_cast<size_t>(q) * V + v]}) * inv_temperature(T) - l;
+            }
+        } else {
+            if (lse) lse[q] = st.pert;
+            if (logp) logp[q] = 0.0f;
+        }
+    }
+}
+
 // Fold the partials of each request (one wavefront per request) and write x_k
 // and lse_d (the row maximum for T == 0) for step k.  The winner's logit is
 // not in the partials; log p_d(x_k) is filled in after the last step by
@@ -829,6 +899,32 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 int mfma_draft_strip() { return kStripV; }
+
+bool parallel_supported(const DraftArgs& a) {
+    return a.logit_dt == DSPARK_BF16 && a.V % 8 == 0 && aligned16(a.base);
+}
+
+hipError_t launch_draft_parallel(const DraftArgs& a, PartialBuf part, size_t part_capacity,
+                                 const int32_t* order) {
+    constexpr int NW = 8;
+    const int64_t rows = static_cast<int64_t>(a.B) * a.K;
+    const int n_strips = static_cast<int>(ceil_div(a.V, kStripV));
+    const int groups = static_cast<int>(ceil_div(rows, 32 * NW));
+    // a few workgroups per CU (no LDS), and no more partials than the workspace holds
+    int parts = std::max(1, std::min(n_strips, 4 * device_cus() / groups));
+    parts = static_cast<int>(
+        std::max<int64_t>(1, std::min<int64_t>(parts, static_cast<int64_t>(part_capacity) / rows)));
+    hipLaunchKernelGGL(draft_rows_parallel<NW>, dim3(static_cast<unsigned>(parts),
+                                                     static_cast<unsigned>(groups)),
+                       dim3(64 * NW), 0, a.stream, static_cast<const uint16_t*>(a.base),
+                       a.temperature, order, a.seed, a.B, a.K, a.V, part, n_strips, parts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(draft_combine_rows, dim3(static_cast<unsigned>(ceil_div(rows, 4))),
+                       dim3(256), 0, a.stream, part, parts, static_cast<const uint16_t*>(a.base),
+                       a.temperature, a.B, a.K, a.V, a.tokens, a.logp, a.lse);
+    return hipGetLastError();
+}
 
 bool mfma_supported(const DraftArgs& a) {
     // two LDS buffers of r x 128 bf16 must fit in 160 KiB

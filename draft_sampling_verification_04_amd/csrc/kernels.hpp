@@ -58,6 +58,7 @@ struct DraftArgs {
 
 size_t draft_workspace_bytes(int B, int K, int V, int r);
 bool draft_uses_mfma(const DraftArgs& a);
+bool parallel_supported(const DraftArgs& a);
 hipError_t launch_draft(const DraftArgs& a);
 
 struct VerifyArgs {

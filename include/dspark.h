@@ -93,6 +93,12 @@ size_t dspark_draft_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r);
  *   draft_lse    [B, K] float           lse_d = log sum_v exp(z_v), z = (base + bias)/T
  *                                       (the row maximum for T == 0); nullable
  * Sizes: B >= 0, K >= 0 (either 0 is a no-op), 1 <= V < 2^30, 1 <= r <= 1024.
+ * A = W = NULL drafts without the Markov head: p_d(x_k) = softmax(base_k / T)
+ * for every position on its own (the transition bias is zero, as with W = 0,
+ * and the draws are the same), so all B x K rows are drawn in one pass;
+ * x_0 is unused, r and factor_dt are ignored, and the logits must be bf16 with
+ * V % 8 == 0 and a 16-byte aligned base (ERR_INVALID_ARG otherwise).  Passing
+ * only one of A and W is ERR_INVALID_ARG.
  */
 dspark_status dspark_draft_sample(const void* base_logits, dspark_dtype logit_dt, const void* A,
                                   const void* W, dspark_dtype factor_dt,

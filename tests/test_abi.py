@@ -127,3 +127,15 @@ def test_profile_session_without_gpu_work(L):
     res = d.dspark_profile_end()
     assert set(res) == set(d.KERNELS)
     assert all(v == (0.0, 0, 0) for v in res.values())
+
+
+def test_parallel_drafting_validation(L):
+    # only one factor given
+    assert _draft(L, A=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, W=None) == bd.DSPARK_ERR_INVALID_ARG
+    # no factors: needs bf16 logits, V % 8 == 0 and an aligned base
+    assert _draft(L, A=None, W=None, ldt=0) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, A=None, W=None, V=101) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft(L, A=None, W=None, V=104, base=ctypes.c_void_p(0x1008)) == \
+        bd.DSPARK_ERR_INVALID_ARG
+    assert b"without factors" in L.dspark_last_error()

@@ -174,3 +174,31 @@ def test_degenerate_schedules(dsp):
     L0, _, _ = dsp.dspark_schedule(conf, B + 40)
     torch.cuda.synchronize()
     assert torch.equal(L1, L0) and int(L0.sum()) == 40
+
+
+@pytest.mark.parametrize("K", [1, 4])
+def test_parallel_drafting_equals_zero_transition(dsp, orc, K):
+    """No factors: every position is drawn from its own base logits.  The
+    tokens equal the Markov path's with W = 0 (same draws, zero bias) on the
+    GPU, and the oracle's with W = 0."""
+    from draft_sampling_verification_04_amd import inputs
+
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=70, K=K, V=3000, r=256)
+    inp = inputs.make_inputs(w, "cuda", seed=40 + K, with_target=False)
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], None, None, inp["prev"], inp["temp"], 17)
+    Az = torch.zeros_like(inp["A"])
+    Wz = torch.zeros_like(inp["W"])
+    tz, lz, ez = dsp.dspark_draft_sample(inp["base"], Az, Wz, inp["prev"], inp["temp"], 17)
+    torch.cuda.synchronize()
+    assert torch.equal(tok, tz)
+    # the two paths merge their partials in different orders, so lse_d may
+    # differ in the last fp32 places (one ulp at |lse| ~ 20 is 1.9e-6)
+    assert torch.allclose(lse, ez, rtol=0, atol=2e-5)
+    assert torch.allclose(logp, lz, rtol=0, atol=2e-5)
+    inp["A"], inp["W"] = Az, Wz
+    idx = [0, 3, 31, 32, 69]
+    ora = P.oracle_draft(orc, inp, idx, 17)
+    tally = P.Tally()
+    P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
+                    inp["temp"].cpu().numpy(), P.tol_for(torch.bfloat16), tally)
+    assert tally.compared >= len(idx) * K - 2
