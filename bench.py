@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--workload", default="long_draft")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=24)
+    ap.add_argument("--markov-vs-parallel", action="store_true",
+                    help="also time the draft with the Markov head against parallel drafting "
+                         "(no transition factors) at K = 4 and K = 16")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy kernel (torch.neg, fp32) of this many MiB before "
                          "warmup, as the reference for HBM counter scaling")
@@ -111,6 +114,37 @@ def cpu_baseline(w, inp, seed, n_req):
                        f"verify of K tokens each, T>0 requests first; {t_total:.2f} s on one "
                        f"thread of {model} ({ncpu} logical CPUs); requests are independent, so "
                        f"the rate does not depend on B")
+
+
+def markov_vs_parallel(d, inp, seed, reps=10):
+    """Draft-call time of the sequential Markov head against parallel drafting
+    (every position from its own base logits, one pass) at K = 4 and K = 16 on
+    the benchmark's requests and vocabulary."""
+    import torch
+
+    out = {}
+    for K in (4, 16):
+        base = inp["base"][:, :K].contiguous()
+        res = {}
+        for mode, A, W in (("markov", inp["A"], inp["W"]), ("parallel", None, None)):
+            def call():
+                d.dspark_draft_sample(base, A, W, inp["prev"], inp["temp"], seed)
+            for _ in range(2):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            res[mode] = e0.elapsed_time(e1) / reps
+        out[f"K={K}"] = {"markov_ms": round(res["markov"], 4),
+                         "parallel_ms": round(res["parallel"], 4),
+                         "markov_over_parallel": round(res["markov"] / res["parallel"], 3)}
+    out["markov_K16_over_K4"] = round(out["K=16"]["markov_ms"] / out["K=4"]["markov_ms"], 3)
+    out["parallel_K16_over_K4"] = round(out["K=16"]["parallel_ms"] / out["K=4"]["parallel_ms"], 3)
+    return out
 
 
 def main():
@@ -296,6 +330,8 @@ def main():
         "vocab_logits_per_s": round((B * K * V + (verified + B) * V) / (ms_step / 1e3), 1),
         "host_cpu": f"{model} x{ncpu}",
     }
+    if args.markov_vs_parallel:
+        out["markov_vs_parallel"] = markov_vs_parallel(d, inp, seed)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, seed, args.cpu_requests)
     print(json.dumps(out), flush=True)
