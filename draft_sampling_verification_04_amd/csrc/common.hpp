@@ -72,9 +72,13 @@ __device__ __forceinline__ uint32_t pick(const u32x4& r, int i) {
     return i == 0 ? r.x : (i == 1 ? r.y : (i == 2 ? r.z : r.w));
 }
 
-// u = ((w >> 9) + 0.5) 2^-23, exact in fp32 (24 significant bits).
+// u = ((w >> 9) + 0.5) 2^-23, exact in fp32 (24 significant bits).  The top 23
+// bits of w become the mantissa of f = 1 + (w >> 9) 2^-23 (one align-bit op
+// puts 0x7F above them: exponent field 127), and f - (1 - 2^-24) is exact
+// because both operands lie within a factor of two of each other.
 __device__ __forceinline__ float uniform_of(uint32_t w) {
-    return __fmaf_rn(static_cast<float>(w >> 9), 0x1p-23f, 0x1p-24f);
+    const float f = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9));
+    return f - 0x1.fffffep-1f;
 }
 
 __device__ __forceinline__ float gumbel_of(uint32_t w) {

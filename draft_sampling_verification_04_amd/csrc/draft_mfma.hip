@@ -202,7 +202,7 @@ __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int e0 = entry_of(i, 0);
-            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh + e0) >> 2);
+            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh >> 2) + (e0 >> 2));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const float arg = fmaf(acc[t][i], c2, -mc);
@@ -303,16 +303,65 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
 }
 
 // ------------------------------------------------- draft: strip in two halves
-// Half h of a 128-entry strip is two 32-row tiles; row m of tile t is entry
-// v0 + 64 h + 2 m + t, so an A-operand lane reads the two entries of a rank row
-// with one 4-byte LDS read (32 lanes cover 128 contiguous bytes), and output
-// lane l's accumulator i of tile t is entry v0 + 64 h + 16 (i / 4) + 8 (l / 32)
-// + 2 (i % 4) + t: run i / 4 is 8 consecutive entries (one 16-byte logit chunk,
-// two Philox blocks).  Working on one half at a time keeps 32 accumulators
+// Half h of a 128-entry strip is two 32-row tiles.  Row m of tile t is entry
+// v0 + 64 h + 16 (m / 8) + 8 ((m / 4) % 2) + 4 t + m % 4, so output lane l's
+// accumulator i of tile t is entry v0 + 64 h + 16 (i / 4) + 8 (l / 32) + 4 t
+// + i % 4: for each run a = i / 4 the lane holds the 8 consecutive entries
+// 16 a + 8 (l / 32) + 0..7 (one 16-byte logit chunk; tile t gives Philox block
+// 4 t .. 4 t + 3 of it).  Working on one half at a time keeps 32 accumulators
 // live, which leaves room to hold the factor fragments in registers.
+//
+// The A operand (8 consecutive ranks of one entry per lane) comes straight
+// from the [rank][entry] strip in LDS through gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): within a group of 16 lanes, lane i names 4 consecutive
+// bf16 of one row, and lane j receives element j % 4 of the rows named by
+// lanes j / 4, j / 4 + 4, j / 4 + 8, j / 4 + 12.  So if lane i of a group names
+// rank row R + i / 4 at entry c0(i % 4), lane j receives ranks R .. R + 3 of
+// entry c0(j / 4) + j % 4; two such reads give an operand.  The strip's 16-byte
+// granules are stored XOR-swizzled within each 256-byte rank row (granule g of
+// row k at position g ^ 4 (k % 4)), so the 16 rows x granules a group touches
+// fall on distinct banks.
+//
 // KS = r / 16 rank steps, fixed at compile time so that the step loop is fully
 // unrolled without guards (per-step guards split it into branches that stall
 // the MFMA pipeline).
+
+// Stage W[0:r, v0:v0+128] in LDS in the swizzled layout above.  As in stage_w,
+// one wave instruction fills four rank rows (1 KiB) and lane i's 16 bytes land
+// at the instruction's base + 16 i: lane i fills position i % 16 of row
+// 4 j + i / 16, so it fetches granule (i % 16) ^ 4 (i / 16) of that row.
+template <int NWAVES>
+__device__ __forceinline__ void stage_w_tr(uint16_t* w_sh, const uint16_t* __restrict__ W, int r,
+                                           int V, int v0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int v = min(v0 + 8 * ((lane & 15) ^ ((lane >> 4) << 2)), V - 8);
+    const uint16_t* src = W + static_cast<size_t>(lane >> 4) * V + v;
+    for (int j = wave; j < r / 4; j += NWAVES) {
+        __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(4 * j) * V,
+                                         w_sh + 4 * j * kPitch, 16, 0, 0);
+    }
+}
+
+// Element offset in a strip buffer of the row piece this lane names for half h,
+// tile 0, rank step 0: lane = 32 kh + 16 gm + 4 u + q reads rank row 8 kh + u
+// at entry 64 h + 32 gm + 16 (q / 2) + 8 (q % 2) (granule 8 h + 4 gm + 2 (q / 2)
+// + q % 2, swizzled by row).  Tile 1 is 4 entries (8 bytes) further inside the
+// same granule; rank step kk is 16 rows further, ranks + 4 are 4 rows further.
+__device__ __forceinline__ int tr_offset(int lane, int h) {
+    const int kh = lane >> 5, gm = (lane >> 4) & 1, u = (lane >> 2) & 3, q = lane & 3;
+    const int g = 8 * h + 4 * gm + 2 * (q >> 1) + (q & 1);
+    return (8 * kh + u) * kPitch + 8 * (g ^ (u << 2));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
 template <int KS>
 __device__ __forceinline__ void bias_half(f32x16 (&acc)[2], const uint16_t* wl,
                                           const uint4 (&afr)[KS]) {
@@ -320,31 +369,16 @@ __device__ __forceinline__ void bias_half(f32x16 (&acc)[2], const uint16_t* wl,
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
-    uint32_t d[2][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) d[0][j] = *reinterpret_cast<const uint32_t*>(wl + j * kPitch);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-        {
-            if (kk + 1 < KS) {
+        const uint16_t* w = wl + kk * 16 * kPitch;
+        const bf16x8 bv = as_bf16x8(afr[kk]);
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    d[(kk + 1) & 1][j] =
-                        *reinterpret_cast<const uint32_t*>(wl + ((kk + 1) * 16 + j) * kPitch);
-            }
-            const uint32_t (&c)[8] = d[kk & 1];
-            const bf16x8 bv = as_bf16x8(afr[kk]);
-            uint4 a;
-            a = make_uint4(__builtin_amdgcn_perm(c[1], c[0], 0x05040100u),
-                           __builtin_amdgcn_perm(c[3], c[2], 0x05040100u),
-                           __builtin_amdgcn_perm(c[5], c[4], 0x05040100u),
-                           __builtin_amdgcn_perm(c[7], c[6], 0x05040100u));
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[0], 0, 0, 0);
-            a = make_uint4(__builtin_amdgcn_perm(c[1], c[0], 0x07060302u),
-                           __builtin_amdgcn_perm(c[3], c[2], 0x07060302u),
-                           __builtin_amdgcn_perm(c[5], c[4], 0x07060302u),
-                           __builtin_amdgcn_perm(c[7], c[6], 0x07060302u));
-            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[1], 0, 0, 0);
+        for (int t = 0; t < 2; ++t) {
+            const uint2 lo = lds_tr16(w + 4 * t);
+            const uint2 hi = lds_tr16(w + 4 * t + 4 * kPitch);
+            const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[t], 0, 0, 0);
         }
     }
 }
@@ -369,18 +403,25 @@ __device__ __forceinline__ void load_strip_logits(uint4 (&q)[8], const uint16_t*
     }
 }
 
+// Chunks 4 h .. 4 h + 3 of a lane's strip logits: the logits of half h.
+__device__ __forceinline__ const uint4 (&half_of(const uint4 (&q)[8], int h))[4] {
+    return *reinterpret_cast<const uint4(*)[4]>(&q[4 * h]);
+}
+
 // Running state of a lane over the halves and strips it visits (sampled or
 // greedy; see draft_epilogue for the key).
-__device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], const uint4 (&bl)[8],
-                                              int h, int vh, float T, uint64_t seed, int b,
+__device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], const uint4 (&q)[4],
+                                              int vh, float T, uint64_t seed, int b,
                                               uint32_t pos) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t dw = dword_of(bl[4 * h + (i >> 2)], i & 3);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const float lg = __uint_as_float(t ? (dw & 0xFFFF0000u) : (dw << 16));
+            // entry 16 (i / 4) + 4 t + i % 4 of the lane's half: element
+            // 4 t + i % 4 of chunk i / 4
+            const uint32_t dw = dword_of(q[i >> 2], 2 * t + ((i & 3) >> 1));
+            const float lg = __uint_as_float((i & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
             const float sv = lg + acc[t][i];
             acc[t][i] = sv;
             mx = fmaxf(mx, sv);
@@ -394,15 +435,15 @@ __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], c
         const float c2 = it * kLog2e;
         const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
         float sum = 0.0f;
+        // blocks in increasing entry order: run a, tile t
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
-            const int i0 = 4 * (blk >> 1) + 2 * (blk & 1);    // accumulators i0, i0 + 1
-            const int e0 = 16 * (blk >> 1) + 4 * (blk & 1);  // lane entry offset of the block
-            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh + e0) >> 2);
+            const int a = blk >> 1, t = blk & 1;
+            const int e0 = 16 * a + 4 * t;  // lane entry offset of the block
+            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh >> 2) + (e0 >> 2));
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const int i = i0 + (w >> 1);
-                const int t = w & 1;
+                const int i = 4 * a + w;
                 const float arg = fmaf(acc[t][i], c2, -mc);
                 sum += __builtin_amdgcn_exp2f(arg);
                 const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, w)));
@@ -419,13 +460,17 @@ __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], c
         st.zb = 0.0f;
         st.idx = vh + be;
     } else {
+        // increasing entry order, so the first of equal maxima wins
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int a = 0; a < 4; ++a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                if (acc[t][i] > best) {
-                    best = acc[t][i];
-                    be = 16 * (i >> 2) + 2 * (i & 3) + t;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    if (acc[t][4 * a + w] > best) {
+                        best = acc[t][4 * a + w];
+                        be = 16 * a + 4 * t + w;
+                    }
                 }
             }
         }
@@ -466,10 +511,10 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
     uint4 afr[KS];  // r == 16 KS
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
-    const int wl_off = (8 * kh) * kPitch + 2 * (lane & 31);
+    const int tr0 = tr_offset(lane, 0), tr1 = tr_offset(lane, 1);
 
     int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
-    stage_w<NWAVES>(w_sh, W, r, V, s * kStripV);
+    stage_w_tr<NWAVES>(w_sh, W, r, V, s * kStripV);
     uint4 bl[8];
     load_strip_logits(bl, brow, s * kStripV, kh, V);
     RowState run = row_empty();
@@ -485,15 +530,16 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
         // can be requested at once
         uint4 bn[8];
         if (more) {
-            stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
+            stage_w_tr<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
             load_strip_logits(bn, brow, sn * kStripV, kh, V);
         }
-        const uint16_t* wl = w_sh + buf * buf_elems + wl_off;
+        const uint16_t* wl = w_sh + buf * buf_elems;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x16 acc[2];
-            bias_half<KS>(acc, wl + 64 * h, afr);
-            epilogue_half(run, acc, bl, h, s * kStripV + 64 * h + 8 * kh, T, seed, b, k + 1);
+            bias_half<KS>(acc, wl + (h ? tr1 : tr0), afr);
+            epilogue_half(run, acc, half_of(bl, h), s * kStripV + 64 * h + 8 * kh, T, seed, b,
+                          k + 1);
         }
         if (!more) break;
 #pragma unroll
@@ -540,7 +586,8 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
-            epilogue_half(run, acc, bl, h, s * kStripV + 64 * h + 8 * kh, T, seed, b, k + 1);
+            epilogue_half(run, acc, half_of(bl, h), s * kStripV + 64 * h + 8 * kh, T, seed, b,
+                          k + 1);
         }
     }
     row_merge(run, shfl_xor_row(run, 32));
@@ -717,7 +764,7 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int e0 = entry_of(i, 0);
-            const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vh + e0) >> 2);
+            const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vh >> 2) + (e0 >> 2));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int v = vh + e0 + t;
