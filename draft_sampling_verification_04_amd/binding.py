@@ -29,7 +29,7 @@ DSPARK_BF16 = 1
 
 # dspark_kernel ids (bit positions of the profiling mask)
 KERNELS = ("draft_strip", "draft_combine", "verify_rows", "verify_resolve", "residual_strip",
-           "residual_combine", "schedule", "draft_logp")
+           "residual_combine", "schedule")
 _DT = {torch.float32: DSPARK_F32, torch.bfloat16: DSPARK_BF16}
 
 

@@ -16,6 +16,13 @@ constexpr int kWave = 64;
 constexpr uint32_t kTagDraft = 0;
 constexpr uint32_t kTagAccept = 1;
 constexpr uint32_t kTagResample = 2;
+constexpr uint32_t kTagDraftBlock = 3;
+// Draft tokens are drawn by Gumbel-max in two levels: blocks of kDraftBlock
+// consecutive vocabulary entries compete with key log(block mass) + G (tag 3,
+// counter word = block index), then the token is the Gumbel-argmax of the
+// logits inside the winning block (tag 0, word = entry).  Exact in distribution
+// for any partition; only the winning block needs per-entry draws.
+constexpr int kDraftBlock = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -91,6 +98,15 @@ __device__ __forceinline__ float gumbel_of(uint32_t w) {
 __device__ __forceinline__ float gumbel_fast(uint32_t w) {
     const float a = -__builtin_amdgcn_logf(uniform_of(w)) * kLn2;
     return -__builtin_amdgcn_logf(a) * kLn2;
+}
+
+// Base-2 Gumbel -log2(-log2 u) of the tag-3 draw of draft block blk: log2(e) G
+// up to a constant shared by every block of the row.
+__device__ __forceinline__ float block_gumbel2(uint64_t seed, uint32_t b, uint32_t pos,
+                                               uint32_t blk) {
+    const u32x4 r = philox_block(seed, b, pos, kTagDraftBlock, blk >> 2);
+    const float l1 = __builtin_amdgcn_logf(uniform_of(pick(r, static_cast<int>(blk & 3u))));
+    return -__builtin_amdgcn_logf(-l1);
 }
 
 // Upper bound of gumbel_of(w) that costs no transcendental:

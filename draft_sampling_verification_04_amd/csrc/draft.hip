@@ -14,6 +14,7 @@
 // The strip kernel exists in two forms: a VALU form for any factor dtype and
 // rank, and an MFMA form (draft_mfma.hip) for bf16 factors.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -72,50 +73,57 @@ __global__ __launch_bounds__(256) void draft_strip_valu(
 
 #pragma unroll
     for (int g = 0; g < kValuRows; ++g) {
-        if (g >= nrows) break;
+        if (g >= nrows) break;  // uniform: every thread handles the same requests
         const int b = b0 + g;
         const float T = temperature[b];
         RowState st = row_empty();
-        if (v0 < V) {
-            const LT* br = base + (static_cast<size_t>(b) * K + k) * V + v0;
-            float s[4];
+        float s[4];
+        const LT* br = base + (static_cast<size_t>(b) * K + k) * V + v0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) s[t] = (v0 + t < V) ? to_f32(br[t]) + acc[g][t] : -INFINITY;
-            if (T > 0.0f) {
-                const float it = inv_temperature(T);
-                float z[4];
-                float m = -INFINITY;
+        for (int t = 0; t < 4; ++t)
+            s[t] = (v0 + t < V) ? to_f32(br[t]) + acc[g][t] : -INFINITY;
+        if (T > 0.0f) {
+            // the thread's softmax partial over its 4 entries, then the key of
+            // its draft block (16 consecutive threads hold the block's 64
+            // entries): log of the block mass plus the block's Gumbel
+            const float it = inv_temperature(T);
+            float m = -INFINITY;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    z[t] = s[t] * it;
-                    m = fmaxf(m, z[t]);
-                }
-                float sum = 0.0f;
+            for (int t = 0; t < 4; ++t) m = fmaxf(m, s[t] * it);
+            float sum = 0.0f;
+            if (m != -INFINITY) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    if (v0 + t < V) sum += expf(z[t] - m);
-                st.m = m;
-                st.s = sum;
-                const u32x4 rnd = philox_block(seed, b, k + 1, kTagDraft, v0 >> 2);
+                    if (v0 + t < V) sum += expf(s[t] * it - m);
+            }
+            st.m = m;
+            st.s = sum;
+            float bm = m, bs = sum;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if (v0 + t < V) {
-                        const float p = z[t] + gumbel_of(pick(rnd, t));
-                        if (beats(p, v0 + t, st.pert, st.idx)) {
-                            st.pert = p;
-                            st.zb = z[t];
-                            st.idx = v0 + t;
-                        }
-                    }
+            for (int o = 1; o < kDraftBlock / 4; o <<= 1) {
+                const float om = __shfl_xor(bm, o, kWave);
+                const float os = __shfl_xor(bs, o, kWave);
+                const float mm = fmaxf(bm, om);
+                if (mm != -INFINITY) {
+                    bs = ((bm == -INFINITY) ? 0.0f : bs * expf(bm - mm)) +
+                         ((om == -INFINITY) ? 0.0f : os * expf(om - mm));
+                    bm = mm;
                 }
-            } else {
+            }
+            if (bm != -INFINITY) {
+                const int blk = v0 / kDraftBlock;
+                const u32x4 rnd = philox_block(seed, b, k + 1, kTagDraftBlock, blk >> 2);
+                st.pert = bm + logf(bs) + gumbel_of(pick(rnd, blk & 3));
+                st.zb = 0.0f;
+                st.idx = blk * kDraftBlock;
+            }
+        } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if (v0 + t < V && beats(s[t], v0 + t, st.pert, st.idx)) {
-                        st.pert = s[t];
-                        st.zb = s[t];
-                        st.idx = v0 + t;
-                    }
+            for (int t = 0; t < 4; ++t) {
+                if (v0 + t < V && beats(s[t], v0 + t, st.pert, st.idx)) {
+                    st.pert = s[t];
+                    st.zb = s[t];
+                    st.idx = v0 + t;
                 }
             }
         }
@@ -131,30 +139,160 @@ __global__ __launch_bounds__(256) void draft_strip_valu(
     }
 }
 
-// Fold the strips of each request (one 256-thread workgroup per request) and
-// write x_k, log p_d(x_k) and lse_d.
-constexpr int kCombineThreads = 256;
+__device__ __forceinline__ uint32_t dword_of4(const uint4& q, int i) {
+    return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
 
-__global__ __launch_bounds__(kCombineThreads) void draft_combine(
-    PartialBuf part, int n_strips, const float* __restrict__ temperature, int K, int k,
-    int32_t* __restrict__ tokens, float* __restrict__ logp, float* __restrict__ lse) {
-    __shared__ RowState red[kCombineThreads / kWave];
-    const int b = blockIdx.x;
+// Fold the partials of each row and draw its token (one wavefront per row,
+// four rows per workgroup).  Rows are requests at step k (k >= 0: partial row
+// b, output b K + k, previous token prev[b prev_stride]) or, for parallel
+// drafting (k < 0, no factors), every (request, position) row q = b K + k'.
+// T == 0: the partial's argmax.  T > 0: the partial's winner is a draft block;
+// the token is the Gumbel-argmax of z = (base + bias) / T over its 64 entries
+// with the tag-0 draws (base-2 keys s c - log2(-log2 u), c = log2(e) / T, which
+// order entries as z + G does).  Lane j holds entry block start + j; the bias
+// of the block's entries is recomputed here (for bf16 factors with 16-byte
+// aligned rows: lane 8 c + p sums ranks p r/8 .. (p+1) r/8 - 1 for entries
+// 8 c .. 8 c + 7 with 16-byte loads, then the 8 rank groups are added across
+// lanes; PER = r / 8 fixed at compile time lets every load be issued before
+// the first is used).  Writes x, lse_d = m + log s (the row maximum for T == 0)
+// and log p_d(x) = z_x - lse_d (0 for T == 0).
+template <typename LT, typename FT, int PER>
+__global__ __launch_bounds__(256) void draft_combine(
+    PartialBuf part, int n_parts, const LT* __restrict__ base, const FT* __restrict__ A,
+    const FT* __restrict__ W, const int32_t* __restrict__ prev, int prev_stride,
+    const float* __restrict__ temperature, uint64_t seed, int n_rows, int K, int V, int r, int k,
+    bool vec_ok, int32_t* __restrict__ tokens, float* __restrict__ logp, float* __restrict__ lse) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows) return;  // whole wavefront
+    const int b = (k >= 0) ? row : row / K;
+    const int pos = (k >= 0) ? k + 1 : row % K + 1;
+    const size_t o = (k >= 0) ? static_cast<size_t>(b) * K + k : static_cast<size_t>(row);
+    const int c = lane >> 3, g = lane & 7;
+    // the factor slice of this lane's rank group does not depend on the merge
+    constexpr bool kFast = PER > 0 && std::is_same<FT, bf16_t>::value;
+    uint4 afr[kFast ? PER / 8 : 1];
+    if (kFast && A != nullptr) {
+        const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
+        const uint4* ap = reinterpret_cast<const uint4*>(A + static_cast<size_t>(p) * r + g * PER);
+#pragma unroll
+        for (int j = 0; j < PER / 8; ++j) afr[j] = ap[j];
+    }
     RowState st = row_empty();
-    for (int s = threadIdx.x; s < n_strips; s += kCombineThreads)
-        row_merge(st, load_partial(part, static_cast<size_t>(b) * n_strips + s));
-    st = block_reduce_row<kCombineThreads>(st, red);
-    if (threadIdx.x == 0) {
-        const size_t o = static_cast<size_t>(b) * K + k;
-        tokens[o] = st.idx;
-        if (temperature[b] > 0.0f) {
-            const float l = st.m + logf(st.s);
-            if (lse) lse[o] = l;
-            if (logp) logp[o] = st.zb - l;
-        } else {
+    {
+        const size_t pr = static_cast<size_t>(row) * n_parts;
+        int s = lane;
+        for (; s + 3 * kWave < n_parts; s += 4 * kWave) {
+            RowState q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = load_partial(part, pr + s + u * kWave);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) row_merge(st, q[u]);
+        }
+        for (; s < n_parts; s += kWave) row_merge(st, load_partial(part, pr + s));
+    }
+    wave_reduce_row(st);  // every lane holds the row's state
+    const float T = temperature[b];
+    if (!(T > 0.0f)) {
+        if (lane == 0) {
+            tokens[o] = st.idx;
             if (lse) lse[o] = st.pert;
             if (logp) logp[o] = 0.0f;
         }
+        return;
+    }
+    const float l = st.m + logf(st.s);
+    const int v0 = min(max(st.idx, 0), V - 1) & ~(kDraftBlock - 1);  // winning block
+    const int v = v0 + lane;
+    float bias = 0.0f;
+    if constexpr (kFast) {
+        if (A != nullptr) {
+            // bf16 factors, r = 8 PER, V % 8 == 0, 16-byte aligned A and W
+            const int vc = min(v0 + 8 * c, V - 8);  // entries past V are never drawn
+            uint4 w8[kFast ? PER : 1];
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                w8[j] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(g * PER + j) * V +
+                                                        vc);
+            float part8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const uint32_t ad = dword_of4(afr[j >> 3], (j & 7) >> 1);
+                const float a = __uint_as_float((j & 1) ? (ad & 0xFFFF0000u) : (ad << 16));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t dw = dword_of4(w8[j], e >> 1);
+                    part8[e] = fmaf(a, __uint_as_float((e & 1) ? (dw & 0xFFFF0000u) : (dw << 16)),
+                                    part8[e]);
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part8[e] += __shfl_xor(part8[e], m, kWave);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e == g) bias = part8[e];
+        }
+    } else if (A != nullptr) {
+        const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
+        const FT* arow = A + static_cast<size_t>(p) * r;
+        if (vec_ok) {
+            // 16-byte rows: r % 8 == 0, V % 8 == 0, 16-byte aligned A and W
+            const int per = r >> 3;
+            const int vc = min(v0 + 8 * c, V - 8);  // entries past V are never drawn
+            float part8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int i = g * per; i < (g + 1) * per; ++i) {
+                const float a = to_f32(arow[i]);
+                const uint4 w8 = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(i) * V + vc);
+                const uint32_t d[4] = {w8.x, w8.y, w8.z, w8.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t dw = d[e >> 1];
+                    part8[e] = fmaf(a, __uint_as_float((e & 1) ? (dw & 0xFFFF0000u) : (dw << 16)),
+                                    part8[e]);
+                }
+            }
+#pragma unroll
+            for (int m = 1; m < 8; m <<= 1)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part8[e] += __shfl_xor(part8[e], m, kWave);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e == g) bias = part8[e];
+        } else if (v < V) {
+            for (int i = 0; i < r; ++i)
+                bias = fmaf(to_f32(arow[i]), to_f32(W[static_cast<size_t>(i) * V + v]), bias);
+        }
+    }
+    const float it = inv_temperature(T);
+    float key = -INFINITY, sv = 0.0f;
+    if (v < V) {
+        sv = to_f32(base[o * V + v]) + bias;
+        const u32x4 rnd = philox_block(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(pos),
+                                       kTagDraft, static_cast<uint32_t>(v) >> 2);
+        const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, v & 3)));
+        key = sv * (it * kLog2e) - __builtin_amdgcn_logf(-l1);
+    }
+    // wave argmax, smallest entry on ties
+    int bv = (v < V) ? v : 0x7fffffff;
+    float bsv = sv;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const float ok = __shfl_xor(key, m, kWave);
+        const int ov = __shfl_xor(bv, m, kWave);
+        const float os = __shfl_xor(bsv, m, kWave);
+        if (beats(ok, ov, key, bv)) {
+            key = ok;
+            bv = ov;
+            bsv = os;
+        }
+    }
+    if (lane == 0) {
+        tokens[o] = bv;
+        if (lse) lse[o] = l;
+        if (logp) logp[o] = bsv * it - l;
     }
 }
 
@@ -169,14 +307,46 @@ void launch_valu_strip(const DraftArgs& a, const int32_t* prev, int prev_stride,
                        a.K, a.V, a.r, k, part, n_strips);
 }
 
+bool aligned16_ptr(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename LT, typename FT>
+void launch_combine_t(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k,
+                      const int32_t* prev, int prev_stride) {
+    const bool vec_ok = a.A != nullptr && a.factor_dt == DSPARK_BF16 && a.r % 8 == 0 &&
+                        a.V % 8 == 0 && aligned16_ptr(a.A) && aligned16_ptr(a.W);
+    const dim3 grid(static_cast<unsigned>(ceil_div(n_rows, 4)));
+    if (vec_ok && a.r == 256 && std::is_same<FT, bf16_t>::value)
+        hipLaunchKernelGGL((draft_combine<LT, FT, 32>), grid, dim3(256), 0, a.stream, part,
+                           n_parts, static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
+                           static_cast<const FT*>(a.W), prev, prev_stride, a.temperature, a.seed,
+                           n_rows, a.K, a.V, a.r, k, vec_ok, a.tokens, a.logp, a.lse);
+    else
+        hipLaunchKernelGGL((draft_combine<LT, FT, 0>), grid, dim3(256), 0, a.stream, part,
+                           n_parts, static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
+                           static_cast<const FT*>(a.W), prev, prev_stride, a.temperature, a.seed,
+                           n_rows, a.K, a.V, a.r, k, vec_ok, a.tokens, a.logp, a.lse);
+}
+
 }  // namespace
+
+hipError_t launch_draft_combine(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k,
+                                const int32_t* prev, int prev_stride) {
+    const bool lb = a.logit_dt == DSPARK_BF16;
+    const bool fb = a.A == nullptr || a.factor_dt == DSPARK_BF16;
+    if (lb && fb)
+        launch_combine_t<bf16_t, bf16_t>(a, part, n_parts, n_rows, k, prev, prev_stride);
+    else if (lb)
+        launch_combine_t<bf16_t, float>(a, part, n_parts, n_rows, k, prev, prev_stride);
+    else if (fb)
+        launch_combine_t<float, bf16_t>(a, part, n_parts, n_rows, k, prev, prev_stride);
+    else
+        launch_combine_t<float, float>(a, part, n_parts, n_rows, k, prev, prev_stride);
+    return hipGetLastError();
+}
 
 // Implemented in draft_mfma.hip.
 bool mfma_supported(const DraftArgs& a);
 int mfma_draft_strip();
-hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts, int k,
-                                    float* lse_ws);
-hipError_t launch_draft_logp_mfma(const DraftArgs& a, const float* lse_ws);
 bool parallel_supported(const DraftArgs& a);
 hipError_t launch_draft_parallel(const DraftArgs& a, PartialBuf part, size_t part_capacity,
                                  const int32_t* order);
@@ -191,7 +361,6 @@ namespace {
 struct DraftWs {
     PartialBuf part;
     int32_t* order;
-    float* lse;  // [B, K] lse_d, kept for the deferred log-probabilities
 };
 
 // Partial records reserved: B max(ceil(V / 64), K), enough for one per
@@ -210,8 +379,6 @@ DraftWs draft_ws(void* ws, int B, int K, int V) {
     d.part.idx = reinterpret_cast<int32_t*>(w + o);
     o += align256(n * sizeof(int32_t));
     d.order = reinterpret_cast<int32_t*>(w + o);
-    o += align256(static_cast<size_t>(B) * sizeof(int32_t));
-    d.lse = reinterpret_cast<float*>(w + o);
     return d;
 }
 
@@ -221,8 +388,7 @@ size_t draft_workspace_bytes(int B, int K, int V, int r) {
     (void)r;
     const size_t n = partial_capacity(B, K, V);
     return align256(n * sizeof(float4)) + align256(n * sizeof(int32_t)) +
-           align256(static_cast<size_t>(B) * sizeof(int32_t)) +
-           align256(static_cast<size_t>(B) * K * sizeof(float));
+           align256(static_cast<size_t>(B) * sizeof(int32_t));
 }
 
 bool draft_uses_mfma(const DraftArgs& a) { return mfma_supported(a); }
@@ -266,19 +432,7 @@ hipError_t launch_draft(const DraftArgs& a) {
         prof_end(strip_scope.slot, a.stream);
         strip_scope.slot = -1;
         ProfScope combine_scope(DSPARK_KERNEL_DRAFT_COMBINE, a.stream);
-        if (mfma) {
-            e = launch_draft_combine_mfma(a, ws.part, n_parts, k, ws.lse);
-        } else {
-            hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(a.B)),
-                               dim3(kCombineThreads), 0, a.stream, ws.part, n_parts,
-                               a.temperature, a.K, k, a.tokens, a.logp, a.lse);
-            e = hipGetLastError();
-        }
-        if (e != hipSuccess) return e;
-    }
-    if (mfma && a.logp) {
-        ProfScope logp_scope(DSPARK_KERNEL_DRAFT_LOGP, a.stream);
-        hipError_t e = launch_draft_logp_mfma(a, ws.lse);
+        e = launch_draft_combine(a, ws.part, n_parts, a.B, k, prev, prev_stride);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -165,62 +165,74 @@ __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_s
 }
 
 // ------------------------------------------------------------------ draft
+// Key of the 64-entry draft block whose entries lanes l and l ^ 32 share (32
+// each): each lane's base-2 log-mass is mcb + log2(sum) (mcb = -inf: the lane
+// holds no entry below V); the block's log2-mass plus its base-2 Gumbel.
+// Both lanes of the pair compute the same key.
+__device__ __forceinline__ float block_key2(float mcb, float sum, uint64_t seed, int b,
+                                            uint32_t pos, int blk) {
+    const float pm = __shfl_xor(mcb, 32, kWave);
+    const float ps = __shfl_xor(sum, 32, kWave);
+    const float M = fmaxf(mcb, pm);
+    if (M == -INFINITY) return -INFINITY;
+    const float S = (mcb == -INFINITY ? 0.0f : sum * __builtin_amdgcn_exp2f(mcb - M)) +
+                    (pm == -INFINITY ? 0.0f : ps * __builtin_amdgcn_exp2f(pm - M));
+    return M + __builtin_amdgcn_logf(S) + block_gumbel2(seed, b, pos, blk);
+}
+
 // Epilogue of one lane (one request, 64 entries vh + entry_of(i, t)): the
-// accumulators become s = base + bias (-inf past V); for T > 0 the lane's
-// softmax partial (max and sum of exp((s - max) / T), on the z = s / T scale)
-// and Gumbel-max winner; for T == 0 the argmax of s.
-// The Gumbel-max compares key = (s - m) c - log2(-log2 u) with c = log2(e) / T
-// and m the lane maximum of s; since -log2(-log2 u) = log2(e) (G + ln ln 2),
-// key + m c = log2(e) (z + G) + log2(e) ln ln 2 orders the entries of a row
-// exactly as z + G does, and it is what lanes and strips compare (the "pert"
-// of the partial).  The first term of key is also the exponent argument of the
-// softmax sum.  Entries are visited in increasing v, so a strict comparison
-// keeps the smallest index among equal keys.  The winner's logit is not kept:
-// the combine step recomputes it for the one winning entry of the row.
+// accumulators become s = base + bias (-inf past V).  For T > 0 the strip is
+// two draft blocks of 64 entries, half of each in this lane and half in lane
+// l ^ 32; per block the lane forms its softmax partial (max and sum of
+// exp((s - max) / T), on the z = s / T scale), the pair merges the two halves
+// into the block's log-mass, and the block key log2(mass) + base-2 Gumbel
+// (tag 3) competes in the running state with the block start as index.  With
+// c = log2(e) / T the block log2-mass is m c + log2(sum of 2^((s - m) c)), so
+// key = log2(e) (log mass + G) + log2(e) ln ln 2: it orders blocks as the
+// natural-log form does.  The combine step draws the entry inside the winning
+// block.  For T == 0 the lane keeps the argmax of s, visiting entries in
+// increasing v so that a strict comparison keeps the smallest index.
 __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4 (&bl)[8], int vh,
                                                    float T, uint64_t seed, int b, uint32_t pos) {
     const bool greedy = !(T > 0.0f);
-    float mx = -INFINITY;
+    // the lane's entries of draft block j (strip entries 64 j .. 64 j + 63) are
+    // accumulators i = 8 j .. 8 j + 7 of every tile
+    float mxb[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float sv = logit_at(bl, i, t) + acc[t][i];
             acc[t][i] = sv;
-            mx = fmaxf(mx, sv);
+            mxb[i >> 3] = fmaxf(mxb[i >> 3], sv);
         }
     }
     RowState st = row_empty();
-    float best = -INFINITY;
-    int be = 0;
     if (!greedy) {
         const float it = inv_temperature(T);
         const float c2 = it * kLog2e;
-        // a lane of the tail strip may hold no entry below V (mx = -inf)
-        const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
-        float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int e0 = entry_of(i, 0);
-            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh >> 2) + (e0 >> 2));
+        for (int j = 0; j < 2; ++j) {
+            // a lane of the tail strip may hold no entry below V (mx = -inf)
+            const float mx = mxb[j];
+            const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
+            float sum = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float arg = fmaf(acc[t][i], c2, -mc);
-                sum += __builtin_amdgcn_exp2f(arg);
-                const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, t)));
-                const float key = arg - __builtin_amdgcn_logf(-l1);
-                if (key > best) {
-                    best = key;
-                    be = e0 + t;
-                }
-            }
+            for (int i = 8 * j; i < 8 * j + 8; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, -mc));
+            RowState sb;
+            sb.m = mx * it;
+            sb.s = sum;
+            sb.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum, seed, b, pos,
+                                 (vh >> 6) + j);
+            sb.zb = 0.0f;
+            sb.idx = (vh & ~(kDraftBlock - 1)) + kDraftBlock * j;
+            row_merge(st, sb);
         }
-        st.m = mx * it;
-        st.s = sum;
-        st.pert = best + mc;
-        st.zb = 0.0f;
-        st.idx = vh + be;
     } else {
+        float best = -INFINITY;
+        int be = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
 #pragma unroll
@@ -334,7 +346,7 @@ template <int NWAVES>
 __device__ __forceinline__ void stage_w_tr(uint16_t* w_sh, const uint16_t* __restrict__ W, int r,
                                            int V, int v0) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int v = min(v0 + 8 * ((lane & 15) ^ ((lane >> 4) << 2)), V - 8);
     const uint16_t* src = W + static_cast<size_t>(lane >> 4) * V + v;
     for (int j = wave; j < r / 4; j += NWAVES) {
@@ -408,6 +420,29 @@ __device__ __forceinline__ const uint4 (&half_of(const uint4 (&q)[8], int h))[4]
     return *reinterpret_cast<const uint4(*)[4]>(&q[4 * h]);
 }
 
+// Chunks c0 .. c1 - 1 of load_strip_logits without the tail fix-up, so that a
+// strip's loads can be spread over the phases of the previous strip.
+__device__ __forceinline__ void load_logit_chunks(uint4 (&q)[8], const uint16_t* row, int v0,
+                                                  int kh, int V, int c0, int c1) {
+#pragma unroll
+    for (int c = c0; c < c1; ++c) {
+        const int v = v0 + 64 * (c >> 2) + 16 * (c & 3) + 8 * kh;
+        q[c] = *reinterpret_cast<const uint4*>(row + min(v, V - 8));
+    }
+}
+
+// The tail fix-up of load_strip_logits, once the loads have landed.
+__device__ __forceinline__ void logit_tail(uint4 (&q)[8], int v0, int kh, int V) {
+    if (v0 + kStripV > V) {
+        const uint32_t ninf2 = 0xFF80FF80u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int v = v0 + 64 * (c >> 2) + 16 * (c & 3) + 8 * kh;
+            if (v >= V) q[c] = make_uint4(ninf2, ninf2, ninf2, ninf2);
+        }
+    }
+}
+
 // Running state of a lane over the halves and strips it visits (sampled or
 // greedy; see draft_epilogue for the key).
 __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], const uint4 (&q)[4],
@@ -431,34 +466,23 @@ __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], c
     float best = -INFINITY;
     int be = 0;
     if (T > 0.0f) {
+        // sampled: this half is one draft block (entries vh & ~63 .. + 63, half
+        // of them in the partner lane); its key enters the running state with
+        // the block start as index, and the online-softmax sum covers the lane's
+        // own entries
         const float it = inv_temperature(T);
         const float c2 = it * kLog2e;
         const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
         float sum = 0.0f;
-        // blocks in increasing entry order: run a, tile t
 #pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
-            const int a = blk >> 1, t = blk & 1;
-            const int e0 = 16 * a + 4 * t;  // lane entry offset of the block
-            const u32x4 rnd = philox_block(seed, b, pos, kTagDraft, (vh >> 2) + (e0 >> 2));
+        for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int i = 4 * a + w;
-                const float arg = fmaf(acc[t][i], c2, -mc);
-                sum += __builtin_amdgcn_exp2f(arg);
-                const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, w)));
-                const float key = arg - __builtin_amdgcn_logf(-l1);
-                if (key > best) {
-                    best = key;
-                    be = e0 + w;
-                }
-            }
-        }
+            for (int t = 0; t < 2; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, -mc));
         st.m = mx * it;
         st.s = sum;
-        st.pert = best + mc;
+        st.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum, seed, b, pos, vh >> 6);
         st.zb = 0.0f;
-        st.idx = vh + be;
+        st.idx = vh & ~(kDraftBlock - 1);
     } else {
         // increasing entry order, so the first of equal maxima wins
 #pragma unroll
@@ -483,9 +507,11 @@ __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], c
 
 // One workgroup per (part, request group), persistent over the strips part,
 // part + n_parts, ...: the factor fragments of each lane's request are loaded
-// once and stay in registers, so the MFMA loops issue no vector-memory loads
-// and the next strip's W (into the other LDS buffer) and logits (into
-// registers) are requested as soon as a strip starts.  Each lane folds the
+// once and stay in registers, so the MFMA loops issue no vector-memory loads.
+// The next strip's W (into the other LDS buffer) is requested as soon as a
+// strip starts, and its logits (into registers) two chunks at a time between
+// the strip's phases: issued all at once, the 16 loads of 8 waves queue behind
+// each other in the CU's memory pipeline and stall the waves that issue last.  Each lane folds the
 // halves and strips it visits into one running state, so a request gets
 // n_parts partials per step.
 template <int NWAVES, int KS>
@@ -524,22 +550,23 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
         // wave is done with the other buffer
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        logit_tail(bl, s * kStripV, kh, V);
         const int sn = s + n_parts;
         const bool more = sn < n_strips;
-        // the MFMA loops issue no vector-memory loads, so the next strip's data
-        // can be requested at once
         uint4 bn[8];
         if (more) {
             stage_w_tr<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
-            load_strip_logits(bn, brow, sn * kStripV, kh, V);
+            load_logit_chunks(bn, brow, sn * kStripV, kh, V, 0, 2);
         }
         const uint16_t* wl = w_sh + buf * buf_elems;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x16 acc[2];
             bias_half<KS>(acc, wl + (h ? tr1 : tr0), afr);
+            if (more) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 2 + 4 * h, 4 + 4 * h);
             epilogue_half(run, acc, half_of(bl, h), s * kStripV + 64 * h + 8 * kh, T, seed, b,
                           k + 1);
+            if (more && h == 0) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 4, 6);
         }
         if (!more) break;
 #pragma unroll
@@ -592,90 +619,6 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
     }
     row_merge(run, shfl_xor_row(run, 32));
     if (active && kh == 0) store_partial(part, static_cast<size_t>(row) * n_parts + blockIdx.x, run);
-}
-
-// Fold the partials of each row (one wavefront per row) and write x, lse_d and
-// log p_d = z_x - lse_d with z = base / T (0 for T == 0).
-__global__ __launch_bounds__(256) void draft_combine_rows(
-    PartialBuf part, int n_parts, const uint16_t* __restrict__ base,
-    const float* __restrict__ temperature, int B, int K, int V, int32_t* __restrict__ tokens,
-    float* __restrict__ logp, float* __restrict__ lse) {
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (q >= static_cast<int64_t>(B) * K) return;  // whole wavefront
-    RowState st = row_empty();
-    for (int s = threadIdx.x & 63; s < n_parts; s += kWave)
-        row_merge(st, load_partial(part, static_cast<size_t>(q) * n_parts + s));
-    wave_reduce_row(st);
-    if ((threadIdx.x & 63) == 0) {
-        const int b = static_cast<int>(q / K);
-        const float T = temperature[b];
-        tokens[q] = st.idx;
-        if (T > 0.0f) {
-            const float l = st.m + logf(st.s);
-            if (lse) lse[q] = l;
-            if (logp) {
-                const int v = clamp_token(st.idx, V);
-                logp[q] = to_f32(bf16_t{base[static_cast<size_t>(q) * V + v]}) * inv_temperature(T) - l;
-            }
-        } else {
-            if (lse) lse[q] = st.pert;
-            if (logp) logp[q] = 0.0f;
-        }
-    }
-}
-
-// Fold the partials of each request (one wavefront per request) and write x_k
-// and lse_d (the row maximum for T == 0) for step k.  The winner's logit is
-// not in the partials; log p_d(x_k) is filled in after the last step by
-// draft_logp_mfma, off the sequential path.
-__global__ __launch_bounds__(kWave) void draft_combine_mfma(
-    PartialBuf part, int n_parts, const float* __restrict__ temperature, int K, int k,
-    int32_t* __restrict__ tokens, float* __restrict__ lse, float* __restrict__ lse_ws) {
-    const int b = blockIdx.x;
-    RowState st = row_empty();
-    for (int s = threadIdx.x; s < n_parts; s += kWave)
-        row_merge(st, load_partial(part, static_cast<size_t>(b) * n_parts + s));
-    wave_reduce_row(st);
-    if (threadIdx.x == 0) {
-        const size_t o = static_cast<size_t>(b) * K + k;
-        const float l = (temperature[b] > 0.0f) ? st.m + logf(st.s) : st.pert;
-        tokens[o] = st.idx;
-        lse_ws[o] = l;
-        if (lse) lse[o] = l;
-    }
-}
-
-// log p_d(x_k) = z_{x_k} - lse_d for every (request, step), one wavefront each:
-// z = (base + A[x_{k-1}] . W[:, x_k]) / T, the bias recomputed as one rank-r
-// dot product; 0 for T == 0.
-__global__ __launch_bounds__(256) void draft_logp_mfma(
-    const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
-    const uint16_t* __restrict__ W, const int32_t* __restrict__ prev_token,
-    const float* __restrict__ temperature, const int32_t* __restrict__ tokens,
-    const float* __restrict__ lse_ws, float* __restrict__ logp, int B, int K, int V, int r) {
-    const int lane = threadIdx.x & 63;
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (g >= static_cast<int64_t>(B) * K) return;  // whole wavefront
-    const int b = static_cast<int>(g / K);
-    const int k = static_cast<int>(g - static_cast<int64_t>(b) * K);
-    const float T = temperature[b];
-    if (!(T > 0.0f)) {
-        if (lane == 0) logp[g] = 0.0f;
-        return;
-    }
-    const int v = clamp_token(tokens[g], V);
-    const int p = clamp_token((k == 0) ? prev_token[b] : tokens[g - 1], V);
-    float d = 0.0f;
-    for (int i = lane; i < r; i += kWave)
-        d = fmaf(to_f32(bf16_t{A[static_cast<size_t>(p) * r + i]}),
-                 to_f32(bf16_t{W[static_cast<size_t>(i) * V + v]}), d);
-#pragma unroll
-    for (int m = kWave / 2; m > 0; m >>= 1) d += __shfl_xor(d, m, kWave);
-    if (lane == 0) {
-        const float z = (to_f32(bf16_t{base[static_cast<size_t>(g) * V + v]}) + d) *
-                        inv_temperature(T);
-        logp[g] = z - lse_ws[g];
-    }
 }
 
 // --------------------------------------------------------------- residual
@@ -967,10 +910,7 @@ hipError_t launch_draft_parallel(const DraftArgs& a, PartialBuf part, size_t par
                        a.temperature, order, a.seed, a.B, a.K, a.V, part, n_strips, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(draft_combine_rows, dim3(static_cast<unsigned>(ceil_div(rows, 4))),
-                       dim3(256), 0, a.stream, part, parts, static_cast<const uint16_t*>(a.base),
-                       a.temperature, a.B, a.K, a.V, a.tokens, a.logp, a.lse);
-    return hipGetLastError();
+    return launch_draft_combine(a, part, parts, static_cast<int>(rows), -1, nullptr, 0);
 }
 
 bool mfma_supported(const DraftArgs& a) {
@@ -999,22 +939,6 @@ hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int p
     if (a.B > 64)
         return launch_draft_step_nw<4>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
     return launch_draft_step_nw<2>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
-}
-
-hipError_t launch_draft_combine_mfma(const DraftArgs& a, PartialBuf part, int n_parts, int k,
-                                    float* lse_ws) {
-    hipLaunchKernelGGL(draft_combine_mfma, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0,
-                       a.stream, part, n_parts, a.temperature, a.K, k, a.tokens, a.lse, lse_ws);
-    return hipGetLastError();
-}
-
-hipError_t launch_draft_logp_mfma(const DraftArgs& a, const float* lse_ws) {
-    const int64_t n = static_cast<int64_t>(a.B) * a.K;
-    hipLaunchKernelGGL(draft_logp_mfma, dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0,
-                       a.stream, static_cast<const uint16_t*>(a.base),
-                       static_cast<const uint16_t*>(a.A), static_cast<const uint16_t*>(a.W),
-                       a.prev_token, a.temperature, a.tokens, lse_ws, a.logp, a.B, a.K, a.V, a.r);
-    return hipGetLastError();
 }
 
 hipError_t launch_residual_mfma(const ResidualArgs& a, int* n_parts) {

@@ -92,6 +92,11 @@ size_t dspark_draft_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r);
  *   draft_logp   [B, K] float           log p_d(x_k) = z_{x_k} - lse_d (0 for T == 0); nullable
  *   draft_lse    [B, K] float           lse_d = log sum_v exp(z_v), z = (base + bias)/T
  *                                       (the row maximum for T == 0); nullable
+ * Draws: for T > 0, x_k ~ p_d by Gumbel-max in two levels with Philox4x32-10
+ * words keyed by (seed, request, position k): blocks of 64 consecutive entries
+ * compete with log(block mass) + G (tag 3, word = block index), then x_k is the
+ * Gumbel-argmax of z inside the winning block (tag 0, word = entry); for
+ * T == 0, x_k is the argmax of base + bias (smallest index on ties).
  * Sizes: B >= 0, K >= 0 (either 0 is a no-op), 1 <= V < 2^30, 1 <= r <= 1024.
  * A = W = NULL drafts without the Markov head: p_d(x_k) = softmax(base_k / T)
  * for every position on its own (the transition bias is zero, as with W = 0,
@@ -185,15 +190,14 @@ dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_tok
  * any thread.
  */
 typedef enum dspark_kernel {
-    DSPARK_KERNEL_DRAFT_STRIP = 0,       /* draft: bias GEMM + logits + Gumbel over a vocab strip */
-    DSPARK_KERNEL_DRAFT_COMBINE = 1,     /* draft: merge of the per-strip partials of one step */
+    DSPARK_KERNEL_DRAFT_STRIP = 0,       /* draft: bias GEMM + logits + block keys over a vocab strip */
+    DSPARK_KERNEL_DRAFT_COMBINE = 1,     /* draft: merge of the partials + draw inside the block */
     DSPARK_KERNEL_VERIFY_ROWS = 2,       /* verify: target normaliser and accept test per row */
     DSPARK_KERNEL_VERIFY_RESOLVE = 3,    /* verify: strict-prefix resolution per request */
     DSPARK_KERNEL_RESIDUAL_STRIP = 4,    /* verify: residual / fallback Gumbel over a vocab strip */
     DSPARK_KERNEL_RESIDUAL_COMBINE = 5,  /* verify: merge of the residual partials */
     DSPARK_KERNEL_SCHEDULE = 6,          /* schedule: survival, selection and row offsets */
-    DSPARK_KERNEL_DRAFT_LOGP = 7,        /* draft: log p_d of the drawn tokens, once per call */
-    DSPARK_KERNEL_COUNT = 8
+    DSPARK_KERNEL_COUNT = 7
 } dspark_kernel;
 
 /* Open a session timing at most max_launches launches (events are created

@@ -36,12 +36,20 @@
  *   - random draws: Philox4x32-10 with key (seed lo32, seed hi32) and counter
  *     (v >> 2, position, request, tag); the draw for vocab index v is output
  *     word v & 3.  Tags: 0 draft Gumbel, 1 accept uniform (v = 0),
- *     2 residual / bonus Gumbel.
+ *     2 residual / bonus Gumbel, 3 draft block Gumbel (v = block index).
  *   - uniform u = ((w >> 9) + 0.5) * 2^-23, exact in fp32, in (0, 1).
  *   - Gumbel G = -log(-log u), evaluated in fp64 and rounded to fp32.
  *   - temperature T > 0 multiplies logits by the fp32 reciprocal 1/T on both
  *     the draft and the target side; T == 0 means greedy on both sides.
  *   - argmax ties go to the smallest index.
+ *   - draft tokens (T > 0) are drawn by Gumbel-max in two levels: the
+ *     vocabulary is cut into blocks of 64 consecutive entries, the block with
+ *     the largest fp32(log-mass) + G (tag 3, keyed by the block index) wins,
+ *     and the token is the Gumbel-argmax of z inside that block (tag 0, keyed
+ *     by the entry).  This is an exact draw from softmax(z) for any partition
+ *     (the first level picks a block with probability equal to its mass, the
+ *     second an entry with its probability inside the block), and with
+ *     V <= 64 it is the plain Gumbel-argmax.
  */
 #include <math.h>
 #include <stdint.h>
@@ -50,7 +58,8 @@
 
 #define ORACLE_API __attribute__((visibility("default")))
 
-enum { TAG_DRAFT = 0, TAG_ACCEPT = 1, TAG_RESAMPLE = 2 };
+enum { TAG_DRAFT = 0, TAG_ACCEPT = 1, TAG_RESAMPLE = 2, TAG_DRAFT_BLOCK = 3 };
+enum { DRAFT_BLOCK = 64 };
 
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10 (SC'11, section 3).  One round multiplies words 0 and 2 by
@@ -149,12 +158,13 @@ static int plain_argmax(const float* z, int V, double* gap) {
     return best;
 }
 
-/* Gumbel-max: argmax_v fp32(z_v + G_v) with G keyed by (seed, b, pos, tag, v). */
-static int gumbel_argmax(const float* z, int V, uint64_t seed, uint32_t b, uint32_t pos,
-                         uint32_t tag, double* gap) {
+/* Gumbel-max over v in [lo, hi): argmax_v fp32(z_v + G_v) with G keyed by
+ * (seed, b, pos, tag, v). */
+static int gumbel_argmax_range(const float* z, int lo, int hi, uint64_t seed, uint32_t b,
+                               uint32_t pos, uint32_t tag, double* gap) {
     int best = -1;
     float best_val = -INFINITY, second_val = -INFINITY;
-    for (int v = 0; v < V; ++v) {
+    for (int v = lo; v < hi; ++v) {
         float pert = z[v] + oracle_gumbel(seed, b, pos, tag, (uint32_t)v);
         if (best < 0 || pert > best_val) {
             second_val = best_val;
@@ -166,6 +176,44 @@ static int gumbel_argmax(const float* z, int V, uint64_t seed, uint32_t b, uint3
     }
     if (gap) *gap = (double)best_val - (double)second_val;
     return best;
+}
+
+static int gumbel_argmax(const float* z, int V, uint64_t seed, uint32_t b, uint32_t pos,
+                         uint32_t tag, double* gap) {
+    return gumbel_argmax_range(z, 0, V, seed, b, pos, tag, gap);
+}
+
+/* Draft draw in two levels (see the readings above): block keys
+ * fp32(log sum_{v in blk} exp z_v) + G(tag 3, blk), then the Gumbel-argmax of z
+ * inside the winning block.  *gap is the smaller of the two levels' top-2
+ * gaps, so a near tie at either level is reported. */
+static int gumbel_argmax_blocks(const float* z, int V, uint64_t seed, uint32_t b, uint32_t pos,
+                                double* gap) {
+    const int nb = (V + DRAFT_BLOCK - 1) / DRAFT_BLOCK;
+    int best = -1;
+    float best_key = -INFINITY, second_key = -INFINITY;
+    for (int blk = 0; blk < nb; ++blk) {
+        const int lo = blk * DRAFT_BLOCK;
+        const int n = (V - lo < DRAFT_BLOCK) ? V - lo : DRAFT_BLOCK;
+        float key = (float)log_sum_exp(z + lo, n) +
+                    oracle_gumbel(seed, b, pos, TAG_DRAFT_BLOCK, (uint32_t)blk);
+        if (best < 0 || key > best_key) {
+            second_key = best_key;
+            best_key = key;
+            best = blk;
+        } else if (key > second_key) {
+            second_key = key;
+        }
+    }
+    const int lo = best * DRAFT_BLOCK;
+    const int hi = (V - lo < DRAFT_BLOCK) ? V : lo + DRAFT_BLOCK;
+    double g_entry;
+    const int x = gumbel_argmax_range(z, lo, hi, seed, b, pos, TAG_DRAFT, &g_entry);
+    if (gap) {
+        const double g_block = (double)best_key - (double)second_key;
+        *gap = g_block < g_entry ? g_block : g_entry;
+    }
+    return x;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -209,7 +257,7 @@ ORACLE_API void oracle_target_probs(const float* t_row, int V, float T, double* 
 /* ------------------------------------------------------------------------ */
 /* Draft for one request ([yage] Markov head; [guide] 3.1 sequential head).
  * For k = 1..K: draft logits with the previous token (x_0 = prev0), then
- * x_k = Gumbel-argmax of z (T > 0) or argmax of s (T == 0).
+ * x_k = two-level Gumbel-argmax of z (T > 0) or argmax of s (T == 0).
  * Outputs per position: token, log p_d(x_k) = z_{x_k} - lse_d, lse_d (for T == 0
  * lse_d is the row maximum and log p_d is 0: p_d is one-hot), and the top-2
  * gap of the values the argmax was taken over. */
@@ -228,7 +276,7 @@ ORACLE_API void oracle_draft_request(const float* base /* [K][V] */, const float
         double g;
         if (T > 0.0f) {
             double l = log_sum_exp(z, V);
-            x = gumbel_argmax(z, V, seed, b, pos, TAG_DRAFT, &g);
+            x = gumbel_argmax_blocks(z, V, seed, b, pos, &g);
             lse[k] = (float)l;
             logp[k] = (float)((double)z[x] - l);
         } else {

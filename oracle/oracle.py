@@ -23,7 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dspark_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-TAG_DRAFT, TAG_ACCEPT, TAG_RESAMPLE = 0, 1, 2
+TAG_DRAFT, TAG_ACCEPT, TAG_RESAMPLE, TAG_DRAFT_BLOCK = 0, 1, 2, 3
+DRAFT_BLOCK = 64
 
 
 def build(force: bool = False) -> str:

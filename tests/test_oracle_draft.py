@@ -151,3 +151,77 @@ def test_softmax_normalisation_and_lse(orc):
     p = orc.draft_probs(base[0], A, W, 9, 1.0)
     np.testing.assert_allclose(logp[0], np.log(p[tok[0]]), rtol=1e-5, atol=1e-6)
     assert (gap > 0).all()
+
+
+def _draws(orc, base_k, A, W, prev, T, n, seed):
+    """n independent single-position drafts (request index = stream)."""
+    V = base_k.shape[0]
+    tok, _, _, gap = orc.draft_batch(np.broadcast_to(base_k[None, None, :], (n, 1, V)), A, W,
+                                     np.full(n, prev, np.int32), np.full(n, T, np.float32), seed)
+    return tok[:, 0], gap[:, 0]
+
+
+def test_two_level_draw_is_an_exact_softmax_sample(orc):
+    """Draft draws over three blocks (64 + 64 + 22 entries) follow softmax(z):
+    per entry, and per block (the first level picks a block with its mass)."""
+    V, r, n = 150, 4, 300000
+    rng = np.random.default_rng(21)
+    base = rng.normal(0, 0.7, V).astype(np.float32)
+    A = rng.normal(0, 0.5, (V, r)).astype(np.float32)
+    W = rng.normal(0, 0.5, (r, V)).astype(np.float32)
+    T = 0.9
+    tok, _ = _draws(orc, base, A, W, 3, T, n, seed=5)
+    p = orc.draft_probs(base, A, W, 3, T)
+    counts = np.bincount(tok, minlength=V)
+    expect = p * n
+    assert expect.min() > 20
+    chi2 = ((counts - expect) ** 2 / expect).sum()
+    assert stats.chi2.sf(chi2, V - 1) > 1e-3
+    blocks = np.arange(V) // 64
+    cb = np.bincount(blocks[tok], minlength=3)
+    eb = np.array([p[blocks == j].sum() for j in range(3)]) * n
+    chi2b = ((cb - eb) ** 2 / eb).sum()
+    assert stats.chi2.sf(chi2b, 2) > 1e-3
+
+
+@pytest.mark.parametrize("V", [64, 65])
+def test_single_populated_block_is_the_plain_gumbel_argmax(orc, V):
+    """With V = 64 there is one block; with V = 65 and the last entry at a
+    logit of -1e30 the second block has no mass.  Either way the draw is the
+    Gumbel-argmax of z over the first 64 entries with the tag-0 draws."""
+    rng = np.random.default_rng(V)
+    base = rng.normal(0, 1.5, (2, V)).astype(np.float32)
+    if V == 65:
+        base[:, 64] = -1e30
+    r = 4
+    A = rng.normal(0, 0.5, (V, r)).astype(np.float32)
+    W = np.zeros((r, V), np.float32)  # no bias: z = base / T
+    T, seed, b = 1.3, 41, 9
+    it = np.float32(1.0) / np.float32(T)
+    tok, _, _, _ = orc.draft_request(base, A, W, 0, T, seed, b)
+    for k in range(2):
+        z = base[k, :64] * it
+        g = np.array([orc.gumbel(seed, b, k + 1, 0, v) for v in range(64)], np.float32)
+        assert tok[k] == int(np.argmax(z + g))
+
+
+def test_mass_in_one_block_draws_inside_it(orc):
+    """Blocks with no mass (logits -1e30) are never chosen, and inside the one
+    populated block the draw is its Gumbel-argmax: a plain Gumbel-max over a
+    sub-range of the vocabulary."""
+    V, r = 300, 4
+    rng = np.random.default_rng(8)
+    base = np.full((3, V), -1e30, np.float32)
+    lo, hi = 128, 192  # block 2
+    base[:, lo:hi] = rng.normal(0, 1.0, (3, hi - lo)).astype(np.float32)
+    A = rng.normal(0, 0.5, (V, r)).astype(np.float32)
+    W = np.zeros((r, V), np.float32)
+    T, seed, b = 0.8, 13, 4
+    it = np.float32(1.0) / np.float32(T)
+    tok, logp, lse, _ = orc.draft_request(base, A, W, 0, T, seed, b)
+    for k in range(3):
+        assert lo <= tok[k] < hi
+        z = base[k, lo:hi] * it
+        g = np.array([orc.gumbel(seed, b, k + 1, 0, v) for v in range(lo, hi)], np.float32)
+        assert tok[k] == lo + int(np.argmax(z + g))
+        np.testing.assert_allclose(lse[k], logsumexp(z.astype(np.float64)), rtol=1e-6)
