@@ -144,7 +144,8 @@ __device__ __forceinline__ uint32_t dword_of4(const uint4& q, int i) {
 }
 
 // Fold the partials of each row and draw its token (one wavefront per row,
-// four rows per workgroup).  Rows are requests at step k (k >= 0: partial row
+// one wavefront per workgroup, so that the rows spread over every CU's memory
+// pipeline).  Rows are requests at step k (k >= 0: partial row
 // b, output b K + k, previous token prev[b prev_stride]) or, for parallel
 // drafting (k < 0, no factors), every (request, position) row q = b K + k'.
 // T == 0: the partial's argmax.  T > 0: the partial's winner is a draft block;
@@ -158,13 +159,13 @@ __device__ __forceinline__ uint32_t dword_of4(const uint4& q, int i) {
 // the first is used).  Writes x, lse_d = m + log s (the row maximum for T == 0)
 // and log p_d(x) = z_x - lse_d (0 for T == 0).
 template <typename LT, typename FT, int PER>
-__global__ __launch_bounds__(256) void draft_combine(
+__global__ __launch_bounds__(kWave) void draft_combine(
     PartialBuf part, int n_parts, const LT* __restrict__ base, const FT* __restrict__ A,
     const FT* __restrict__ W, const int32_t* __restrict__ prev, int prev_stride,
     const float* __restrict__ temperature, uint64_t seed, int n_rows, int K, int V, int r, int k,
     bool vec_ok, int32_t* __restrict__ tokens, float* __restrict__ logp, float* __restrict__ lse) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int row = blockIdx.x;
     if (row >= n_rows) return;  // whole wavefront
     const int b = (k >= 0) ? row : row / K;
     const int pos = (k >= 0) ? k + 1 : row % K + 1;
@@ -314,14 +315,14 @@ void launch_combine_t(const DraftArgs& a, PartialBuf part, int n_parts, int n_ro
                       const int32_t* prev, int prev_stride) {
     const bool vec_ok = a.A != nullptr && a.factor_dt == DSPARK_BF16 && a.r % 8 == 0 &&
                         a.V % 8 == 0 && aligned16_ptr(a.A) && aligned16_ptr(a.W);
-    const dim3 grid(static_cast<unsigned>(ceil_div(n_rows, 4)));
+    const dim3 grid(static_cast<unsigned>(n_rows));
     if (vec_ok && a.r == 256 && std::is_same<FT, bf16_t>::value)
-        hipLaunchKernelGGL((draft_combine<LT, FT, 32>), grid, dim3(256), 0, a.stream, part,
+        hipLaunchKernelGGL((draft_combine<LT, FT, 32>), grid, dim3(kWave), 0, a.stream, part,
                            n_parts, static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
                            static_cast<const FT*>(a.W), prev, prev_stride, a.temperature, a.seed,
                            n_rows, a.K, a.V, a.r, k, vec_ok, a.tokens, a.logp, a.lse);
     else
-        hipLaunchKernelGGL((draft_combine<LT, FT, 0>), grid, dim3(256), 0, a.stream, part,
+        hipLaunchKernelGGL((draft_combine<LT, FT, 0>), grid, dim3(kWave), 0, a.stream, part,
                            n_parts, static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
                            static_cast<const FT*>(a.W), prev, prev_stride, a.temperature, a.seed,
                            n_rows, a.K, a.V, a.r, k, vec_ok, a.tokens, a.logp, a.lse);
