@@ -316,12 +316,13 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
 
 // ------------------------------------------------- draft: strip in two halves
 // Half h of a 128-entry strip is two 32-row tiles.  Row m of tile t is entry
-// v0 + 64 h + 16 (m / 8) + 8 ((m / 4) % 2) + 4 t + m % 4, so output lane l's
-// accumulator i of tile t is entry v0 + 64 h + 16 (i / 4) + 8 (l / 32) + 4 t
-// + i % 4: for each run a = i / 4 the lane holds the 8 consecutive entries
-// 16 a + 8 (l / 32) + 0..7 (one 16-byte logit chunk; tile t gives Philox block
-// 4 t .. 4 t + 3 of it).  Working on one half at a time keeps 32 accumulators
-// live, which leaves room to hold the factor fragments in registers.
+// v0 + 64 h + 16 (m / 8) + 8 ((m / 4) % 2) + 4 (t ^ ((m / 8) % 2)) + m % 4, so
+// output lane l's accumulator i of tile t is entry v0 + 64 h + 16 (i / 4)
+// + 8 (l / 32) + 4 (t ^ ((i / 4) % 2)) + i % 4: for each run a = i / 4 the lane
+// holds the 8 consecutive entries 16 a + 8 (l / 32) + 0..7, one 16-byte logit
+// chunk, half of it from each tile.  Working on one half at a time keeps 32
+// accumulators live, which leaves room to hold the factor fragments in
+// registers.
 //
 // The A operand (8 consecutive ranks of one entry per lane) comes straight
 // from the [rank][entry] strip in LDS through gfx950's transposing LDS read
@@ -329,25 +330,34 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
 // bf16 of one row, and lane j receives element j % 4 of the rows named by
 // lanes j / 4, j / 4 + 4, j / 4 + 8, j / 4 + 12.  So if lane i of a group names
 // rank row R + i / 4 at entry c0(i % 4), lane j receives ranks R .. R + 3 of
-// entry c0(j / 4) + j % 4; two such reads give an operand.  The strip's 16-byte
-// granules are stored XOR-swizzled within each 256-byte rank row (granule g of
-// row k at position g ^ 4 (k % 4)), so the 16 rows x granules a group touches
-// fall on distinct banks.
+// entry c0(j / 4) + j % 4; two such reads give an operand.  The 16 lanes of a
+// group name 4 rows x 4 eight-byte pieces, 128 bytes in all.  The strip's
+// 16-byte granules are stored XOR-swizzled within each 256-byte rank row
+// (granule g of row k at position p = f(g) ^ s(k % 4), with f flipping bit 3
+// of g when bit 2 is set and s(u) = 4 (u % 2) + 2 (u / 2)), and a lane naming
+// piece q of row u reads the (t ^ (q / 2))-th eight-byte half of its granule
+// for tile t: together these put the 16 pieces of a group on 16 distinct
+// 8-byte bank slots of a 128-byte line (and the two groups of a 32-lane half
+// on different 128-byte halves of the row).
 //
 // KS = r / 16 rank steps, fixed at compile time so that the step loop is fully
 // unrolled without guards (per-step guards split it into branches that stall
 // the MFMA pipeline).
 
+__device__ __forceinline__ constexpr int tr_row_swizzle(int u) { return 4 * (u & 1) + 2 * (u >> 1); }
+__device__ __forceinline__ constexpr int tr_granule_flip(int g) { return g ^ ((g & 4) << 1); }
+
 // Stage W[0:r, v0:v0+128] in LDS in the swizzled layout above.  As in stage_w,
 // one wave instruction fills four rank rows (1 KiB) and lane i's 16 bytes land
 // at the instruction's base + 16 i: lane i fills position i % 16 of row
-// 4 j + i / 16, so it fetches granule (i % 16) ^ 4 (i / 16) of that row.
+// 4 j + i / 16, so it fetches the granule stored there (f is its own inverse).
 template <int NWAVES>
 __device__ __forceinline__ void stage_w_tr(uint16_t* w_sh, const uint16_t* __restrict__ W, int r,
                                            int V, int v0) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int v = min(v0 + 8 * ((lane & 15) ^ ((lane >> 4) << 2)), V - 8);
+    const int g = tr_granule_flip((lane & 15) ^ tr_row_swizzle(lane >> 4));
+    const int v = min(v0 + 8 * g, V - 8);
     const uint16_t* src = W + static_cast<size_t>(lane >> 4) * V + v;
     for (int j = wave; j < r / 4; j += NWAVES) {
         __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(4 * j) * V,
@@ -356,14 +366,15 @@ __device__ __forceinline__ void stage_w_tr(uint16_t* w_sh, const uint16_t* __res
 }
 
 // Element offset in a strip buffer of the row piece this lane names for half h,
-// tile 0, rank step 0: lane = 32 kh + 16 gm + 4 u + q reads rank row 8 kh + u
-// at entry 64 h + 32 gm + 16 (q / 2) + 8 (q % 2) (granule 8 h + 4 gm + 2 (q / 2)
-// + q % 2, swizzled by row).  Tile 1 is 4 entries (8 bytes) further inside the
-// same granule; rank step kk is 16 rows further, ranks + 4 are 4 rows further.
-__device__ __forceinline__ int tr_offset(int lane, int h) {
+// tile t, rank step 0: lane = 32 kh + 16 gm + 4 u + q reads rank row 8 kh + u
+// at entry 64 h + 32 gm + 16 (q / 2) + 8 (q % 2) + 4 (t ^ (q / 2)) (granule
+// g = 8 h + 4 gm + q, stored at f(g) ^ s(u), and the 8-byte half t ^ (q / 2)
+// of it).  Rank step kk is 16 rows further, ranks + 4 are 4 rows further.
+__device__ __forceinline__ int tr_offset(int lane, int h, int t) {
     const int kh = lane >> 5, gm = (lane >> 4) & 1, u = (lane >> 2) & 3, q = lane & 3;
-    const int g = 8 * h + 4 * gm + 2 * (q >> 1) + (q & 1);
-    return (8 * kh + u) * kPitch + 8 * (g ^ (u << 2));
+    const int g = 8 * h + 4 * gm + q;
+    return (8 * kh + u) * kPitch + 8 * (tr_granule_flip(g) ^ tr_row_swizzle(u)) +
+           4 * (t ^ (q >> 1));
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -374,8 +385,9 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// wt[t] = strip buffer + tr_offset(lane, h, t).
 template <int KS>
-__device__ __forceinline__ void bias_half(f32x16 (&acc)[2], const uint16_t* wl,
+__device__ __forceinline__ void bias_half(f32x16 (&acc)[2], const uint16_t* const (&wt)[2],
                                           const uint4 (&afr)[KS]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -383,12 +395,11 @@ __device__ __forceinline__ void bias_half(f32x16 (&acc)[2], const uint16_t* wl,
         for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-        const uint16_t* w = wl + kk * 16 * kPitch;
         const bf16x8 bv = as_bf16x8(afr[kk]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint2 lo = lds_tr16(w + 4 * t);
-            const uint2 hi = lds_tr16(w + 4 * t + 4 * kPitch);
+            const uint2 lo = lds_tr16(wt[t] + kk * 16 * kPitch);
+            const uint2 hi = lds_tr16(wt[t] + kk * 16 * kPitch + 4 * kPitch);
             const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
             acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), bv, acc[t], 0, 0, 0);
         }
@@ -453,9 +464,9 @@ __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], c
     for (int i = 0; i < 16; ++i) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            // entry 16 (i / 4) + 4 t + i % 4 of the lane's half: element
-            // 4 t + i % 4 of chunk i / 4
-            const uint32_t dw = dword_of(q[i >> 2], 2 * t + ((i & 3) >> 1));
+            // entry 16 (i / 4) + 4 (t ^ ((i / 4) % 2)) + i % 4 of the lane's
+            // half: element 4 (t ^ ((i / 4) % 2)) + i % 4 of chunk i / 4
+            const uint32_t dw = dword_of(q[i >> 2], 2 * (t ^ ((i >> 2) & 1)) + ((i & 3) >> 1));
             const float lg = __uint_as_float((i & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
             const float sv = lg + acc[t][i];
             acc[t][i] = sv;
@@ -488,12 +499,13 @@ __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], c
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int tt = 0; tt < 2; ++tt) {
+                const int t = tt ^ (a & 1);  // entries 16 a + 4 tt + w
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     if (acc[t][4 * a + w] > best) {
                         best = acc[t][4 * a + w];
-                        be = 16 * a + 4 * t + w;
+                        be = 16 * a + 4 * tt + w;
                     }
                 }
             }
@@ -537,7 +549,8 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
     uint4 afr[KS];  // r == 16 KS
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
-    const int tr0 = tr_offset(lane, 0), tr1 = tr_offset(lane, 1);
+    const int tro[2][2] = {{tr_offset(lane, 0, 0), tr_offset(lane, 0, 1)},
+                           {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
 
     int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
     stage_w_tr<NWAVES>(w_sh, W, r, V, s * kStripV);
@@ -562,7 +575,8 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x16 acc[2];
-            bias_half<KS>(acc, wl + (h ? tr1 : tr0), afr);
+            const uint16_t* const wt[2] = {wl + tro[h][0], wl + tro[h][1]};
+            bias_half<KS>(acc, wt, afr);
             if (more) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 2 + 4 * h, 4 + 4 * h);
             epilogue_half(run, acc, half_of(bl, h), s * kStripV + 64 * h + 8 * kh, T, seed, b,
                           k + 1);
