@@ -41,6 +41,11 @@ def parse():
     ap.add_argument("--markov-vs-parallel", action="store_true",
                     help="also time the draft with the Markov head against parallel drafting "
                          "(no transition factors) at K = 4 and K = 16")
+    ap.add_argument("--sps-curve", action="store_true",
+                    help="also measure a stair-step step-latency curve (a bf16 GEMM over N batch "
+                         "tokens) and schedule the confidence workload with it: greedy early stop "
+                         "against a global search over N, and with the budget taken from "
+                         "confidences two steps back")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy kernel (torch.neg, fp32) of this many MiB before "
                          "warmup, as the reference for HBM counter scaling")
@@ -145,6 +150,111 @@ def markov_vs_parallel(d, inp, seed, reps=10):
     out["markov_K16_over_K4"] = round(out["K=16"]["markov_ms"] / out["K=4"]["markov_ms"], 3)
     out["parallel_K16_over_K4"] = round(out["K=16"]["parallel_ms"] / out["K=4"]["parallel_ms"], 3)
     return out
+
+
+def gemm_latency_curve(dev, n_min, n_max, step=64, hidden=2560, inner=9728, reps=10):
+    """Latency (ms) of one bf16 GEMM [N, hidden] x [hidden, inner] for N = n_min,
+    n_min + step, ..., n_max: the shape of a 4B-class target model's MLP
+    up-projection, a stand-in for the step latency of the target batch.  The
+    library's tiling makes it a stair-step function of N."""
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(5)
+    w = torch.randn((hidden, inner), generator=g, device=dev).to(torch.bfloat16)
+    x = torch.randn((n_max, hidden), generator=g, device=dev).to(torch.bfloat16)
+    ns, lat = [], []
+    for n in range(n_min, n_max + 1, step):
+        xn = x[:n]
+        for _ in range(3):
+            torch.matmul(xn, w)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(xn, w)
+        e1.record()
+        torch.cuda.synchronize()
+        ns.append(float(n))
+        lat.append(e0.elapsed_time(e1) / reps)
+    return ns, lat
+
+
+def objective(B, surv_sel_sum, n_tokens, ns, lat):
+    """f(N) = (B + sum of selected S) / tau(N), tau piecewise linear in the
+    curve points and flat outside them."""
+    import numpy as np
+
+    tau = float(np.interp(n_tokens, ns, lat))
+    return (B + surv_sel_sum) / tau
+
+
+def global_best(B, S, D, ns, lat):
+    """max over n = 0..D of f(B + n) taking the n largest survival values: the
+    global search over N the greedy early stop is compared with."""
+    import numpy as np
+
+    s = np.sort(S[S > 0].astype(np.float64))[::-1][:D]
+    pre = np.concatenate([[0.0], np.cumsum(s)])
+    n = np.arange(len(pre))
+    f = (B + pre) / np.interp(B + n, ns, lat)
+    i = int(np.argmax(f))
+    return float(f[i]), int(B + i)
+
+
+def sps_curve(d, inputs, dev, steps=12):
+    """Next row 2: a measured stair-step curve in the confidence scheduler.
+    Greedy early stop (the schedule kernel) against a global search over N on
+    the confidence-scheduled workload, and the asynchronous variant whose
+    budget comes from the confidences two steps back while the selection uses
+    the current ones."""
+    import numpy as np
+    import torch
+
+    w = inputs.WORKLOADS["conf_sched"]
+    B, K, budget = w.B, w.K, w.budget
+    D = max(0, budget - B)
+    # the scheduler sees N in [B, budget]: 49 points at a step of 64 tokens
+    ns, lat = gemm_latency_curve(dev, B, budget)
+    jumps = [(int(ns[i]), round(lat[i] / lat[i - 1], 3)) for i in range(1, len(lat))
+             if lat[i] > 1.15 * lat[i - 1]]
+
+    def greedy(conf):
+        L, _, S = d.dspark_schedule(conf, budget, ns, lat)
+        torch.cuda.synchronize()
+        L, S = L.cpu().numpy(), S.cpu().numpy()
+        sel = sum(float(S[b, :L[b]].sum()) for b in range(B))
+        n = B + int(L.sum())
+        return L, S, n, objective(B, sel, n, ns, lat)
+
+    confs = [inputs.make_confidence(w, dev, seed=100 + t)[0] for t in range(steps)]
+    rows = []
+    for t, conf in enumerate(confs):
+        L, S, n_g, f_g = greedy(conf)
+        f_star, n_star = global_best(B, S, D, ns, lat)
+        row = {"n_greedy": n_g, "f_greedy": f_g, "n_global": n_star, "f_global": f_star}
+        if t >= 2:
+            # budget from the confidences of step t - 2, selection with the current ones
+            _, _, n_lag, _ = greedy(confs[t - 2])
+            Ll, _, Sl = d.dspark_schedule(conf, n_lag)
+            torch.cuda.synchronize()
+            Ll, Sl = Ll.cpu().numpy(), Sl.cpu().numpy()
+            sel = sum(float(Sl[b, :Ll[b]].sum()) for b in range(B))
+            row["n_lag"] = B + int(Ll.sum())
+            row["f_lag"] = objective(B, sel, row["n_lag"], ns, lat)
+        rows.append(row)
+    lag = [r["f_lag"] / r["f_greedy"] for r in rows if "f_lag" in r]
+    return {
+        "curve": {"gemm": "bf16 [N, 2560] x [2560, 9728]", "n": [int(ns[0]), int(ns[-1])],
+                  "points": len(ns),
+                  "step": int(ns[1] - ns[0]), "ms_at_budget": round(float(np.interp(budget, ns, lat)), 4),
+                  "jumps_over_15pct": jumps[:12]},
+        "workload": f"conf_sched (B={B}, K={K}, budget {budget} tokens), {steps} steps of fresh "
+                    f"confidences",
+        "greedy_over_global": round(float(np.mean([r["f_greedy"] / r["f_global"] for r in rows])), 4),
+        "n_greedy_mean": round(float(np.mean([r["n_greedy"] for r in rows])), 1),
+        "n_global_mean": round(float(np.mean([r["n_global"] for r in rows])), 1),
+        "lagged_over_greedy": round(float(np.mean(lag)), 4),
+        "n_lag_mean": round(float(np.mean([r["n_lag"] for r in rows if "n_lag" in r])), 1),
+    }
 
 
 def main():
@@ -332,6 +442,8 @@ def main():
     }
     if args.markov_vs_parallel:
         out["markov_vs_parallel"] = markov_vs_parallel(d, inp, seed)
+    if args.sps_curve:
+        out["sps_curve"] = sps_curve(d, inputs, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, seed, args.cpu_requests)
     print(json.dumps(out), flush=True)

@@ -160,6 +160,26 @@ def test_schedule_parity_random(dsp, orc, seed):
             np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
 
 
+@pytest.mark.parametrize("jump", [1.05, 1.3, 2.0])
+def test_schedule_stair_step_curve_parity(dsp, orc, inputs, jump):
+    """A stair-step latency curve over the whole selectable range (49 points
+    from B to the budget, a jump every 256 tokens, as a library GEMM's tiling
+    gives): the early stop lands at a stair edge, bit-exact with the oracle."""
+    w = inputs.WORKLOADS["conf_sched"]
+    conf, _ = inputs.make_confidence(w, "cuda", seed=11)
+    ns = np.arange(w.B, w.budget + 1, 64, dtype=np.float64)
+    tau = (1.0 + 0.01 * (ns - w.B) / 64.0) * jump ** np.floor(ns / 256.0)
+    cn, ct = ns.astype(np.float32), tau.astype(np.float32)
+    L, offs, S = dsp.dspark_schedule(conf, w.budget, cn.tolist(), ct.tolist())
+    torch.cuda.synchronize()
+    oL, ooffs, oS, n = orc.schedule(conf.cpu().numpy(), w.budget, cn.astype(np.float64),
+                                    ct.astype(np.float64))
+    np.testing.assert_array_equal(S.cpu().numpy(), oS)
+    np.testing.assert_array_equal(L.cpu().numpy(), oL)
+    np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+    assert 0 < n <= w.budget - w.B
+
+
 def test_schedule_high_conc_parity(dsp, orc, inputs):
     w = inputs.WORKLOADS["high_conc"]
     conf, _ = inputs.make_confidence(w, "cuda", seed=4)
