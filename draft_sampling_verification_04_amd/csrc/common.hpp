@@ -120,8 +120,10 @@ __device__ __forceinline__ float gumbel_upper(uint32_t w) {
 
 // ---------------------------------------------------------------- row state
 // Partial reduction state of one logits row over a subset of the vocabulary:
-// online-softmax max m and sum s = sum exp(z - m); the Gumbel-max winner
-// (perturbed value, logit at the winner, index).  Ties go to the smaller index.
+// online-softmax max m and sum s = sum exp(z - m); the winner of a keyed
+// argmax (its key, a value carried with it, its index): a perturbed entry, a
+// draft block (key = log-mass + Gumbel, index = block start) or, for T == 0,
+// the largest logit.  Ties go to the smaller index.
 struct RowState {
     float m;
     float s;

@@ -4,15 +4,18 @@
 // Per draft position k (sequential, x_k feeds position k+1):
 //   bias_v = A[x_{k-1}, :] . W[:, v]     rank-r transition lookup
 //   z_v    = (base[b, k, v] + bias_v) * (1/T_b)
-//   x_k    = argmax_v z_v + G_v          Philox-keyed Gumbel-max (T > 0)
+//   x_k    ~ softmax(z) by Gumbel-max in two levels (T > 0): the 64-entry
+//            block with the largest log(mass) + G (tag 3) wins, then
+//            x_k = argmax over its entries of z_v + G_v (tag 0)
 //          = argmax_v base + bias        (T == 0)
 //   lse_d  = log sum_v exp(z_v),  log p_d(x_k) = z_{x_k} - lse_d
 //
 // Each position is two launches: a strip kernel that produces, per request and
-// vocabulary strip, an online-softmax / Gumbel-max partial (RowState), and a
-// combine kernel that folds the strips of each request into x_k, log p_d, lse_d.
-// The strip kernel exists in two forms: a VALU form for any factor dtype and
-// rank, and an MFMA form (draft_mfma.hip) for bf16 factors.
+// vocabulary strip (or part of strips), an online-softmax partial with the best
+// block key (RowState), and a combine kernel that folds them into lse_d and the
+// winning block, draws x_k inside that block and writes log p_d.  The strip
+// kernel exists in two forms: a VALU form for any factor dtype and rank, and an
+// MFMA form (draft_mfma.hip) for bf16 factors.
 #include <algorithm>
 #include <type_traits>
 

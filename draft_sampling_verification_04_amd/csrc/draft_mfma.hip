@@ -1,17 +1,19 @@
 // draft_mfma.hip -- MFMA strip kernels for bf16 logits and factors (rank a
-// multiple of 16, V a multiple of 8): the Markov-head draft step and the
-// verification residual.
+// multiple of 16, V a multiple of 8): the Markov-head draft step, parallel
+// drafting and the verification residual.
 //
-// Both need, per (request, vocabulary entry), the transition bias of the
+// All need, per (request, vocabulary entry), the transition bias of the
 // previous token: bias^T[v, b] = sum_i W[i, v] A[x_prev[b], i].  It is a dense
 // contraction (M = V, N = requests, K = r), so it runs on
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation and never leaves registers;
 // the epilogue consumes the accumulators directly.
 //
-// Workgroup = NWAVES wavefronts = one 128-entry vocabulary strip x 32*NWAVES
-// requests.  The strip of W (r x 128 bf16) is staged once in LDS and shared by
-// the waves; each wave owns 32 requests (one MFMA column tile) and all four
-// 32-row tiles of the strip.  Row m of tile t is entry v = strip start + 4 m + t:
+// Workgroup = NWAVES wavefronts = a persistent walk over 128-entry vocabulary
+// strips x 32*NWAVES requests.  The strip of W (r x 128 bf16) is staged in LDS
+// and shared by the waves; each wave owns 32 requests (one MFMA column tile).
+// The rank-256 kernel works a strip in two 64-entry halves (one draft block
+// each) with transposing LDS reads; the runtime-rank kernel keeps four 32-row
+// tiles per strip, where row m of tile t is entry v = strip start + 4 m + t:
 //   - an A-operand lane (row m) reads 4 consecutive entries of 8 rank rows
 //     with one 8-byte LDS read per row, and the 16 lanes of an LDS pass read
 //     128 consecutive bytes (no bank conflicts);
