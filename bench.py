@@ -46,6 +46,10 @@ def parse():
                          "tokens) and schedule the confidence workload with it: greedy early stop "
                          "against a global search over N, and with the budget taken from "
                          "confidences two steps back")
+    ap.add_argument("--calibration", action="store_true",
+                    help="also calibrate a synthetic, over-confident confidence head against "
+                         "the acceptance outcomes of dspark_verify with sequential temperature "
+                         "scaling, and report the expected calibration error before and after")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy kernel (torch.neg, fp32) of this many MiB before "
                          "warmup, as the reference for HBM counter scaling")
@@ -257,6 +261,121 @@ def sps_curve(d, inputs, dev, steps=12):
     }
 
 
+def ece(conf, label, bins=15):
+    """Expected calibration error: over equal-width confidence bins, the
+    sample-weighted mean of |mean label - mean confidence|."""
+    import numpy as np
+
+    c = np.asarray(conf, np.float64)
+    y = np.asarray(label, np.float64)
+    if c.size == 0:
+        return 0.0
+    idx = np.minimum((c * bins).astype(np.int64), bins - 1)
+    err = 0.0
+    for j in range(bins):
+        m = idx == j
+        if m.any():
+            err += m.sum() * abs(y[m].mean() - c[m].mean())
+    return float(err / c.size)
+
+
+def sts_fit(c_raw, label, reached, lo=0.05, hi=20.0, min_samples=50):
+    """Sequential temperature scaling: for positions k = 1..K in order, the
+    temperature tau_k that minimises the Bernoulli log-loss of position k's
+    acceptance labels over the samples that reached k (every earlier token
+    accepted), with calibrated confidence sigmoid(logit(c_raw) / tau_k).  A
+    position reached by fewer than min_samples samples keeps the temperature
+    of the position before it (1 for the first)."""
+    import numpy as np
+    from scipy.optimize import minimize_scalar
+
+    eps = 1e-6
+    taus = []
+    for k in range(c_raw.shape[1]):
+        m = reached[:, k]
+        if m.sum() < min_samples:
+            taus.append(taus[-1] if taus else 1.0)
+            continue
+        c = np.clip(c_raw[m, k].astype(np.float64), eps, 1 - eps)
+        x = np.log(c) - np.log1p(-c)
+        y = label[m, k].astype(np.float64)
+
+        def nll(lt):
+            q = np.clip(1.0 / (1.0 + np.exp(-x / np.exp(lt))), eps, 1 - eps)
+            return -np.mean(y * np.log(q) + (1 - y) * np.log1p(-q))
+
+        res = minimize_scalar(nll, bounds=(np.log(lo), np.log(hi)), method="bounded")
+        taus.append(float(np.exp(res.x)))
+    return taus
+
+
+def sts_apply(c_raw, taus):
+    import numpy as np
+
+    c = np.clip(c_raw.astype(np.float64), 1e-6, 1 - 1e-6)
+    x = np.log(c) - np.log1p(-c)
+    return 1.0 / (1.0 + np.exp(-x / np.asarray(taus)[None, :]))
+
+
+def calibration(d, inp, w, dev, seeds=16, over=2.0):
+    """Next row 3: confidence calibration on synthetic labels.  The synthetic
+    confidence head predicts, for each drafted position, the exact conditional
+    acceptance probability alpha_k = sum_v min(p_t, p_d) of the drafted prefix,
+    made over-confident as sigmoid(over * logit(alpha_k)); the labels are the
+    acceptance outcomes of dspark_verify (position k is labelled when every
+    earlier token was accepted).  Sequential temperature scaling is fitted on
+    half of the draws and the expected calibration error is measured on the
+    other half."""
+    import numpy as np
+    import torch
+
+    B, K, V = w.B, w.K, w.V
+    sampled = (inp["temp"] > 0).cpu().numpy()
+    tsafe = torch.where(inp["temp"] > 0, inp["temp"], torch.ones_like(inp["temp"]))
+    it = (1.0 / tsafe).view(B, 1, 1)
+    target = inp["target"]
+    pt = torch.softmax(target[:, :K].float() * it, dim=-1)
+    offs = torch.arange(B, dtype=torch.int64, device=dev) * (K + 1)
+    Wf = inp["W"].float()
+    craw, lab, rch = [], [], []
+    for s in range(seeds):
+        tok, logp, lse = d.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                               inp["temp"], 7000 + s)
+        prevs = torch.cat([inp["prev"].view(B, 1), tok[:, :-1]], dim=1).long()
+        alpha = torch.empty((B, K), device=dev)
+        for k in range(K):
+            bias = inp["A"][prevs[:, k]].float() @ Wf
+            pd = torch.softmax((inp["base"][:, k].float() + bias) * it.view(B, 1), dim=-1)
+            alpha[:, k] = torch.minimum(pd, pt[:, k]).sum(-1)
+        acc, _, _, _ = d.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                       inp["W"], target.reshape(-1, V), offs, inp["temp"],
+                                       9000 + s)
+        torch.cuda.synchronize()
+        a = acc.cpu().numpy()[sampled]
+        al = alpha.clamp(1e-6, 1 - 1e-6).cpu().numpy()[sampled]
+        kk = np.arange(K)[None, :]
+        lab.append((kk < a[:, None]).astype(np.float64))
+        rch.append(kk <= a[:, None])
+        lg = np.log(al) - np.log1p(-al)
+        craw.append(1.0 / (1.0 + np.exp(-over * lg)))
+    half = seeds // 2
+    cf, yf, rf = (np.concatenate(x[:half]) for x in (craw, lab, rch))
+    ce, ye, re_ = (np.concatenate(x[half:]) for x in (craw, lab, rch))
+    taus = sts_fit(cf, yf, rf)
+    cc = sts_apply(ce, taus)
+    return {
+        "head": f"synthetic: sigmoid({over} logit(alpha_k)), alpha_k = sum_v min(p_t, p_d) of the "
+                f"drafted prefix; labels from dspark_verify",
+        "requests": int(sampled.sum()), "draws": seeds, "fit_draws": half,
+        "labelled_positions_eval": int(re_.sum()),
+        "tau": [round(t, 3) for t in taus],
+        "ece_raw": round(ece(ce[re_], ye[re_]), 4),
+        "ece_sts": round(ece(cc[re_], ye[re_]), 4),
+        "ece_raw_first4": [round(ece(ce[re_[:, k], k], ye[re_[:, k], k]), 4) for k in range(4)],
+        "ece_sts_first4": [round(ece(cc[re_[:, k], k], ye[re_[:, k], k]), 4) for k in range(4)],
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -444,6 +563,8 @@ def main():
         out["markov_vs_parallel"] = markov_vs_parallel(d, inp, seed)
     if args.sps_curve:
         out["sps_curve"] = sps_curve(d, inputs, dev)
+    if args.calibration:
+        out["calibration"] = calibration(d, inp, w, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, seed, args.cpu_requests)
     print(json.dumps(out), flush=True)
