@@ -109,15 +109,6 @@ __device__ __forceinline__ float block_gumbel2(uint64_t seed, uint32_t b, uint32
     return -__builtin_amdgcn_logf(-l1);
 }
 
-// Upper bound of gumbel_of(w) that costs no transcendental:
-// G = -log(-log u) <= -log(1 - u) and 1 - u >= n 2^-24 with n = 2^23 - (w >> 9),
-// so G <= (24 - floor(log2 n)) ln 2 = (clz(n) - 7) ln 2.  A margin of 1e-4
-// covers the rounding of the fp32 evaluation of G.
-__device__ __forceinline__ float gumbel_upper(uint32_t w) {
-    const uint32_t n = 0x800000u - (w >> 9);
-    return static_cast<float>(__clz(static_cast<int>(n)) - 7) * kLn2 + 1e-4f;
-}
-
 // ---------------------------------------------------------------- row state
 // Partial reduction state of one logits row over a subset of the vocabulary:
 // online-softmax max m and sum s = sum exp(z - m); the winner of a keyed
