@@ -818,17 +818,26 @@ __global__ __launch_bounds__(1024) void temperature_order(const float* __restric
 
 constexpr int kMaxLds = 160 * 1024;
 
-// Let the kernel take all the LDS its static arrays leave.
+// Devices a kernel's LDS limit has been raised on (the attribute is per device).
+struct LdsReady {
+    bool dev[64] = {};
+};
+
+// Let the kernel take all the LDS its static arrays leave, once per device.
 template <typename Kern>
-hipError_t allow_big_lds(Kern* kern, bool& done) {
-    if (done) return hipSuccess;
+hipError_t allow_big_lds(Kern* kern, LdsReady& ready) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool track = dev >= 0 && dev < 64;
+    if (track && ready.dev[dev]) return hipSuccess;
     hipFuncAttributes fa;
-    hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             kMaxLds - static_cast<int>(fa.sharedSizeBytes));
-    if (e == hipSuccess) done = true;
+    if (e == hipSuccess && track) ready.dev[dev] = true;
     return e;
 }
 
@@ -847,7 +856,7 @@ int device_cus() {
 }
 
 template <int NWAVES, typename Kern>
-hipError_t launch_draft_strip(Kern* kern, bool& lds_ok, const DraftArgs& a, const int32_t* prev,
+hipError_t launch_draft_strip(Kern* kern, LdsReady& lds_ok, const DraftArgs& a, const int32_t* prev,
                               int prev_stride, int k, const int32_t* order, PartialBuf part,
                               int n_strips, int* n_parts) {
     hipError_t e = allow_big_lds(kern, lds_ok);
@@ -871,18 +880,18 @@ hipError_t launch_draft_step_nw(const DraftArgs& a, const int32_t* prev, int pre
                                 const int32_t* order, PartialBuf part, int n_strips,
                                 int* n_parts) {
     if (a.r == 256) {
-        static bool lds_ok = false;
+        static LdsReady lds_ok;
         return launch_draft_strip<NWAVES>(&draft_strip_mfma_rk<NWAVES, 16>, lds_ok, a, prev,
                                           prev_stride, k, order, part, n_strips, n_parts);
     }
-    static bool lds_ok = false;
+    static LdsReady lds_ok;
     return launch_draft_strip<NWAVES>(&draft_strip_mfma<NWAVES>, lds_ok, a, prev, prev_stride, k,
                                       order, part, n_strips, n_parts);
 }
 
 template <int NWAVES>
 hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
-    static bool lds_ok = false;
+    static LdsReady lds_ok;
     hipError_t e = allow_big_lds(&residual_strip_mfma<NWAVES>, lds_ok);
     if (e != hipSuccess) return e;
     const VerifyArgs& v = *a.v;
