@@ -90,6 +90,11 @@ def test_tiny_full_parity(dsp, orc, inputs):
     # count that leaves lanes idle, and a one-chunk vocabulary
     (1000, 256, 3, 40, torch.bfloat16, torch.bfloat16),
     (8, 256, 2, 3, torch.bfloat16, torch.bfloat16),
+    # four-wave groups (64 < B <= 128) and a last strip of 8 entries, so the
+    # last draft block holds 8 entries
+    (4104, 256, 3, 100, torch.bfloat16, torch.bfloat16),
+    # the runtime-rank MFMA kernel with eight-wave groups (B > 128)
+    (2056, 64, 2, 150, torch.bfloat16, torch.bfloat16),
 ])
 def test_small_shapes_parity(dsp, orc, inputs, V, r, K, B, ldt, fdt):
     w = inputs.resized(inputs.WORKLOADS["long_draft"], B=B, K=K, V=V, r=r, dtype=ldt)
