@@ -100,12 +100,17 @@ __device__ __forceinline__ float gumbel_fast(uint32_t w) {
     return -__builtin_amdgcn_logf(a) * kLn2;
 }
 
-// Base-2 Gumbel -log2(-log2 u) of the tag-3 draw of draft block blk: log2(e) G
-// up to a constant shared by every block of the row.
-__device__ __forceinline__ float block_gumbel2(uint64_t seed, uint32_t b, uint32_t pos,
-                                               uint32_t blk) {
-    const u32x4 r = philox_block(seed, b, pos, kTagDraftBlock, blk >> 2);
-    const float l1 = __builtin_amdgcn_logf(uniform_of(pick(r, static_cast<int>(blk & 3u))));
+// Tag-3 draws of draft blocks 4 (blk / 4) .. 4 (blk / 4) + 3: block blk takes
+// word blk % 4 of Philox block blk / 4.
+__device__ __forceinline__ u32x4 block_draws(uint64_t seed, uint32_t b, uint32_t pos,
+                                             uint32_t blk) {
+    return philox_block(seed, b, pos, kTagDraftBlock, blk >> 2);
+}
+
+// Base-2 Gumbel -log2(-log2 u) of a draft block's draw word: log2(e) G up to a
+// constant shared by every block of the row.
+__device__ __forceinline__ float block_gumbel2(uint32_t word) {
+    const float l1 = __builtin_amdgcn_logf(uniform_of(word));
     return -__builtin_amdgcn_logf(-l1);
 }
 

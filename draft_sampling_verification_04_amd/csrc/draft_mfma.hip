@@ -171,15 +171,14 @@ __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_s
 // each): each lane's base-2 log-mass is mcb + log2(sum) (mcb = -inf: the lane
 // holds no entry below V); the block's log2-mass plus its base-2 Gumbel.
 // Both lanes of the pair compute the same key.
-__device__ __forceinline__ float block_key2(float mcb, float sum, uint64_t seed, int b,
-                                            uint32_t pos, int blk) {
+__device__ __forceinline__ float block_key2(float mcb, float sum, uint32_t word) {
     const float pm = __shfl_xor(mcb, 32, kWave);
     const float ps = __shfl_xor(sum, 32, kWave);
     const float M = fmaxf(mcb, pm);
     if (M == -INFINITY) return -INFINITY;
     const float S = (mcb == -INFINITY ? 0.0f : sum * __builtin_amdgcn_exp2f(mcb - M)) +
                     (pm == -INFINITY ? 0.0f : ps * __builtin_amdgcn_exp2f(pm - M));
-    return M + __builtin_amdgcn_logf(S) + block_gumbel2(seed, b, pos, blk);
+    return M + __builtin_amdgcn_logf(S) + block_gumbel2(word);
 }
 
 // Epilogue of one lane (one request, 64 entries vh + entry_of(i, t)): the
@@ -213,6 +212,8 @@ __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4
     if (!greedy) {
         const float it = inv_temperature(T);
         const float c2 = it * kLog2e;
+        // the strip's blocks 2 s' and 2 s' + 1 share Philox counter s' / 2
+        const u32x4 rb = block_draws(seed, b, pos, vh >> 6);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             // a lane of the tail strip may hold no entry below V (mx = -inf)
@@ -226,8 +227,8 @@ __device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4
             RowState sb;
             sb.m = mx * it;
             sb.s = sum;
-            sb.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum, seed, b, pos,
-                                 (vh >> 6) + j);
+            sb.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum,
+                                 pick(rb, ((vh >> 6) + j) & 3));
             sb.zb = 0.0f;
             sb.idx = (vh & ~(kDraftBlock - 1)) + kDraftBlock * j;
             row_merge(st, sb);
@@ -387,14 +388,25 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-// wt[t] = strip buffer + tr_offset(lane, h, t).
+// Accumulator i of tile t holds entry 16 (i / 4) + 4 (t ^ ((i / 4) % 2)) + i % 4
+// of the lane's half, which is element 4 (t ^ ((i / 4) % 2)) + i % 4 of logit
+// chunk i / 4 (q = the half's four chunks): the accumulators start from the
+// logits, so the MFMAs leave s = base + bias in them.
+__device__ __forceinline__ void acc_from_logits(f32x16 (&acc)[2], const uint4 (&q)[4]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t dw = dword_of(q[i >> 2], 2 * (t ^ ((i >> 2) & 1)) + ((i & 3) >> 1));
+            acc[t][i] = __uint_as_float((i & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
+        }
+    }
+}
+
+// wt[t] = strip buffer + tr_offset(lane, h, t); acc holds the half's logits.
 template <int KS>
 __device__ __forceinline__ void bias_half(f32x16 (&acc)[2], const uint16_t* const (&wt)[2],
                                           const uint4 (&afr)[KS]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         const bf16x8 bv = as_bf16x8(afr[kk]);
@@ -457,24 +469,16 @@ __device__ __forceinline__ void logit_tail(uint4 (&q)[8], int v0, int kh, int V)
 }
 
 // Running state of a lane over the halves and strips it visits (sampled or
-// greedy; see draft_epilogue for the key).
-__device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], const uint4 (&q)[4],
-                                              int vh, float T, uint64_t seed, int b,
-                                              uint32_t pos) {
+// greedy; see draft_epilogue for the key).  acc holds s = base + bias of the
+// half (entry layout of acc_from_logits); `word` is the tag-3 draw of its
+// draft block.
+__device__ __forceinline__ void epilogue_half(RowState& run, const f32x16 (&acc)[2], int vh,
+                                              float T, uint32_t word) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            // entry 16 (i / 4) + 4 (t ^ ((i / 4) % 2)) + i % 4 of the lane's
-            // half: element 4 (t ^ ((i / 4) % 2)) + i % 4 of chunk i / 4
-            const uint32_t dw = dword_of(q[i >> 2], 2 * (t ^ ((i >> 2) & 1)) + ((i & 3) >> 1));
-            const float lg = __uint_as_float((i & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
-            const float sv = lg + acc[t][i];
-            acc[t][i] = sv;
-            mx = fmaxf(mx, sv);
-        }
-    }
+        for (int t = 0; t < 2; ++t) mx = fmaxf(mx, acc[t][i]);
     RowState st = row_empty();
     float best = -INFINITY;
     int be = 0;
@@ -493,7 +497,7 @@ __device__ __forceinline__ void epilogue_half(RowState& run, f32x16 (&acc)[2], c
             for (int t = 0; t < 2; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, -mc));
         st.m = mx * it;
         st.s = sum;
-        st.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum, seed, b, pos, vh >> 6);
+        st.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum, word);
         st.zb = 0.0f;
         st.idx = vh & ~(kDraftBlock - 1);
     } else {
@@ -574,14 +578,17 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
             load_logit_chunks(bn, brow, sn * kStripV, kh, V, 0, 2);
         }
         const uint16_t* wl = w_sh + buf * buf_elems;
+        // draft blocks 2 s and 2 s + 1: words 2 (s % 2) and 2 (s % 2) + 1 of one
+        // Philox block
+        const u32x4 rb = block_draws(seed, b, k + 1, 2 * s);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x16 acc[2];
             const uint16_t* const wt[2] = {wl + tro[h][0], wl + tro[h][1]};
+            acc_from_logits(acc, half_of(bl, h));
             bias_half<KS>(acc, wt, afr);
             if (more) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 2 + 4 * h, 4 + 4 * h);
-            epilogue_half(run, acc, half_of(bl, h), s * kStripV + 64 * h + 8 * kh, T, seed, b,
-                          k + 1);
+            epilogue_half(run, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
             if (more && h == 0) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 4, 6);
         }
         if (!more) break;
@@ -622,15 +629,12 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
     for (int s = blockIdx.x; s < n_strips; s += n_parts) {
         uint4 bl[8];
         load_strip_logits(bl, brow, s * kStripV, kh, V);
+        const u32x4 rb = block_draws(seed, b, k + 1, 2 * s);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x16 acc[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
-            epilogue_half(run, acc, half_of(bl, h), s * kStripV + 64 * h + 8 * kh, T, seed, b,
-                          k + 1);
+            acc_from_logits(acc, half_of(bl, h));
+            epilogue_half(run, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
         }
     }
     row_merge(run, shfl_xor_row(run, 32));
