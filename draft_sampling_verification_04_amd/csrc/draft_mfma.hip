@@ -170,14 +170,24 @@ __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_s
 // Key of the 64-entry draft block whose entries lanes l and l ^ 32 share (32
 // each): each lane's base-2 log-mass is mcb + log2(sum) (mcb = -inf: the lane
 // holds no entry below V); the block's log2-mass plus its base-2 Gumbel.
-// Both lanes of the pair compute the same key.
+// The pair exchanges its partials with gfx950's lane swap (no LDS round
+// trip): afterwards every lane holds the values of lanes l % 32 and l % 32 + 32,
+// in that order, so both lanes of the pair compute the same key.
+__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float block_key2(float mcb, float sum, uint32_t word) {
-    const float pm = __shfl_xor(mcb, 32, kWave);
-    const float ps = __shfl_xor(sum, 32, kWave);
-    const float M = fmaxf(mcb, pm);
+    float m0, m1, s0, s1;
+    lane_pair(mcb, m0, m1);
+    lane_pair(sum, s0, s1);
+    const float M = fmaxf(m0, m1);
     if (M == -INFINITY) return -INFINITY;
-    const float S = (mcb == -INFINITY ? 0.0f : sum * __builtin_amdgcn_exp2f(mcb - M)) +
-                    (pm == -INFINITY ? 0.0f : ps * __builtin_amdgcn_exp2f(pm - M));
+    const float S = (m0 == -INFINITY ? 0.0f : s0 * __builtin_amdgcn_exp2f(m0 - M)) +
+                    (m1 == -INFINITY ? 0.0f : s1 * __builtin_amdgcn_exp2f(m1 - M));
     return M + __builtin_amdgcn_logf(S) + block_gumbel2(word);
 }
 
