@@ -533,10 +533,55 @@ __device__ __forceinline__ void epilogue_half(RowState& run, const f32x16 (&acc)
     row_merge(run, st);
 }
 
+// One strip of draft_strip_mfma_rk: this strip's W is in `cur`, the next
+// strip's goes into `nxt`.  The caller alternates two static LDS arrays, so
+// every LDS access here names one array: the compiler then sees that the
+// transposing reads of `cur` cannot alias the direct loads into `nxt`, and
+// issues the MFMA loop without first waiting for the next strip's W (with one
+// dynamically indexed LDS array it has to wait for every outstanding direct
+// load before the first LDS read).  Returns false after the last strip.
+template <int NWAVES, int KS>
+__device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int& s, uint4 (&bl)[8],
+                                         RowState& run, const uint16_t* __restrict__ W,
+                                         const uint16_t* brow, const uint4 (&afr)[KS],
+                                         const int (&tro)[2][2], float T, uint64_t seed, int b,
+                                         int k, int V, int kh, int n_strips, int n_parts) {
+    // this strip's W (all waves' shares) and logits have landed, and every
+    // wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    logit_tail(bl, s * kStripV, kh, V);
+    const int sn = s + n_parts;
+    const bool more = sn < n_strips;
+    uint4 bn[8];
+    if (more) {
+        stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
+        load_logit_chunks(bn, brow, sn * kStripV, kh, V, 0, 2);
+    }
+    // draft blocks 2 s and 2 s + 1: words 2 (s % 2) and 2 (s % 2) + 1 of one
+    // Philox block
+    const u32x4 rb = block_draws(seed, b, k + 1, 2 * s);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f32x16 acc[2];
+        const uint16_t* const wt[2] = {cur + tro[h][0], cur + tro[h][1]};
+        acc_from_logits(acc, half_of(bl, h));
+        bias_half<KS>(acc, wt, afr);
+        if (more) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 2 + 4 * h, 4 + 4 * h);
+        epilogue_half(run, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
+        if (more && h == 0) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 4, 6);
+    }
+    if (!more) return false;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) bl[c] = bn[c];
+    s = sn;
+    return true;
+}
+
 // One workgroup per (part, request group), persistent over the strips part,
 // part + n_parts, ...: the factor fragments of each lane's request are loaded
 // once and stay in registers, so the MFMA loops issue no vector-memory loads.
-// The next strip's W (into the other LDS buffer) is requested as soon as a
+// The next strip's W (into the other LDS array) is requested as soon as a
 // strip starts, and its logits (into registers) two chunks at a time between
 // the strip's phases: issued all at once, the 16 loads of 8 waves queue behind
 // each other in the CU's memory pipeline and stall the waves that issue last.  Each lane folds the
@@ -549,7 +594,9 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
                       int prev_stride, const float* __restrict__ temperature,
                       const int32_t* __restrict__ order, uint64_t seed, int B, int K, int V,
                       int r, int k, PartialBuf part, int n_strips, int n_parts) {
-    extern __shared__ uint16_t w_sh[];  // two buffers of [r][kPitch]
+    // the two W buffers, [16 KS][kPitch] each (r == 16 KS)
+    __shared__ __attribute__((aligned(16))) uint16_t w_a[16 * KS * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t w_b[16 * KS * kPitch];
     const int lane = threadIdx.x & 63;
     const int kh = lane >> 5;
     const int slot = (blockIdx.y * NWAVES + (threadIdx.x >> 6)) * 32 + (lane & 31);
@@ -561,7 +608,6 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
     const float T = temperature[b];
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
     const uint16_t* brow = base + (static_cast<size_t>(b) * K + k) * V;
-    const int buf_elems = r * kPitch;
     uint4 afr[KS];  // r == 16 KS
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
@@ -569,43 +615,15 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
                            {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
 
     int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
-    stage_w_tr<NWAVES>(w_sh, W, r, V, s * kStripV);
+    stage_w_tr<NWAVES>(w_a, W, r, V, s * kStripV);
     uint4 bl[8];
     load_strip_logits(bl, brow, s * kStripV, kh, V);
     RowState run = row_empty();
-    int buf = 0;
-    for (;;) {
-        // this strip's W (all waves' shares) and logits have landed, and every
-        // wave is done with the other buffer
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        logit_tail(bl, s * kStripV, kh, V);
-        const int sn = s + n_parts;
-        const bool more = sn < n_strips;
-        uint4 bn[8];
-        if (more) {
-            stage_w_tr<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
-            load_logit_chunks(bn, brow, sn * kStripV, kh, V, 0, 2);
-        }
-        const uint16_t* wl = w_sh + buf * buf_elems;
-        // draft blocks 2 s and 2 s + 1: words 2 (s % 2) and 2 (s % 2) + 1 of one
-        // Philox block
-        const u32x4 rb = block_draws(seed, b, k + 1, 2 * s);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x16 acc[2];
-            const uint16_t* const wt[2] = {wl + tro[h][0], wl + tro[h][1]};
-            acc_from_logits(acc, half_of(bl, h));
-            bias_half<KS>(acc, wt, afr);
-            if (more) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 2 + 4 * h, 4 + 4 * h);
-            epilogue_half(run, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
-            if (more && h == 0) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 4, 6);
-        }
-        if (!more) break;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) bl[c] = bn[c];
-        buf ^= 1;
-        s = sn;
+    // strips alternate between w_a and w_b
+    while (rk_strip<NWAVES, KS>(w_a, w_b, s, bl, run, W, brow, afr, tro, T, seed, b, k, V, kh,
+                                n_strips, n_parts) &&
+           rk_strip<NWAVES, KS>(w_b, w_a, s, bl, run, W, brow, afr, tro, T, seed, b, k, V, kh,
+                                n_strips, n_parts)) {
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
     row_merge(run, shfl_xor_row(run, 32));
@@ -869,13 +887,14 @@ int device_cus() {
     return cus[dev];
 }
 
+// `lds` is the dynamic LDS of the launch (0 for a kernel whose W buffers are
+// static arrays).
 template <int NWAVES, typename Kern>
-hipError_t launch_draft_strip(Kern* kern, LdsReady& lds_ok, const DraftArgs& a, const int32_t* prev,
-                              int prev_stride, int k, const int32_t* order, PartialBuf part,
-                              int n_strips, int* n_parts) {
+hipError_t launch_draft_strip(Kern* kern, LdsReady& lds_ok, size_t lds, const DraftArgs& a,
+                              const int32_t* prev, int prev_stride, int k, const int32_t* order,
+                              PartialBuf part, int n_strips, int* n_parts) {
     hipError_t e = allow_big_lds(kern, lds_ok);
     if (e != hipSuccess) return e;
-    const size_t lds = 2 * sizeof(uint16_t) * static_cast<size_t>(a.r) * kPitch;
     // one resident workgroup per CU (the two W buffers take most of the LDS)
     const int groups = static_cast<int>(ceil_div(a.B, 32 * NWAVES));
     const int parts = std::max(1, std::min(n_strips, device_cus() / groups));
@@ -895,12 +914,13 @@ hipError_t launch_draft_step_nw(const DraftArgs& a, const int32_t* prev, int pre
                                 int* n_parts) {
     if (a.r == 256) {
         static LdsReady lds_ok;
-        return launch_draft_strip<NWAVES>(&draft_strip_mfma_rk<NWAVES, 16>, lds_ok, a, prev,
+        return launch_draft_strip<NWAVES>(&draft_strip_mfma_rk<NWAVES, 16>, lds_ok, 0, a, prev,
                                           prev_stride, k, order, part, n_strips, n_parts);
     }
     static LdsReady lds_ok;
-    return launch_draft_strip<NWAVES>(&draft_strip_mfma<NWAVES>, lds_ok, a, prev, prev_stride, k,
-                                      order, part, n_strips, n_parts);
+    const size_t lds = 2 * sizeof(uint16_t) * static_cast<size_t>(a.r) * kPitch;
+    return launch_draft_strip<NWAVES>(&draft_strip_mfma<NWAVES>, lds_ok, lds, a, prev, prev_stride,
+                                      k, order, part, n_strips, n_parts);
 }
 
 template <int NWAVES>
