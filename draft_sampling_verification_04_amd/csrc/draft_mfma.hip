@@ -478,59 +478,79 @@ __device__ __forceinline__ void logit_tail(uint4 (&q)[8], int v0, int kh, int V)
     }
 }
 
-// Running state of a lane over the halves and strips it visits (sampled or
-// greedy; see draft_epilogue for the key).  acc holds s = base + bias of the
-// half (entry layout of acc_from_logits); `word` is the tag-3 draw of its
-// draft block.
-__device__ __forceinline__ void epilogue_half(RowState& run, const f32x16 (&acc)[2], int vh,
+// Running state of a lane over the halves and strips it visits.  Sampled
+// (T > 0): the online-softmax partial of the lane's own entries in base 2 (m2 =
+// the largest z log2(e) seen, s = the sum of 2^(z log2(e) - m2)) and the best
+// draft-block key with its block start.  Greedy (T == 0): the largest logit
+// (key) and its entry.  lane_row turns it into the row state the combine
+// merges (m on the z scale).
+struct LaneRun {
+    float m2;
+    float s;
+    float key;
+    int idx;
+};
+
+__device__ __forceinline__ LaneRun lane_empty() { return {-INFINITY, 0.0f, -INFINITY, 0x7fffffff}; }
+
+__device__ __forceinline__ RowState lane_row(const LaneRun& r, bool sampled) {
+    return {r.m2 == -INFINITY ? -INFINITY : r.m2 * kLn2, r.s, r.key, sampled ? 0.0f : r.key,
+            r.idx};
+}
+
+// One half (entries vh + offsets of acc_from_logits' layout) into the running
+// state.  acc holds s = base + bias; `word` is the tag-3 draw of its draft block.
+__device__ __forceinline__ void epilogue_half(LaneRun& run, const f32x16 (&acc)[2], int vh,
                                               float T, uint32_t word) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
         for (int t = 0; t < 2; ++t) mx = fmaxf(mx, acc[t][i]);
-    RowState st = row_empty();
-    float best = -INFINITY;
-    int be = 0;
     if (T > 0.0f) {
         // sampled: this half is one draft block (entries vh & ~63 .. + 63, half
         // of them in the partner lane); its key enters the running state with
         // the block start as index, and the online-softmax sum covers the lane's
         // own entries
-        const float it = inv_temperature(T);
-        const float c2 = it * kLog2e;
-        const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
+        const float c2 = inv_temperature(T) * kLog2e;
+        const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
+        const float mr = (mx == -INFINITY) ? 0.0f : mc;
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, -mc));
-        st.m = mx * it;
-        st.s = sum;
-        st.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum, word);
-        st.zb = 0.0f;
-        st.idx = vh & ~(kDraftBlock - 1);
+            for (int t = 0; t < 2; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, -mr));
+        const float key = block_key2(mc, sum, word);
+        const int blk = vh & ~(kDraftBlock - 1);
+        const float M = fmaxf(run.m2, mc);
+        if (M != -INFINITY) {
+            // exp2(-inf) = 0 drops a side that holds no entry yet
+            run.s = run.s * __builtin_amdgcn_exp2f(run.m2 - M) + sum * __builtin_amdgcn_exp2f(mc - M);
+            run.m2 = M;
+        }
+        if (beats(key, blk, run.key, run.idx)) {
+            run.key = key;
+            run.idx = blk;
+        }
     } else {
-        // increasing entry order, so the first of equal maxima wins
+        // the first entry (in increasing order) that holds the largest logit:
+        // entries 16 a + 4 tt + w, visited from the last one down
+        int be = 0;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 3; a >= 0; --a) {
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int t = tt ^ (a & 1);  // entries 16 a + 4 tt + w
+            for (int tt = 1; tt >= 0; --tt) {
+                const int t = tt ^ (a & 1);
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    if (acc[t][4 * a + w] > best) {
-                        best = acc[t][4 * a + w];
-                        be = 16 * a + 4 * tt + w;
-                    }
-                }
+                for (int w = 3; w >= 0; --w)
+                    if (acc[t][4 * a + w] == mx) be = 16 * a + 4 * tt + w;
             }
         }
-        st.pert = best;
-        st.zb = best;
-        st.idx = vh + be;
+        if (beats(mx, vh + be, run.key, run.idx)) {
+            run.key = mx;
+            run.idx = vh + be;
+        }
     }
-    row_merge(run, st);
 }
 
 // One strip of draft_strip_mfma_rk: this strip's W is in `cur`, the next
@@ -542,7 +562,8 @@ __device__ __forceinline__ void epilogue_half(RowState& run, const f32x16 (&acc)
 // load before the first LDS read).  Returns false after the last strip.
 template <int NWAVES, int KS>
 __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int& s, uint4 (&bl)[8],
-                                         RowState& run, const uint16_t* __restrict__ W,
+                                         uint4 (&bn)[8], LaneRun& run,
+                                         const uint16_t* __restrict__ W,
                                          const uint16_t* brow, const uint4 (&afr)[KS],
                                          const int (&tro)[2][2], float T, uint64_t seed, int b,
                                          int k, int V, int kh, int n_strips, int n_parts) {
@@ -553,7 +574,6 @@ __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int
     logit_tail(bl, s * kStripV, kh, V);
     const int sn = s + n_parts;
     const bool more = sn < n_strips;
-    uint4 bn[8];
     if (more) {
         stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
         load_logit_chunks(bn, brow, sn * kStripV, kh, V, 0, 2);
@@ -572,8 +592,6 @@ __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int
         if (more && h == 0) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 4, 6);
     }
     if (!more) return false;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) bl[c] = bn[c];
     s = sn;
     return true;
 }
@@ -616,16 +634,17 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
 
     int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
     stage_w_tr<NWAVES>(w_a, W, r, V, s * kStripV);
-    uint4 bl[8];
-    load_strip_logits(bl, brow, s * kStripV, kh, V);
-    RowState run = row_empty();
-    // strips alternate between w_a and w_b
-    while (rk_strip<NWAVES, KS>(w_a, w_b, s, bl, run, W, brow, afr, tro, T, seed, b, k, V, kh,
-                                n_strips, n_parts) &&
-           rk_strip<NWAVES, KS>(w_b, w_a, s, bl, run, W, brow, afr, tro, T, seed, b, k, V, kh,
-                                n_strips, n_parts)) {
+    uint4 bl0[8], bl1[8];
+    load_strip_logits(bl0, brow, s * kStripV, kh, V);
+    LaneRun lr = lane_empty();
+    // strips alternate between w_a and w_b, and their logits between bl0 and bl1
+    while (rk_strip<NWAVES, KS>(w_a, w_b, s, bl0, bl1, lr, W, brow, afr, tro, T, seed, b, k, V,
+                                kh, n_strips, n_parts) &&
+           rk_strip<NWAVES, KS>(w_b, w_a, s, bl1, bl0, lr, W, brow, afr, tro, T, seed, b, k, V,
+                                kh, n_strips, n_parts)) {
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
+    RowState run = lane_row(lr, T > 0.0f);
     row_merge(run, shfl_xor_row(run, 32));
     if (active && kh == 0)
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
@@ -653,7 +672,7 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
     const int row = b * K + k;
     const float T = temperature[b];
     const uint16_t* brow = base + static_cast<size_t>(row) * V;
-    RowState run = row_empty();
+    LaneRun lr = lane_empty();
     for (int s = blockIdx.x; s < n_strips; s += n_parts) {
         uint4 bl[8];
         load_strip_logits(bl, brow, s * kStripV, kh, V);
@@ -662,9 +681,10 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
         for (int h = 0; h < 2; ++h) {
             f32x16 acc[2];
             acc_from_logits(acc, half_of(bl, h));
-            epilogue_half(run, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
+            epilogue_half(lr, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
         }
     }
+    RowState run = lane_row(lr, T > 0.0f);
     row_merge(run, shfl_xor_row(run, 32));
     if (active && kh == 0) store_partial(part, static_cast<size_t>(row) * n_parts + blockIdx.x, run);
 }
