@@ -136,11 +136,15 @@ __device__ __forceinline__ bool beats(float p1, int i1, float p0, int i0) {
     return p1 > p0 || (p1 == p0 && i1 < i0);
 }
 
+// The rescaling factors exp(m_a - m) lie in (0, 1]: the hardware exp2 of the
+// log2(e)-scaled difference is enough (no range reduction needed).
 __device__ __forceinline__ void row_merge(RowState& a, const RowState& b) {
     const float m = fmaxf(a.m, b.m);
     if (m != -INFINITY) {
-        const float sa = (a.m == -INFINITY) ? 0.0f : a.s * expf(a.m - m);
-        const float sb = (b.m == -INFINITY) ? 0.0f : b.s * expf(b.m - m);
+        const float sa =
+            (a.m == -INFINITY) ? 0.0f : a.s * __builtin_amdgcn_exp2f((a.m - m) * kLog2e);
+        const float sb =
+            (b.m == -INFINITY) ? 0.0f : b.s * __builtin_amdgcn_exp2f((b.m - m) * kLog2e);
         a.s = sa + sb;
         a.m = m;
     }
@@ -151,19 +155,59 @@ __device__ __forceinline__ void row_merge(RowState& a, const RowState& b) {
     }
 }
 
-__device__ __forceinline__ RowState shfl_xor_row(const RowState& a, int mask) {
-    RowState o;
-    o.m = __shfl_xor(a.m, mask, kWave);
-    o.s = __shfl_xor(a.s, mask, kWave);
-    o.pert = __shfl_xor(a.pert, mask, kWave);
-    o.zb = __shfl_xor(a.zb, mask, kWave);
-    o.idx = __shfl_xor(a.idx, mask, kWave);
-    return o;
+// Partner of each lane at step STEP of a wavefront all-reduce, by register
+// exchanges only (no LDS): steps 0 and 1 swap lanes within quads (l ^ 1,
+// l ^ 2, DPP quad_perm), step 2 mirrors each group of 8 (l ^ 7, DPP
+// row_half_mirror), step 3 each row of 16 (l ^ 15, DPP row_mirror), step 4
+// swaps adjacent rows of 16 (l ^ 16, v_permlane16_swap) and step 5 the halves
+// (l ^ 32, v_permlane32_swap).  The six masks are linearly independent bit
+// patterns, so after steps 0..s a commutative merge at every step leaves the
+// total of each aligned group of 2^(s+1) lanes in all of them.
+template <int STEP>
+__device__ __forceinline__ uint32_t xlane(uint32_t x) {
+    if constexpr (STEP == 0) {
+        return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (STEP == 1) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (STEP == 2) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false);
+    } else if constexpr (STEP == 3) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false);
+    } else if constexpr (STEP == 4) {
+        // rows 2 q + 1 of the first result and rows 2 q of the second hold the
+        // other row of each pair
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return ((threadIdx.x >> 5) & 1) ? r[0] : r[1];
+    }
 }
 
+template <int STEP>
+__device__ __forceinline__ float xlane_f(float x) {
+    return __uint_as_float(xlane<STEP>(__float_as_uint(x)));
+}
+template <int STEP>
+__device__ __forceinline__ int xlane_i(int x) {
+    return static_cast<int>(xlane<STEP>(static_cast<uint32_t>(x)));
+}
+
+template <int STEP>
+__device__ __forceinline__ RowState xlane_row(const RowState& a) {
+    return {xlane_f<STEP>(a.m), xlane_f<STEP>(a.s), xlane_f<STEP>(a.pert), xlane_f<STEP>(a.zb),
+            xlane_i<STEP>(a.idx)};
+}
+
+// Every lane ends with the wavefront's merged state (bit-identical in all
+// lanes: each step merges a symmetric pair with a commutative rule).
 __device__ __forceinline__ void wave_reduce_row(RowState& a) {
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) row_merge(a, shfl_xor_row(a, mask));
+    row_merge(a, xlane_row<0>(a));
+    row_merge(a, xlane_row<1>(a));
+    row_merge(a, xlane_row<2>(a));
+    row_merge(a, xlane_row<3>(a));
+    row_merge(a, xlane_row<4>(a));
+    row_merge(a, xlane_row<5>(a));
 }
 
 // Workgroup reduction of one RowState per thread; the result is valid in

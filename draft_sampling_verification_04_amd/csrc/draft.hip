@@ -146,6 +146,20 @@ __device__ __forceinline__ uint32_t dword_of4(const uint4& q, int i) {
     return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
 }
 
+// One step of a wavefront argmax (largest key, smallest entry on ties) that
+// carries a value with the winner; see xlane.
+template <int STEP>
+__device__ __forceinline__ void argmax_step(float& key, int& idx, float& val) {
+    const float ok = xlane_f<STEP>(key);
+    const int oi = xlane_i<STEP>(idx);
+    const float ov = xlane_f<STEP>(val);
+    if (beats(ok, oi, key, idx)) {
+        key = ok;
+        idx = oi;
+        val = ov;
+    }
+}
+
 // Fold the partials of each row and draw its token (one wavefront per row,
 // one wavefront per workgroup, so that the rows spread over every CU's memory
 // pipeline).  Rows are requests at step k (k >= 0: partial row
@@ -231,10 +245,13 @@ __global__ __launch_bounds__(kWave) void draft_combine(
                                     part8[e]);
                 }
             }
+            // sum over the 8 lanes of the rank groups (lanes 8 c .. 8 c + 7)
 #pragma unroll
-            for (int m = 1; m < 8; m <<= 1)
+            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<0>(part8[e]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) part8[e] += __shfl_xor(part8[e], m, kWave);
+            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<1>(part8[e]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<2>(part8[e]);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (e == g) bias = part8[e];
@@ -258,10 +275,13 @@ __global__ __launch_bounds__(kWave) void draft_combine(
                                     part8[e]);
                 }
             }
+            // sum over the 8 lanes of the rank groups (lanes 8 c .. 8 c + 7)
 #pragma unroll
-            for (int m = 1; m < 8; m <<= 1)
+            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<0>(part8[e]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) part8[e] += __shfl_xor(part8[e], m, kWave);
+            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<1>(part8[e]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<2>(part8[e]);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (e == g) bias = part8[e];
@@ -282,17 +302,12 @@ __global__ __launch_bounds__(kWave) void draft_combine(
     // wave argmax, smallest entry on ties
     int bv = (v < V) ? v : 0x7fffffff;
     float bsv = sv;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const float ok = __shfl_xor(key, m, kWave);
-        const int ov = __shfl_xor(bv, m, kWave);
-        const float os = __shfl_xor(bsv, m, kWave);
-        if (beats(ok, ov, key, bv)) {
-            key = ok;
-            bv = ov;
-            bsv = os;
-        }
-    }
+    argmax_step<0>(key, bv, bsv);
+    argmax_step<1>(key, bv, bsv);
+    argmax_step<2>(key, bv, bsv);
+    argmax_step<3>(key, bv, bsv);
+    argmax_step<4>(key, bv, bsv);
+    argmax_step<5>(key, bv, bsv);
     if (lane == 0) {
         tokens[o] = bv;
         if (lse) lse[o] = l;

@@ -322,7 +322,7 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
         s = sn;
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
-    row_merge(run, shfl_xor_row(run, 32));
+    row_merge(run, xlane_row<5>(run));
     if (active && kh == 0)
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
 }
@@ -645,7 +645,7 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
     RowState run = lane_row(lr, T > 0.0f);
-    row_merge(run, shfl_xor_row(run, 32));
+    row_merge(run, xlane_row<5>(run));
     if (active && kh == 0)
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
 }
@@ -685,7 +685,7 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
         }
     }
     RowState run = lane_row(lr, T > 0.0f);
-    row_merge(run, shfl_xor_row(run, 32));
+    row_merge(run, xlane_row<5>(run));
     if (active && kh == 0) store_partial(part, static_cast<size_t>(row) * n_parts + blockIdx.x, run);
 }
 
@@ -805,8 +805,8 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
         buf ^= 1;
         s = sn;
     }
-    row_merge(sr, shfl_xor_row(sr, 32));
-    row_merge(sf, shfl_xor_row(sf, 32));
+    row_merge(sr, xlane_row<5>(sr));
+    row_merge(sf, xlane_row<5>(sf));
     if (active && kh == 0) {
         store_partial(res, static_cast<size_t>(slot) * n_parts + blockIdx.x, sr);
         store_partial(fall, static_cast<size_t>(slot) * n_parts + blockIdx.x, sf);
