@@ -82,6 +82,34 @@ def stored_traffic():
         return None
 
 
+def verify_position_launches(K):
+    """Position ranges of the verify-rows launches when no per-row outputs are
+    asked for (the schedule dspark_verify documents): starts 1, 3, 5, 9, 17, ...,
+    and a launch that would leave one position takes it too."""
+    out, j = [], 1
+    while j <= K + 1:
+        left = K + 2 - j
+        span = min(2 if j <= 3 else j - 1, left)
+        if left - span <= 1:
+            span = left
+        out.append((j, j + span - 1))
+        j += span
+    return out
+
+
+def target_rows_read(lengths, accepted, K):
+    """Target rows verify reads without per-row outputs: request b takes part
+    in a launch over positions j0..j1 while rows 1..j0-1 were all accepted
+    (accepted[b] >= j0 - 1), and reads its rows j0..min(j1, L_b + 1) there."""
+    n = 0
+    for L_b, a_b in zip(lengths, accepted):
+        for j0, j1 in verify_position_launches(K):
+            if j0 > L_b + 1 or a_b < j0 - 1:
+                break
+            n += min(j1, L_b + 1) - j0 + 1
+    return n
+
+
 def host_cpu():
     model = "unknown"
     try:
@@ -409,9 +437,6 @@ def main():
     surv = torch.empty((B, K), dtype=torch.float32, device=dev)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
-    rows = target.shape[0]
-    rl = torch.empty(rows, dtype=torch.float32, device=dev)
-    rr = torch.empty(rows, dtype=torch.float32, device=dev)
     ws_d = torch.empty(d.dspark_draft_workspace_bytes(B, K, V, r), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(max(256, d.dspark_schedule_workspace_bytes(B, K)), dtype=torch.uint8,
                        device=dev)
@@ -439,8 +464,8 @@ def main():
         if events:
             events[2].record(stream)
         d.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"], inp["W"], target,
-                        offs, inp["temp"], seed, L, accepted=acc, next_token=nxt, row_lse_t=rl,
-                        row_logratio=rr, workspace=ws_v)
+                        offs, inp["temp"], seed, L, accepted=acc, next_token=nxt,
+                        row_outputs=False, workspace=ws_v)
         if events:
             events[3].record(stream)
 
@@ -487,6 +512,7 @@ def main():
 
     verified = int(L.sum())
     emitted = int(acc.sum()) + B
+    rows_read = target_rows_read(L.cpu().tolist(), acc.cpu().tolist(), K)
     tokens_per_s = B * K / (ms_step / 1e3)
 
     es = 2 if w.dtype == torch.bfloat16 else 4
@@ -498,10 +524,11 @@ def main():
     achieved_gbs = strip_bytes / strip_avg_s / 1e9
     traffic = stored_traffic()
 
-    # algorithmic bytes of the verify rows kernel per launch: every visited
-    # target row once (selected rows + the bonus row of each request)
+    # algorithmic bytes of the verify rows kernel per step (several launches):
+    # every target row it reads, once
     rows_ms, _, rows_timed = per_kernel["verify_rows"]
-    rows_bytes = es * (verified + B) * V
+    prof_steps = max(1, min(args.steps, 5))
+    rows_bytes = es * rows_read * V
     res_ms, _, res_timed = per_kernel["residual_strip"]
     rejected = int(((acc < L) & (inp["temp"] > 0)).sum())  # sampled rejections only
     res_bytes = es * (2 * rejected * V + r * V + rejected * r)
@@ -517,7 +544,9 @@ def main():
         hbm_gbs=gbs(strip_bytes, *per_kernel["draft_strip"][::2]),
         mfma_tflops=round(strip_flops / (per_kernel["draft_strip"][0] /
                                          max(per_kernel["draft_strip"][2], 1) / 1e3) / 1e12, 1))
-    kernels["verify_rows"].update(hbm_gbs=gbs(rows_bytes, rows_ms, rows_timed))
+    kernels["verify_rows"].update(hbm_gbs=gbs(rows_bytes, rows_ms, prof_steps),
+                                  target_rows_read_per_step=rows_read,
+                                  target_rows_scheduled_per_step=verified + B)
     kernels["residual_strip"].update(hbm_gbs=gbs(res_bytes, res_ms, res_timed))
 
     model, ncpu = host_cpu()
@@ -536,7 +565,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "K": K, "V": V, "r": r,
                    "temperatures": list(w.temps), "budget_tokens": budget,
-                   "verify": "every drafted token", "parallelism": "single GPU"},
+                   "verify": "every drafted token; target rows read up to each request's "
+                             "first rejection (position launches "
+                             + ", ".join(f"{a}-{b}" for a, b in verify_position_launches(K))
+                             + ")",
+                   "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
@@ -556,7 +589,7 @@ def main():
                       "verify": round(verify_ms, 4)},
         "kernels": kernels,
         "emitted_tokens_per_s": round(emitted / (ms_step / 1e3), 1),
-        "vocab_logits_per_s": round((B * K * V + (verified + B) * V) / (ms_step / 1e3), 1),
+        "vocab_logits_per_s": round((B * K * V + rows_read * V) / (ms_step / 1e3), 1),
         "host_cpu": f"{model} x{ncpu}",
     }
     if args.markov_vs_parallel:

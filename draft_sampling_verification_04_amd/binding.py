@@ -209,11 +209,13 @@ def dspark_schedule(conf, budget_tokens, curve_n=None, curve_latency=None, *, le
 def dspark_verify(draft_tokens, prev_token, draft_logp, draft_lse, base_logits, A, W,
                   target_logits, target_row_offsets, temperature, seed, lengths=None, *,
                   accepted=None, next_token=None, row_lse_t=None, row_logratio=None,
-                  workspace=None, stream=None):
+                  row_outputs=True, workspace=None, stream=None):
     """Rejection-sampling verification; returns (accepted, next_token, row_lse_t, row_logratio).
 
     target_logits is [rows, V] (or [B, K+1, V], viewed as rows); request b's
-    rows start at target_row_offsets[b] (int64, [B] or more entries)."""
+    rows start at target_row_offsets[b] (int64, [B] or more entries).
+    row_outputs=False passes no per-row outputs (both returned as None): the
+    library then reads only the target rows that can decide the result."""
     for t, n in ((draft_tokens, "draft_tokens"), (prev_token, "prev_token"),
                  (draft_logp, "draft_logp"), (draft_lse, "draft_lse"),
                  (base_logits, "base_logits"), (A, "A"), (W, "W"),
@@ -234,10 +236,14 @@ def dspark_verify(draft_tokens, prev_token, draft_logp, draft_lse, base_logits, 
         accepted = torch.empty(B, dtype=torch.int32, device=dev)
     if next_token is None:
         next_token = torch.empty(B, dtype=torch.int32, device=dev)
-    if row_lse_t is None:
-        row_lse_t = torch.full((n_rows,), float("nan"), dtype=torch.float32, device=dev)
-    if row_logratio is None:
-        row_logratio = torch.full((n_rows,), float("nan"), dtype=torch.float32, device=dev)
+    if not row_outputs:
+        if row_lse_t is not None or row_logratio is not None:
+            raise DsparkError(DSPARK_ERR_INVALID_ARG, "row outputs given with row_outputs=False")
+    else:
+        if row_lse_t is None:
+            row_lse_t = torch.full((n_rows,), float("nan"), dtype=torch.float32, device=dev)
+        if row_logratio is None:
+            row_logratio = torch.full((n_rows,), float("nan"), dtype=torch.float32, device=dev)
     workspace = _workspace(workspace, dspark_verify_workspace_bytes(B, K, V, r), dev)
     _check(lib().dspark_verify(
         _ptr(draft_tokens), _ptr(prev_token), _ptr(draft_logp), _ptr(draft_lse),

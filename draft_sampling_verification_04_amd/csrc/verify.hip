@@ -87,26 +87,56 @@ __device__ __forceinline__ void load8<float>(const float* row, int v0, int V, bo
     }
 }
 
+// Chunk v0 .. v0 + 7 of a row for the verify loop; entries past V read as
+// -inf, which changes no maximum, sum of exponentials or argmax.  VEC
+// (16-byte aligned rows, V % 8 == 0): an unconditional load, from the row's
+// last chunk when v0 is past V, so that the loads of one loop iteration go out
+// together with no branch between them.  Otherwise entries are read one by
+// one below V.
+template <typename LT, bool VEC>
+__device__ __forceinline__ void row_chunk(const LT* row, int v0, int V, float (&x)[8]) {
+    if constexpr (VEC) {
+        load8<LT>(row, min(v0, V - 8), V, true, x);
+        const bool past = v0 >= V;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = past ? -INFINITY : x[e];
+    } else {
+        load8<LT>(row, v0, V, false, x);
+    }
+}
+
 // verify_rows: one 512-thread workgroup per visited row with two 16-byte loads
 // in flight per lane (measured best among 64 / 256 / 512 / 1024 threads and
 // one, two or four loads per lane).
 constexpr int kVRowThreads = 512;
 constexpr int kVRowUnroll = 2;
 
-template <typename LT>
+template <typename LT, bool VEC>
 __global__ __launch_bounds__(kVRowThreads) void verify_rows(
     const LT* __restrict__ target, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ lengths, const int32_t* __restrict__ tokens,
     const float* __restrict__ draft_logp, const float* __restrict__ temperature, uint64_t seed,
-    int K, int V, int64_t n_rows, bool vec_ok, bool bonus_draw, float* __restrict__ row_lse_t,
-    float* __restrict__ row_logratio, VerifyWs ws) {
+    int K, int V, int64_t n_rows, bool bonus_draw, float* __restrict__ row_lse_t,
+    float* __restrict__ row_logratio, VerifyWs ws, int j_lo, int span) {
     __shared__ RowState red[kVRowThreads / kWave];
     const int64_t id = blockIdx.x;
-    const int b = static_cast<int>(id / (K + 1));
-    const int j = static_cast<int>(id - static_cast<int64_t>(b) * (K + 1)) + 1;
+    // the residual list starts empty; verify_resolve appends to it after the
+    // last launch of this kernel
+    if (j_lo == 1 && id == 0 && threadIdx.x == 0) *ws.count = 0;
+    // this launch covers positions j_lo .. j_lo + span - 1 of every request
+    const int b = static_cast<int>(id / span);
+    const int j = static_cast<int>(id - static_cast<int64_t>(b) * span) + j_lo;
     const int L = lengths ? clamp_len(lengths[b], K) : K;
     if (j > L + 1) return;
     if (row_off[b] < 0 || row_off[b] + L + 1 > n_rows) return;  // reported by verify_resolve
+    // Strict prefix: row j matters only while rows 1 .. j - 1 are all accepted.
+    // Rows of earlier launches are decided (thread i reads row i + 1's flag);
+    // a rejected one among them ends the request.
+    if (j_lo > 1) {
+        const int32_t* acc = ws.accept + static_cast<size_t>(b) * (K + 1);
+        const bool rejected = threadIdx.x < j_lo - 1 && !acc[threadIdx.x];
+        if (__syncthreads_or(rejected)) return;
+    }
     const int64_t row = row_off[b] + (j - 1);
     const float T = temperature[b];
     const bool greedy = !(T > 0.0f);
@@ -115,7 +145,6 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
     // not make it (bonus_draw); the normaliser is always computed
     const bool draw = bonus && bonus_draw;
     const LT* trow = target + row * static_cast<int64_t>(V);
-    const bool vec = vec_ok && (V % 8 == 0);
     RowState st = row_empty();
     if (greedy) {
         // argmax of t, smallest index on ties (visited in increasing v per thread)
@@ -126,12 +155,11 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
 #pragma unroll
             for (int u = 0; u < kVRowUnroll; ++u) {
                 const int v0 = c0 + u * kVRowThreads * 8;
-                if (v0 < V) load8<LT>(trow, v0, V, vec, xs[u]);
+                row_chunk<LT, VEC>(trow, v0, V, xs[u]);
             }
 #pragma unroll
             for (int u = 0; u < kVRowUnroll; ++u) {
                 const int v0 = c0 + u * kVRowThreads * 8;
-                if (v0 >= V) break;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     if (xs[u][e] > best) {
@@ -157,12 +185,11 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
 #pragma unroll
           for (int u = 0; u < kVRowUnroll; ++u) {
             const int v0 = c0 + u * kVRowThreads * 8;
-            if (v0 < V) load8<LT>(trow, v0, V, vec, xs[u]);
+            row_chunk<LT, VEC>(trow, v0, V, xs[u]);
           }
 #pragma unroll
           for (int u = 0; u < kVRowUnroll; ++u) {
             const int v0 = c0 + u * kVRowThreads * 8;
-            if (v0 >= V) break;
             const float (&x)[8] = xs[u];
             float cm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -223,11 +250,6 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
             if (row_logratio) row_logratio[row] = ratio;
         }
     }
-}
-
-__global__ void fill_i32(int32_t* p, int n, int32_t v) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
 }
 
 __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_rows,
@@ -438,6 +460,16 @@ size_t verify_workspace_bytes(int B, int K, int V, int r) {
     return verify_layout(B, K, V).total;
 }
 
+// Positions j_lo .. j_lo + span - 1 of one verify_rows launch when only the
+// rows that decide the result are read: launches start at positions 1, 3, 5,
+// 9, 17, ... (2, 2, 4, 8, ... positions), and a launch that would leave a
+// single position for the next one takes it too (K = 16: 1-2, 3-4, 5-8, 9-17).
+int verify_rows_chunk(int j_lo, int K) {
+    const int left = K + 2 - j_lo;  // positions j_lo .. K + 1
+    const int span = std::min((j_lo <= 3) ? 2 : j_lo - 1, left);
+    return (left - span <= 1) ? left : span;
+}
+
 hipError_t launch_verify(const VerifyArgs& a) {
     if (a.B == 0) return hipSuccess;
     const WsLayout l = verify_layout(a.B, a.K, a.V);
@@ -452,29 +484,41 @@ hipError_t launch_verify(const VerifyArgs& a) {
     ws.res = {reinterpret_cast<float4*>(w + l.res_v), reinterpret_cast<int32_t*>(w + l.res_i)};
     ws.fall = {reinterpret_cast<float4*>(w + l.fall_v), reinterpret_cast<int32_t*>(w + l.fall_i)};
 
-    hipLaunchKernelGGL(fill_i32, dim3(1), dim3(64), 0, a.stream, ws.count, 1, 0);
-    const dim3 rows_grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * (a.K + 1)));
-    const bool vec_ok = aligned16(a.target);
+    // whole 16-byte chunks of every row: the branch-free load path
+    const bool vec = aligned16(a.target) && a.V % 8 == 0;
     // With draft rows and the MFMA residual kernel, the sampled bonus draws are
     // made there (its fallback draw over row L_b + 1 is the bonus draw), only
     // for the requests that accepted every drafted token.
     const bool bonus_in_residual = a.K > 0 && residual_mfma_supported(a);
-    ProfScope rows_scope(DSPARK_KERNEL_VERIFY_ROWS, a.stream);
-    if (a.logit_dt == DSPARK_BF16) {
-        hipLaunchKernelGGL(verify_rows<bf16_t>, rows_grid, dim3(kVRowThreads), 0, a.stream,
-                           static_cast<const bf16_t*>(a.target), a.row_off, a.lengths, a.tokens,
-                           a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
-                           !bonus_in_residual, a.row_lse_t, a.row_logratio, ws);
-    } else {
-        hipLaunchKernelGGL(verify_rows<float>, rows_grid, dim3(kVRowThreads), 0, a.stream,
-                           static_cast<const float*>(a.target), a.row_off, a.lengths, a.tokens,
-                           a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows, vec_ok,
-                           !bonus_in_residual, a.row_lse_t, a.row_logratio, ws);
+    // With the per-row outputs requested every row is read (one launch over all
+    // positions).  Without them only the rows that can decide the result are:
+    // positions go in launches of 2, 2, 4, 8, ... and a request stops at the
+    // launch after its first rejection (verify_rows_chunk).
+    const bool every_row = a.row_lse_t != nullptr || a.row_logratio != nullptr;
+    hipError_t e = hipSuccess;
+    for (int j_lo = 1; j_lo <= a.K + 1;) {
+        const int span = every_row ? a.K + 1 : verify_rows_chunk(j_lo, a.K);
+        const dim3 rows_grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * span));
+        ProfScope rows_scope(DSPARK_KERNEL_VERIFY_ROWS, a.stream);
+        if (a.logit_dt == DSPARK_BF16) {
+            hipLaunchKernelGGL((vec ? verify_rows<bf16_t, true> : verify_rows<bf16_t, false>),
+                               rows_grid, dim3(kVRowThreads), 0, a.stream,
+                               static_cast<const bf16_t*>(a.target), a.row_off, a.lengths,
+                               a.tokens, a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows,
+                               !bonus_in_residual, a.row_lse_t, a.row_logratio, ws, j_lo, span);
+        } else {
+            hipLaunchKernelGGL((vec ? verify_rows<float, true> : verify_rows<float, false>),
+                               rows_grid, dim3(kVRowThreads), 0, a.stream,
+                               static_cast<const float*>(a.target), a.row_off, a.lengths,
+                               a.tokens, a.draft_logp, a.temperature, a.seed, a.K, a.V, a.n_rows,
+                               !bonus_in_residual, a.row_lse_t, a.row_logratio, ws, j_lo, span);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        prof_end(rows_scope.slot, a.stream);
+        rows_scope.slot = -1;
+        j_lo += span;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    prof_end(rows_scope.slot, a.stream);
-    rows_scope.slot = -1;
     {
         ProfScope resolve_scope(DSPARK_KERNEL_VERIFY_RESOLVE, a.stream);
         hipLaunchKernelGGL(verify_resolve, dim3(static_cast<unsigned>(ceil_div(a.B, 256))), dim3(256),

@@ -62,7 +62,14 @@ def _draft_and_verify(dsp, orc, inp, seed, idx, tol, lengths=None, row_off=None,
         row_off = torch.arange(B, dtype=torch.int64, device=tok.device) * (K + 1)
     acc, nxt, rl, rr = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
                                          inp["W"], target, row_off, inp["temp"], seed, lengths)
+    # without per-row outputs only the rows up to each request's first
+    # rejection are read (position launches 1-2, 3-4, 5-8, ...): the same result
+    acc2, nxt2, rl2, rr2 = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                             inp["W"], target, row_off, inp["temp"], seed,
+                                             lengths, row_outputs=False)
     torch.cuda.synchronize()
+    assert rl2 is None and rr2 is None
+    assert torch.equal(acc2, acc) and torch.equal(nxt2, nxt)
     L = {b: (K if lengths is None else int(lengths[b])) for b in idx}
     ro = row_off.cpu().numpy()
     rows = {b: P.np32(target[int(ro[b]):int(ro[b]) + L[b] + 1]) for b in idx}
@@ -221,10 +228,14 @@ def test_verify_edge_cases(dsp, orc, inputs):
     bad[3] = -1
     acc, nxt, _, _ = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
                                        inp["W"], target, bad, inp["temp"], 2)
+    acc2, nxt2, _, _ = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                         inp["W"], target, bad, inp["temp"], 2,
+                                         row_outputs=False)
     torch.cuda.synchronize()
     assert int(acc[1]) == 0 and int(nxt[1]) == -1
     assert int(acc[3]) == 0 and int(nxt[3]) == -1
     assert (nxt[[0, 2, 4]] >= 0).all()
+    assert torch.equal(acc2, acc) and torch.equal(nxt2, nxt)
 
 
 def test_two_streams_and_determinism(dsp, inputs):
