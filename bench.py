@@ -84,16 +84,11 @@ def stored_traffic():
 
 def verify_position_launches(K):
     """Position ranges of the verify-rows launches when no per-row outputs are
-    asked for (the schedule dspark_verify documents): starts 1, 3, 5, 9, 17, ...,
-    and a launch that would leave one position takes it too."""
-    out, j = [], 1
-    while j <= K + 1:
-        left = K + 2 - j
-        span = min(2 if j <= 3 else j - 1, left)
-        if left - span <= 1:
-            span = left
-        out.append((j, j + span - 1))
-        j += span
+    asked for (the schedule dspark_verify documents): 1..min(4, K+1), then
+    5..K+1."""
+    out = [(1, min(4, K + 1))]
+    if K + 1 > 4:
+        out.append((5, K + 1))
     return out
 
 

@@ -461,13 +461,14 @@ size_t verify_workspace_bytes(int B, int K, int V, int r) {
 }
 
 // Positions j_lo .. j_lo + span - 1 of one verify_rows launch when only the
-// rows that decide the result are read: launches start at positions 1, 3, 5,
-// 9, 17, ... (2, 2, 4, 8, ... positions), and a launch that would leave a
-// single position for the next one takes it too (K = 16: 1-2, 3-4, 5-8, 9-17).
+// rows that decide the result are read: positions 1-4, then 5 .. K + 1.  Each
+// launch costs about 27 us however few rows it holds, so more, smaller launches
+// lost (four launches 1-2, 3-4, 5-8, 9-17 took 134 us per long-draft step,
+// these two 114 us; 1-3/4-6/7-17, 1-4/5-8/9-17, 1-5/6-17 and 1-6/7-17 took
+// 123-129 us).
 int verify_rows_chunk(int j_lo, int K) {
     const int left = K + 2 - j_lo;  // positions j_lo .. K + 1
-    const int span = std::min((j_lo <= 3) ? 2 : j_lo - 1, left);
-    return (left - span <= 1) ? left : span;
+    return (j_lo == 1) ? std::min(4, left) : left;
 }
 
 hipError_t launch_verify(const VerifyArgs& a) {
@@ -492,8 +493,8 @@ hipError_t launch_verify(const VerifyArgs& a) {
     const bool bonus_in_residual = a.K > 0 && residual_mfma_supported(a);
     // With the per-row outputs requested every row is read (one launch over all
     // positions).  Without them only the rows that can decide the result are:
-    // positions go in launches of 2, 2, 4, 8, ... and a request stops at the
-    // launch after its first rejection (verify_rows_chunk).
+    // positions go in two launches (verify_rows_chunk) and a request whose
+    // first rejection lies in the first takes no part in the second.
     const bool every_row = a.row_lse_t != nullptr || a.row_logratio != nullptr;
     hipError_t e = hipSuccess;
     for (int j_lo = 1; j_lo <= a.K + 1;) {

@@ -171,10 +171,9 @@ size_t dspark_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r)
  * Rows read: with row_lse_t or row_logratio given, every row j = 1 .. L_b + 1
  * of every request is read and reported.  With both NULL only the rows that
  * can decide accepted and next_token are read (strict prefix: a row after the
- * first rejection changes nothing).  Positions are then verified in launches
- * starting at 1, 3, 5, 9, 17, ... (2, 2, 4, 8, ... positions; a launch that
- * would leave one position takes it too), and a request is dropped from the
- * launches after the one that holds its first rejection.  accepted and
+ * first rejection changes nothing).  Positions are then verified in two
+ * launches, 1 .. min(4, K + 1) and 5 .. K + 1, and a request whose first
+ * rejection lies in the first is not read in the second.  accepted and
  * next_token are the same either way.
  */
 dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_token,

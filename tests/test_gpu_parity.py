@@ -62,8 +62,8 @@ def _draft_and_verify(dsp, orc, inp, seed, idx, tol, lengths=None, row_off=None,
         row_off = torch.arange(B, dtype=torch.int64, device=tok.device) * (K + 1)
     acc, nxt, rl, rr = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
                                          inp["W"], target, row_off, inp["temp"], seed, lengths)
-    # without per-row outputs only the rows up to each request's first
-    # rejection are read (position launches 1-2, 3-4, 5-8, ...): the same result
+    # without per-row outputs only the rows that can decide the result are read
+    # (positions 1-4, then 5..K+1 for requests with no rejection in 1-4)
     acc2, nxt2, rl2, rr2 = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
                                              inp["W"], target, row_off, inp["temp"], seed,
                                              lengths, row_outputs=False)
