@@ -23,6 +23,10 @@ constexpr uint32_t kTagDraftBlock = 3;
 // logits inside the winning block (tag 0, word = entry).  Exact in distribution
 // for any partition; only the winning block needs per-entry draws.
 constexpr int kDraftBlock = 64;
+// The verifier's residual, fallback and bonus draws use the same 64-entry
+// blocks: block keys with tag-4 draws (word = block index), then tag-2 draws
+// (word = entry) inside the winning block.
+constexpr uint32_t kTagVerifyBlock = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

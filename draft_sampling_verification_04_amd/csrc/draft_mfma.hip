@@ -770,33 +770,43 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
         bias_tiles(acc, w_sh + buf * buf_elems, arow, r, lane);
         // requested after the MFMA loop's factor loads (in-order load counter)
         if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
+        // the strip's two 64-entry blocks: accumulators 8 j .. 8 j + 7 of every
+        // tile hold this lane's 32 entries of block j (the partner lane l ^ 32
+        // holds the other 32); both blocks take words of one tag-4 draw block
+        const u32x4 rb = philox_block(seed, b, js, kTagVerifyBlock, s >> 1);
         float br = -INFINITY, bf = -INFINITY;
         int ir = 0x7fffffff, jf = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int e0 = entry_of(i, 0);
-            const u32x4 rnd = philox_block(seed, b, js, kTagResample, (vh >> 2) + (e0 >> 2));
+        for (int j = 0; j < 2; ++j) {
+            // linear block masses of the residual max(0, p_t - p_d) and of p_t
+            // (entries past V have a = d = -inf and add nothing)
+            float mr = 0.0f, mf = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int v = vh + e0 + t;
-                const float d = fmaf(logit_at(bl, i, t) + acc[t][i], c2, -ld2);
-                const float a = fmaf(logit_at(tl, i, t), c2, -lt2);
-                const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, t)));
-                const float g2 = __builtin_amdgcn_logf(-l1);  // log2(-log2 u)
-                // entries past V have a = -inf and take part in neither draw
-                if (!bonus && a > d) {
-                    const float kr =
-                        a + __builtin_amdgcn_logf(1.0f - __builtin_amdgcn_exp2f(d - a)) - g2;
-                    if (kr > br) {
-                        br = kr;
-                        ir = v;
-                    }
+            for (int i = 8 * j; i < 8 * j + 8; ++i) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float d = fmaf(logit_at(bl, i, t) + acc[t][i], c2, -ld2);
+                    const float a = fmaf(logit_at(tl, i, t), c2, -lt2);
+                    const float pt = __builtin_amdgcn_exp2f(a);
+                    mr += fmaxf(pt - __builtin_amdgcn_exp2f(d), 0.0f);
+                    mf += pt;
                 }
-                const float kf = a - g2;
-                if (kf > bf) {
-                    bf = kf;
-                    jf = v;
-                }
+            }
+            float r0, r1, f0, f1;
+            lane_pair(mr, r0, r1);
+            lane_pair(mf, f0, f1);
+            const float g2 = block_gumbel2(pick(rb, 2 * (s & 1) + j));
+            const int blk = v0 + kDraftBlock * j;
+            const float mrb = r0 + r1, mfb = f0 + f1;
+            const float kr = (!bonus && mrb > 0.0f) ? __builtin_amdgcn_logf(mrb) + g2 : -INFINITY;
+            const float kf = (mfb > 0.0f) ? __builtin_amdgcn_logf(mfb) + g2 : -INFINITY;
+            if (kr > br) {
+                br = kr;
+                ir = blk;
+            }
+            if (kf > bf) {
+                bf = kf;
+                jf = blk;
             }
         }
         row_merge(sr, RowState{-INFINITY, 0.0f, br, br, ir});

@@ -36,7 +36,8 @@
  *   - random draws: Philox4x32-10 with key (seed lo32, seed hi32) and counter
  *     (v >> 2, position, request, tag); the draw for vocab index v is output
  *     word v & 3.  Tags: 0 draft Gumbel, 1 accept uniform (v = 0),
- *     2 residual / bonus Gumbel, 3 draft block Gumbel (v = block index).
+ *     2 residual / bonus Gumbel, 3 draft block Gumbel (v = block index),
+ *     4 residual / bonus block Gumbel (v = block index).
  *   - uniform u = ((w >> 9) + 0.5) * 2^-23, exact in fp32, in (0, 1).
  *   - Gumbel G = -log(-log u), evaluated in fp64 and rounded to fp32.
  *   - temperature T > 0 multiplies logits by the fp32 reciprocal 1/T on both
@@ -50,6 +51,13 @@
  *     (the first level picks a block with probability equal to its mass, the
  *     second an entry with its probability inside the block), and with
  *     V <= 64 it is the plain Gumbel-argmax.
+ *   - the verifier's draws (the residual at the first rejection, the fallback
+ *     to p_t and the bonus token) are made in two levels the same way, over
+ *     the same 64-entry blocks, with block draws of tag 4 and entry draws of
+ *     tag 2.  Residual: block mass sum of max(0, p_t - p_d) in fp64, block key
+ *     fp32(log mass) + G for blocks with positive mass, then inside the
+ *     winning block the Gumbel-argmax of fp32(log(p_t - p_d)) over its
+ *     positive entries.  Fallback and bonus: the two-level draw of y = t / T.
  */
 #include <math.h>
 #include <stdint.h>
@@ -58,7 +66,7 @@
 
 #define ORACLE_API __attribute__((visibility("default")))
 
-enum { TAG_DRAFT = 0, TAG_ACCEPT = 1, TAG_RESAMPLE = 2, TAG_DRAFT_BLOCK = 3 };
+enum { TAG_DRAFT = 0, TAG_ACCEPT = 1, TAG_RESAMPLE = 2, TAG_DRAFT_BLOCK = 3, TAG_VERIFY_BLOCK = 4 };
 enum { DRAFT_BLOCK = 64 };
 
 /* ------------------------------------------------------------------------ */
@@ -178,17 +186,13 @@ static int gumbel_argmax_range(const float* z, int lo, int hi, uint64_t seed, ui
     return best;
 }
 
-static int gumbel_argmax(const float* z, int V, uint64_t seed, uint32_t b, uint32_t pos,
-                         uint32_t tag, double* gap) {
-    return gumbel_argmax_range(z, 0, V, seed, b, pos, tag, gap);
-}
-
-/* Draft draw in two levels (see the readings above): block keys
- * fp32(log sum_{v in blk} exp z_v) + G(tag 3, blk), then the Gumbel-argmax of z
- * inside the winning block.  *gap is the smaller of the two levels' top-2
- * gaps, so a near tie at either level is reported. */
-static int gumbel_argmax_blocks(const float* z, int V, uint64_t seed, uint32_t b, uint32_t pos,
-                                double* gap) {
+/* Softmax draw in two levels (see the readings above): block keys
+ * fp32(log sum_{v in blk} exp z_v) + G(block_tag, blk), then the Gumbel-argmax
+ * of z inside the winning block with the entry_tag draws.  *gap is the smaller
+ * of the two levels' top-2 gaps, so a near tie at either level is reported. */
+static int gumbel_argmax_blocks_tags(const float* z, int V, uint64_t seed, uint32_t b,
+                                     uint32_t pos, uint32_t block_tag, uint32_t entry_tag,
+                                     double* gap) {
     const int nb = (V + DRAFT_BLOCK - 1) / DRAFT_BLOCK;
     int best = -1;
     float best_key = -INFINITY, second_key = -INFINITY;
@@ -196,7 +200,7 @@ static int gumbel_argmax_blocks(const float* z, int V, uint64_t seed, uint32_t b
         const int lo = blk * DRAFT_BLOCK;
         const int n = (V - lo < DRAFT_BLOCK) ? V - lo : DRAFT_BLOCK;
         float key = (float)log_sum_exp(z + lo, n) +
-                    oracle_gumbel(seed, b, pos, TAG_DRAFT_BLOCK, (uint32_t)blk);
+                    oracle_gumbel(seed, b, pos, block_tag, (uint32_t)blk);
         if (best < 0 || key > best_key) {
             second_key = best_key;
             best_key = key;
@@ -208,9 +212,66 @@ static int gumbel_argmax_blocks(const float* z, int V, uint64_t seed, uint32_t b
     const int lo = best * DRAFT_BLOCK;
     const int hi = (V - lo < DRAFT_BLOCK) ? V : lo + DRAFT_BLOCK;
     double g_entry;
-    const int x = gumbel_argmax_range(z, lo, hi, seed, b, pos, TAG_DRAFT, &g_entry);
+    const int x = gumbel_argmax_range(z, lo, hi, seed, b, pos, entry_tag, &g_entry);
     if (gap) {
         const double g_block = (double)best_key - (double)second_key;
+        *gap = g_block < g_entry ? g_block : g_entry;
+    }
+    return x;
+}
+
+/* The draft token draw: blocks with tag 3, entries with tag 0. */
+static int gumbel_argmax_blocks(const float* z, int V, uint64_t seed, uint32_t b, uint32_t pos,
+                                double* gap) {
+    return gumbel_argmax_blocks_tags(z, V, seed, b, pos, TAG_DRAFT_BLOCK, TAG_DRAFT, gap);
+}
+
+/* Residual draw in two levels: res[v] = p_t(v) - p_d(v) in fp64.  Blocks of 64
+ * entries with positive mass sum_{v in blk, res > 0} res_v compete with key
+ * fp32(log mass) + G(tag 4, blk); inside the winning block the token is the
+ * argmax over its positive entries of fp32(log res_v) + G(tag 2, v).  Returns
+ * -1 when no entry is positive (the caller then falls back to p_t). */
+static int residual_two_level(const double* res, int V, uint64_t seed, uint32_t b, uint32_t pos,
+                              double* gap) {
+    const int nb = (V + DRAFT_BLOCK - 1) / DRAFT_BLOCK;
+    int best = -1;
+    float best_key = -INFINITY, second_key = -INFINITY;
+    for (int blk = 0; blk < nb; ++blk) {
+        const int lo = blk * DRAFT_BLOCK;
+        const int hi = (V - lo < DRAFT_BLOCK) ? V : lo + DRAFT_BLOCK;
+        double mass = 0.0;
+        for (int v = lo; v < hi; ++v)
+            if (res[v] > 0.0) mass += res[v];
+        if (!(mass > 0.0)) continue;
+        const float key =
+            (float)log(mass) + oracle_gumbel(seed, b, pos, TAG_VERIFY_BLOCK, (uint32_t)blk);
+        if (best < 0 || key > best_key) {
+            second_key = best_key;
+            best_key = key;
+            best = blk;
+        } else if (key > second_key) {
+            second_key = key;
+        }
+    }
+    if (best < 0) return -1;
+    const int lo = best * DRAFT_BLOCK;
+    const int hi = (V - lo < DRAFT_BLOCK) ? V : lo + DRAFT_BLOCK;
+    int x = -1;
+    float bv = -INFINITY, sv = -INFINITY;
+    for (int v = lo; v < hi; ++v) {
+        if (!(res[v] > 0.0)) continue;
+        const float p = (float)log(res[v]) + oracle_gumbel(seed, b, pos, TAG_RESAMPLE, (uint32_t)v);
+        if (x < 0 || p > bv) {
+            sv = bv;
+            bv = p;
+            x = v;
+        } else if (p > sv) {
+            sv = p;
+        }
+    }
+    if (gap) {
+        const double g_block = (double)best_key - (double)second_key;
+        const double g_entry = (double)bv - (double)sv;
         *gap = g_block < g_entry ? g_block : g_entry;
     }
     return x;
@@ -340,7 +401,6 @@ ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t p
     float* z = (float*)malloc(sizeof(float) * (size_t)V);
     float* y = (float*)malloc(sizeof(float) * (size_t)V);
     double* scratch = (double*)malloc(sizeof(double) * (size_t)V);
-    float* pert = (float*)malloc(sizeof(float) * (size_t)V);
     const float it = (T > 0.0f) ? inv_temperature(T) : 1.0f;
     double min_gap = INFINITY;
     int a = 0;
@@ -401,38 +461,12 @@ ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t p
             double lse_d = log_sum_exp(z, V);
             for (int v = 0; v < V; ++v) y[v] = t[v] * it;
             double lse_t = log_sum_exp(y, V);
-            int any = 0;
-            for (int v = 0; v < V; ++v) {
-                double pt = exp((double)y[v] - lse_t);
-                double pd = exp((double)z[v] - lse_d);
-                double res = pt - pd;
-                if (res > 0.0) {
-                    float lr = (float)log(res);
-                    pert[v] = lr + oracle_gumbel(seed, b, (uint32_t)js, TAG_RESAMPLE, (uint32_t)v);
-                    any = 1;
-                } else {
-                    pert[v] = -INFINITY;
-                }
-            }
-            if (any) {
-                /* argmax over the positive-residual entries only */
-                int best = -1;
-                float bv = -INFINITY, sv = -INFINITY;
-                for (int v = 0; v < V; ++v) {
-                    if (pert[v] == -INFINITY) continue;
-                    if (best < 0 || pert[v] > bv) {
-                        sv = bv;
-                        bv = pert[v];
-                        best = v;
-                    } else if (pert[v] > sv) {
-                        sv = pert[v];
-                    }
-                }
-                next = best;
-                ng = (double)bv - (double)sv;
-            } else {
-                next = gumbel_argmax(y, V, seed, b, (uint32_t)js, TAG_RESAMPLE, &ng);
-            }
+            for (int v = 0; v < V; ++v)
+                scratch[v] = exp((double)y[v] - lse_t) - exp((double)z[v] - lse_d);
+            next = residual_two_level(scratch, V, seed, b, (uint32_t)js, &ng);
+            if (next < 0)  /* no positive residual mass (rounding only) */
+                next = gumbel_argmax_blocks_tags(y, V, seed, b, (uint32_t)js, TAG_VERIFY_BLOCK,
+                                                 TAG_RESAMPLE, &ng);
         } else {
             next = plain_argmax(t, V, &ng);
         }
@@ -440,7 +474,8 @@ ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t p
         const float* t = target + (size_t)L * (size_t)V;
         if (T > 0.0f) {
             for (int v = 0; v < V; ++v) y[v] = t[v] * it;
-            next = gumbel_argmax(y, V, seed, b, (uint32_t)(L + 1), TAG_RESAMPLE, &ng);
+            next = gumbel_argmax_blocks_tags(y, V, seed, b, (uint32_t)(L + 1), TAG_VERIFY_BLOCK,
+                                             TAG_RESAMPLE, &ng);
         } else {
             next = plain_argmax(t, V, &ng);
         }
@@ -453,7 +488,6 @@ ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t p
     free(z);
     free(y);
     free(scratch);
-    free(pert);
 }
 
 /* Batch form over ragged target rows: request b's rows start at row_offset[b]

@@ -231,3 +231,70 @@ def test_row_outputs(orc):
                                    rtol=1e-5, atol=1e-5)
         prev = tok[j]
     assert res["row_logratio"][K] == 0.0
+
+
+def _chi2_ok(counts, p, min_expect=20.0):
+    """Chi-square of counts against probabilities p, with the bins expected
+    below min_expect lumped into one."""
+    n = counts.sum()
+    e = p * n
+    big = e >= min_expect
+    obs = np.append(counts[big], counts[~big].sum())
+    exp = np.append(e[big], e[~big].sum())
+    keep = exp > 0
+    obs, exp = obs[keep], exp[keep]
+    chi2 = ((obs - exp) ** 2 / exp).sum()
+    return stats.chi2.sf(chi2, len(obs) - 1) > 1e-3
+
+
+def _three_block_case(seed_rng):
+    V, r = 150, 4
+    rng = np.random.default_rng(seed_rng)
+    base = rng.normal(0, 1.0, (1, V)).astype(np.float32)
+    A = rng.normal(0, 0.5, (V, r)).astype(np.float32)
+    W = rng.normal(0, 0.5, (r, V)).astype(np.float32)
+    rows = np.stack([base[0] + rng.normal(0, 1.5, V), rng.normal(0, 1.2, V)]).astype(np.float32)
+    return V, base, A, W, rows
+
+
+def test_two_level_residual_over_several_blocks(orc):
+    """After a rejection at position 1 the next token is drawn in two levels
+    (block mass of max(0, p_t - p_d), then inside the block) over three blocks
+    of 64 + 64 + 22 entries; it must follow normalise(max(0, p_t - p_d)) per
+    entry and per block."""
+    V, base, A, W, rows = _three_block_case(33)
+    T, prev = 1.0, 3
+    pd = orc.draft_probs(base[0], A, W, prev, T)
+    pt = orc.target_probs(rows[0], T)
+    res = np.maximum(pt - pd, 0.0)
+    res /= res.sum()
+    counts = np.zeros(V, np.int64)
+    for seed in range(40000):
+        tok, _, _, _ = orc.draft_request(base, A, W, prev, T, seed, 0)
+        out = orc.verify_request(tok, prev, base, A, W, rows, 1, T, seed, 0)
+        if out["accepted"] == 0:
+            counts[out["next_token"]] += 1
+    assert counts.sum() > 10000
+    assert _chi2_ok(counts, res)
+    blocks = np.arange(V) // 64
+    cb = np.bincount(blocks, weights=counts, minlength=3)
+    eb = np.array([res[blocks == j].sum() for j in range(3)])
+    assert _chi2_ok(cb, eb)
+
+
+def test_two_level_bonus_over_several_blocks(orc):
+    """With L = 0 the next token is the bonus draw from target row 1, in two
+    levels over three blocks; it must follow p_t per entry and per block."""
+    V, base, A, W, rows = _three_block_case(34)
+    T, prev = 0.8, 5
+    pt = orc.target_probs(rows[1], T)
+    counts = np.zeros(V, np.int64)
+    tok = np.zeros(1, np.int32)
+    for seed in range(30000):
+        out = orc.verify_request(tok, prev, base, A, W, rows[1:2], 0, T, seed, 0)
+        counts[out["next_token"]] += 1
+    assert _chi2_ok(counts, pt)
+    blocks = np.arange(V) // 64
+    cb = np.bincount(blocks, weights=counts, minlength=3)
+    eb = np.array([pt[blocks == j].sum() for j in range(3)])
+    assert _chi2_ok(cb, eb)
