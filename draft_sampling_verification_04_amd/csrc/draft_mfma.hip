@@ -692,17 +692,17 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
 // --------------------------------------------------------------- residual
 // For every request whose first rejection is at j* = a_b + 1 (sampled, T > 0):
 // recompute the draft logits at j* (previous token x_{j*-1}), read the target
-// row, and draw next ~ normalise(max(0, p_t - p_d)) by Gumbel-max of
-// log(p_t - p_d) over the positive entries (tag 2, position j*).  The Gumbel-max
-// of the target row with the same draws is kept as the fallback for a residual
-// without positive mass.  Rejected requests are listed in `list` (count
-// entries), and so are sampled requests that accepted every drafted token:
-// their bonus token is exactly that fallback draw over row L_b + 1.
-// In base 2, with c = log2(e) / T: a = log2 p_t = t c - lse_t log2(e) and
-// d = log2 p_d = s c - lse_d log2(e), so p_t > p_d iff a > d and
-// log2(p_t - p_d) = a + log2(1 - 2^(d - a)).  Keys are log2 r - log2(-log2 u)
-// (residual) and a - log2(-log2 u) (fallback), each log2(e) (log x + G) up to
-// a constant shared by the row, so they order entries as the natural-log forms.
+// row, and make the first level of the draws from normalise(max(0, p_t - p_d))
+// and, as the fallback for a residual without positive mass, from p_t: per
+// 64-entry block the masses of max(0, p_t - p_d) and of p_t, and the block
+// keys log2 mass - log2(-log2 u) with the block's tag-4 draw (position j*).
+// verify_residual_combine then draws inside the winning block.  Rejected
+// requests are listed in `list` (count entries), and so are sampled requests
+// that accepted every drafted token: their bonus token is exactly that
+// fallback draw over row L_b + 1.  With c = log2(e) / T: a = log2 p_t =
+// t c - lse_t log2(e) and d = log2 p_d = s c - lse_d log2(e); the block keys
+// are log2(e) (log mass + G) up to a constant shared by the row, so they order
+// blocks as the natural-log forms do.
 // Persistent like the draft kernel: one workgroup per (part, slot group) walks
 // the strips part, part + n_parts, ... with W double-buffered in LDS.
 template <int NWAVES>
