@@ -878,6 +878,193 @@ __global__ __launch_bounds__(1024) void temperature_order(const float* __restric
     }
 }
 
+// ------------------------------------------------- residual: rank 256
+// The residual strip of residual_strip_mfma for rank 256, built like
+// draft_strip_mfma_rk: factor fragments in registers (the MFMA loops issue no
+// vector-memory loads), W double-buffered in two static LDS arrays, and a
+// strip worked in two 64-entry halves (one block each).  The base and target
+// logits of a half are loaded one phase ahead into registers that the phase
+// before has freed: a strip's half-1 base logits go out before the next
+// strip's W, so waiting for them never waits for that W.
+
+// Chunks a = 0..3 of half h of a lane's strip logits (entries v0 + 64 h +
+// 16 a + 8 kh .. + 7); loads in bounds (the row's last chunk stands in past V).
+__device__ __forceinline__ void load_half(uint4 (&q)[4], const uint16_t* row, int v0, int h,
+                                          int kh, int V) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+        q[a] = *reinterpret_cast<const uint4*>(row + min(v0 + 64 * h + 16 * a + 8 * kh, V - 8));
+}
+
+// Chunks past V become bf16 -inf once the loads have landed.
+__device__ __forceinline__ void tail_half(uint4 (&q)[4], int v0, int h, int kh, int V) {
+    if (v0 + kStripV > V) {
+        const uint32_t ninf2 = 0xFF80FF80u;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            if (v0 + 64 * h + 16 * a + 8 * kh >= V) q[a] = make_uint4(ninf2, ninf2, ninf2, ninf2);
+    }
+}
+
+// Block masses and keys of one half (one 64-entry block; see
+// residual_strip_mfma): acc holds s = base + bias, tq the target logits in the
+// same entry layout (acc_from_logits).
+__device__ __forceinline__ void residual_half(const f32x16 (&acc)[2], const uint4 (&tq)[4],
+                                              float c2, float ld2, float lt2, bool bonus,
+                                              uint32_t word, int blk, float& br, int& ir,
+                                              float& bf, int& jf) {
+    float mr = 0.0f, mf = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t dw = dword_of(tq[i >> 2], 2 * (t ^ ((i >> 2) & 1)) + ((i & 3) >> 1));
+            const float tv = __uint_as_float((i & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
+            const float d = fmaf(acc[t][i], c2, -ld2);
+            const float a = fmaf(tv, c2, -lt2);
+            const float pt = __builtin_amdgcn_exp2f(a);
+            mr += fmaxf(pt - __builtin_amdgcn_exp2f(d), 0.0f);
+            mf += pt;
+        }
+    }
+    float r0, r1, f0, f1;
+    lane_pair(mr, r0, r1);
+    lane_pair(mf, f0, f1);
+    const float g2 = block_gumbel2(word);
+    const float mrb = r0 + r1, mfb = f0 + f1;
+    const float kr = (!bonus && mrb > 0.0f) ? __builtin_amdgcn_logf(mrb) + g2 : -INFINITY;
+    const float kf = (mfb > 0.0f) ? __builtin_amdgcn_logf(mfb) + g2 : -INFINITY;
+    if (kr > br) {
+        br = kr;
+        ir = blk;
+    }
+    if (kf > bf) {
+        bf = kf;
+        jf = blk;
+    }
+}
+
+struct ResLane {
+    const uint16_t* brow;
+    const uint16_t* trow;
+    float c2, ld2, lt2;
+    bool bonus;
+    int b, js;
+    float br, bf;
+    int ir, jf;
+};
+
+// One strip: this strip's W is in `cur`, the next strip's goes into `nxt`;
+// b0 / t0 hold this strip's half-0 logits on entry and the next strip's on
+// return.
+template <int NWAVES, int KS>
+__device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t* nxt, int& s,
+                                                  uint4 (&b0)[4], uint4 (&t0)[4], ResLane& L,
+                                                  const uint16_t* __restrict__ W,
+                                                  const uint4 (&afr)[KS], const int (&tro)[2][2],
+                                                  uint64_t seed, int V, int kh, int n_strips,
+                                                  int n_parts) {
+    // this strip's W (all waves' shares) and half-0 logits have landed, and
+    // every wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int v0 = s * kStripV;
+    tail_half(b0, v0, 0, kh, V);
+    tail_half(t0, v0, 0, kh, V);
+    const int sn = s + n_parts;
+    const bool more = sn < n_strips;
+    uint4 b1[4], t1[4];
+    load_half(b1, L.brow, v0, 1, kh, V);  // before the next W: its wait does not include it
+    if (more) stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
+    const u32x4 rb = philox_block(seed, L.b, L.js, kTagVerifyBlock, s >> 1);
+    f32x16 acc[2];
+    {
+        const uint16_t* const wt[2] = {cur + tro[0][0], cur + tro[0][1]};
+        acc_from_logits(acc, b0);
+        bias_half<KS>(acc, wt, afr);
+    }
+    if (more) load_half(b0, L.brow, sn * kStripV, 0, kh, V);
+    residual_half(acc, t0, L.c2, L.ld2, L.lt2, L.bonus, pick(rb, 2 * (s & 1)), v0, L.br, L.ir,
+                  L.bf, L.jf);
+    load_half(t1, L.trow, v0, 1, kh, V);
+    if (more) load_half(t0, L.trow, sn * kStripV, 0, kh, V);
+    tail_half(b1, v0, 1, kh, V);
+    {
+        const uint16_t* const wt[2] = {cur + tro[1][0], cur + tro[1][1]};
+        acc_from_logits(acc, b1);
+        bias_half<KS>(acc, wt, afr);
+    }
+    tail_half(t1, v0, 1, kh, V);
+    residual_half(acc, t1, L.c2, L.ld2, L.lt2, L.bonus, pick(rb, 2 * (s & 1) + 1),
+                  v0 + kDraftBlock, L.br, L.ir, L.bf, L.jf);
+    if (!more) return false;
+    s = sn;
+    return true;
+}
+
+template <int NWAVES, int KS>
+__global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
+    const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
+    const uint16_t* __restrict__ W, const uint16_t* __restrict__ target,
+    const int64_t* __restrict__ row_off, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ prev_token, const float* __restrict__ draft_lse,
+    const float* __restrict__ temperature, const int32_t* __restrict__ accepted,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ count_ptr,
+    const int32_t* __restrict__ lengths, const float* __restrict__ lse_tab, uint64_t seed, int K,
+    int V, int r, PartialBuf res, PartialBuf fall, int n_strips, int n_parts) {
+    __shared__ __attribute__((aligned(16))) uint16_t w_a[16 * KS * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t w_b[16 * KS * kPitch];
+    const int count = *count_ptr;
+    const int slot0 = blockIdx.y * NWAVES * 32;
+    if (slot0 >= count) return;  // whole workgroup idle
+    const int lane = threadIdx.x & 63;
+    const int kh = lane >> 5;
+    const int slot = slot0 + (threadIdx.x >> 6) * 32 + (lane & 31);
+    const bool active = slot < count;
+    // lanes past the list run request list[0]'s rows and store nothing
+    ResLane L;
+    L.b = list[active ? slot : 0];
+    L.js = accepted[L.b] + 1;
+    // js > L_b: a listed full acceptance (its bonus is the fallback draw over
+    // row L_b + 1); its draft side reads row 1 as an in-range stand-in
+    L.bonus = L.js > (lengths ? clamp_len(lengths[L.b], K) : K);
+    const int jd = L.bonus ? 1 : L.js;
+    const int p = clamp_token(
+        (jd == 1) ? prev_token[L.b] : tokens[static_cast<size_t>(L.b) * K + jd - 2], V);
+    L.c2 = inv_temperature(temperature[L.b]) * kLog2e;
+    L.ld2 = draft_lse[static_cast<size_t>(L.b) * K + jd - 1] * kLog2e;
+    L.lt2 = lse_tab[static_cast<size_t>(L.b) * (K + 1) + L.js - 1] * kLog2e;
+    L.brow = base + (static_cast<size_t>(L.b) * K + jd - 1) * V;
+    L.trow = target + (row_off[L.b] + L.js - 1) * static_cast<int64_t>(V);
+    L.br = -INFINITY;
+    L.bf = -INFINITY;
+    L.ir = 0x7fffffff;
+    L.jf = 0x7fffffff;
+    const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
+    uint4 afr[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
+    const int tro[2][2] = {{tr_offset(lane, 0, 0), tr_offset(lane, 0, 1)},
+                           {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
+    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
+    stage_w_tr<NWAVES>(w_a, W, r, V, s * kStripV);
+    uint4 b0[4], t0[4];
+    load_half(b0, L.brow, s * kStripV, 0, kh, V);
+    load_half(t0, L.trow, s * kStripV, 0, kh, V);
+    while (residual_rk_strip<NWAVES, KS>(w_a, w_b, s, b0, t0, L, W, afr, tro, seed, V, kh,
+                                         n_strips, n_parts) &&
+           residual_rk_strip<NWAVES, KS>(w_b, w_a, s, b0, t0, L, W, afr, tro, seed, V, kh,
+                                         n_strips, n_parts)) {
+    }
+    // both lanes of a pair hold the same keys
+    if (active && kh == 0) {
+        store_partial(res, static_cast<size_t>(slot) * n_parts + blockIdx.x,
+                      RowState{-INFINITY, 0.0f, L.br, L.br, L.ir});
+        store_partial(fall, static_cast<size_t>(slot) * n_parts + blockIdx.x,
+                      RowState{-INFINITY, 0.0f, L.bf, L.bf, L.jf});
+    }
+}
+
 constexpr int kMaxLds = 160 * 1024;
 
 // Devices a kernel's LDS limit has been raised on (the attribute is per device).
@@ -955,10 +1142,27 @@ hipError_t launch_draft_step_nw(const DraftArgs& a, const int32_t* prev, int pre
 
 template <int NWAVES>
 hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
+    const VerifyArgs& v = *a.v;
+    if (v.r == 256) {
+        static LdsReady lds_rk;
+        hipError_t e = allow_big_lds(&residual_strip_mfma_rk<NWAVES, 16>, lds_rk);
+        if (e != hipSuccess) return e;
+        const int groups = static_cast<int>(ceil_div(v.B, 32 * NWAVES));
+        const int parts = std::max(1, std::min(a.n_strips, device_cus() / groups));
+        *n_parts = parts;
+        dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(groups));
+        hipLaunchKernelGGL((residual_strip_mfma_rk<NWAVES, 16>), grid, dim3(64 * NWAVES), 0,
+                           v.stream, static_cast<const uint16_t*>(v.base),
+                           static_cast<const uint16_t*>(v.A), static_cast<const uint16_t*>(v.W),
+                           static_cast<const uint16_t*>(v.target), v.row_off, v.tokens,
+                           v.prev_token, v.draft_lse, v.temperature, v.accepted, a.list, a.count,
+                           v.lengths, a.lse_tab, v.seed, v.K, v.V, v.r, a.res, a.fall, a.n_strips,
+                           parts);
+        return hipGetLastError();
+    }
     static LdsReady lds_ok;
     hipError_t e = allow_big_lds(&residual_strip_mfma<NWAVES>, lds_ok);
     if (e != hipSuccess) return e;
-    const VerifyArgs& v = *a.v;
     const size_t lds = 2 * sizeof(uint16_t) * static_cast<size_t>(v.r) * kPitch;
     const int groups = static_cast<int>(ceil_div(v.B, 32 * NWAVES));
     const int parts = std::max(1, std::min(a.n_strips, device_cus() / groups));
