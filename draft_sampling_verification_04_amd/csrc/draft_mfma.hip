@@ -963,12 +963,20 @@ __device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t*
                                                   const uint16_t* __restrict__ W,
                                                   const uint4 (&afr)[KS], const int (&tro)[2][2],
                                                   uint64_t seed, int V, int kh, int n_strips,
-                                                  int n_parts) {
+                                                  int n_parts, bool busy) {
     // this strip's W (all waves' shares) and half-0 logits have landed, and
     // every wave is done with the other buffer
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int v0 = s * kStripV;
+    if (!busy) {
+        // a wave with no listed request only stages its share of W
+        const int sn = s + n_parts;
+        if (sn >= n_strips) return false;
+        stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
+        s = sn;
+        return true;
+    }
     tail_half(b0, v0, 0, kh, V);
     tail_half(t0, v0, 0, kh, V);
     const int sn = s + n_parts;
@@ -1021,6 +1029,8 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     const int kh = lane >> 5;
     const int slot = slot0 + (threadIdx.x >> 6) * 32 + (lane & 31);
     const bool active = slot < count;
+    // waves wholly past the list only stage W and meet the barriers
+    const bool busy = slot0 + (threadIdx.x >> 6) * 32 < count;
     // lanes past the list run request list[0]'s rows and store nothing
     ResLane L;
     L.b = list[active ? slot : 0];
@@ -1042,19 +1052,23 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     L.jf = 0x7fffffff;
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
     uint4 afr[KS];
+    uint4 b0[4], t0[4];
+    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
+    if (busy) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
+        for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
+    }
     const int tro[2][2] = {{tr_offset(lane, 0, 0), tr_offset(lane, 0, 1)},
                            {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
-    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
     stage_w_tr<NWAVES>(w_a, W, r, V, s * kStripV);
-    uint4 b0[4], t0[4];
-    load_half(b0, L.brow, s * kStripV, 0, kh, V);
-    load_half(t0, L.trow, s * kStripV, 0, kh, V);
+    if (busy) {
+        load_half(b0, L.brow, s * kStripV, 0, kh, V);
+        load_half(t0, L.trow, s * kStripV, 0, kh, V);
+    }
     while (residual_rk_strip<NWAVES, KS>(w_a, w_b, s, b0, t0, L, W, afr, tro, seed, V, kh,
-                                         n_strips, n_parts) &&
+                                         n_strips, n_parts, busy) &&
            residual_rk_strip<NWAVES, KS>(w_b, w_a, s, b0, t0, L, W, afr, tro, seed, V, kh,
-                                         n_strips, n_parts)) {
+                                         n_strips, n_parts, busy)) {
     }
     // both lanes of a pair hold the same keys
     if (active && kh == 0) {
