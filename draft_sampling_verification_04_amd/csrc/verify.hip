@@ -487,33 +487,43 @@ __global__ __launch_bounds__(kCombThreads) void verify_residual_combine(
     const int32_t* __restrict__ accepted, uint64_t seed, int K, int V, int r,
     int32_t* __restrict__ next_token) {
     constexpr int NW = kCombThreads / kWave;
-    __shared__ RowState red[NW];
+    __shared__ RowState red_r[NW], red_f[NW];
     __shared__ float bias_sh[NW][kDraftBlock];
+    __shared__ int sh_blk, sh_residual;
     const int slot = blockIdx.x;
     if (slot >= *ws.count) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // both block states in one pass: per wavefront in registers, then the NW
+    // wavefront states by wavefront 0
     RowState sr = row_empty();
     RowState sf = row_empty();
     for (int s = threadIdx.x; s < n_strips; s += kCombThreads) {
         row_merge(sr, load_partial(ws.res, static_cast<size_t>(slot) * n_strips + s));
         row_merge(sf, load_partial(ws.fall, static_cast<size_t>(slot) * n_strips + s));
     }
-    sr = block_reduce_row<kCombThreads>(sr, red);
+    wave_reduce_row(sr);
+    wave_reduce_row(sf);
+    if (lane == 0) {
+        red_r[wave] = sr;
+        red_f[wave] = sf;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) red[1] = sr;  // block_reduce_row leaves it in thread 0
+    if (wave == 0) {
+        sr = (lane < NW) ? red_r[lane] : row_empty();
+        sf = (lane < NW) ? red_f[lane] : row_empty();
+        wave_reduce_row(sr);
+        wave_reduce_row(sf);
+        if (lane == 0) {
+            sh_residual = sr.pert > -INFINITY;
+            sh_blk = sh_residual ? sr.idx : sf.idx;
+        }
+    }
     __syncthreads();
-    sr = red[1];
-    __syncthreads();
-    sf = block_reduce_row<kCombThreads>(sf, red);
-    __syncthreads();
-    if (threadIdx.x == 0) red[1] = sf;
-    __syncthreads();
-    sf = red[1];
-    const bool residual = sr.pert > -INFINITY;
-    const int blk = residual ? sr.idx : sf.idx;
+    const bool residual = sh_residual != 0;
+    const int blk = sh_blk;
     const int b = ws.list[slot];
     const int js = accepted[b] + 1;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     // a block start in [0, V) (no partial with a key leaves the index at
     // 0x7fffffff: then nothing is read and next_token gets that index)
     const bool blk_ok = blk >= 0 && blk < V;
