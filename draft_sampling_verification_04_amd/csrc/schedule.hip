@@ -15,8 +15,12 @@
 // 64-bit key: high word ~bits(S) (S > 0 is a positive float, so its bit pattern
 // is monotone), low word k * B + b.  Without a curve the D-th smallest key is
 // found by an 8-pass byte-wise radix select and L_b counts keys at or below it.
-// With a curve the candidates are sorted (bitonic, in workspace memory) and
-// the strict-rise test is evaluated at every rank from an fp64 prefix sum.
+// With a curve the candidates are sorted (bitonic) and the strict-rise test is
+// evaluated at every rank from an fp64 prefix sum; the key at the stop rank
+// becomes the threshold.  Up to 16384 candidates are sorted in registers and
+// LDS (compare-exchange partners in the same wavefront swap by register
+// exchange, only strides across wavefronts pass through LDS); more are sorted
+// in workspace memory.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,6 +29,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr uint64_t kNoKey = ~0ull;
+constexpr int kSortLds = 16384;  // largest candidate count sorted in LDS (128 KB of keys)
+constexpr int kKeyRegs = 32;     // keys per thread kept in registers while B * K <= 32768
 
 struct Curve {
     int n;
@@ -87,22 +93,171 @@ __device__ T block_exclusive_scan(T v, T* sh /* [kThreads / kWave] */, T* total)
     return before + incl - v;
 }
 
+// Register exchange of a 64-bit value with lane ^ m (m a power of two < 64).
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x, int m) {
+    const uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
+    uint32_t a, b;
+    switch (m) {
+        case 1: a = xlane<0>(lo); b = xlane<0>(hi); break;
+        case 2: a = xlane<1>(lo); b = xlane<1>(hi); break;
+        case 16: a = xlane<4>(lo); b = xlane<4>(hi); break;
+        case 32: a = xlane<5>(lo); b = xlane<5>(hi); break;
+        default: a = __shfl_xor(lo, m, kWave); b = __shfl_xor(hi, m, kWave); break;
+    }
+    return (static_cast<uint64_t>(b) << 32) | a;
+}
+
+__device__ __forceinline__ uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a < b ? b : a; }
+
+// One bitonic stage of stride S < E inside a thread's E registers.
+template <int E, int S>
+__device__ __forceinline__ void stage_in_thread(uint64_t (&v)[E], int base, int size) {
+    if constexpr (S < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if ((e & S) == 0) {
+                const bool up = ((base + e) & size) == 0;
+                const uint64_t a = v[e], b = v[e | S];
+                v[e] = up ? min64(a, b) : max64(a, b);
+                v[e | S] = up ? max64(a, b) : min64(a, b);
+            }
+        }
+    }
+}
+
+// Ascending bitonic sort of the E * kThreads keys in sh.  Thread t holds
+// positions t E .. t E + E - 1 in registers; the partner of position i at a
+// stage of stride s is i ^ s, in the same thread for s < E, in lane ^ (s / E)
+// of the same wavefront for s < 64 E, otherwise read back through LDS.
+template <int E>
+__device__ void sort_keys_lds(uint64_t* sh) {
+    constexpr int npow = E * kThreads;
+    const int base = threadIdx.x * E;
+    uint64_t v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = sh[base + e];
+    for (int size = 2; size <= npow; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= kWave * E) {
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < E; ++e) sh[base + e] = v[e];
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int i = base + e;
+                    const uint64_t p = sh[i ^ stride];
+                    const bool keep_min = ((i & stride) == 0) == ((i & size) == 0);
+                    v[e] = keep_min ? min64(v[e], p) : max64(v[e], p);
+                }
+            } else if (stride >= E) {
+                const int m = stride / E;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int i = base + e;
+                    const uint64_t p = lane_xor64(v[e], m);
+                    const bool keep_min = ((i & stride) == 0) == ((i & size) == 0);
+                    v[e] = keep_min ? min64(v[e], p) : max64(v[e], p);
+                }
+            } else {
+                switch (stride) {
+                    case 1: stage_in_thread<E, 1>(v, base, size); break;
+                    case 2: stage_in_thread<E, 2>(v, base, size); break;
+                    case 4: stage_in_thread<E, 4>(v, base, size); break;
+                    default: stage_in_thread<E, 8>(v, base, size); break;
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e) sh[base + e] = v[e];
+    __syncthreads();
+}
+
+// Strict-rise test over the n sorted candidates (ascending keys = descending
+// S): the first rank whose item does not raise (B + sum S) / tau(B + taken)
+// stops the walk.  Returns the threshold key (the last key taken, 0 = none).
+__device__ __forceinline__ uint64_t curve_stop(const uint64_t* srt, int n, int B,
+                                               const Curve& curve, double* sh_f64,
+                                               unsigned long long* sh_stop) {
+    const int tid = threadIdx.x;
+    const int chunk = (n + kThreads - 1) / kThreads;
+    const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
+    double local = 0.0;
+    for (int i = lo; i < hi; ++i) local += static_cast<double>(key_survival(srt[i]));
+    const double before = block_exclusive_scan<double>(local, sh_f64, nullptr);
+    if (tid == 0) *sh_stop = static_cast<unsigned long long>(n);
+    __syncthreads();
+    double E = static_cast<double>(B) + before;
+    for (int i = lo; i < hi; ++i) {
+        const double S = static_cast<double>(key_survival(srt[i]));
+        const double N = static_cast<double>(B) + i;
+        const double f_now = E / curve_tau(curve, N);
+        const double f_next = (E + S) / curve_tau(curve, N + 1.0);
+        if (!(f_next > f_now)) {
+            atomicMin(sh_stop, static_cast<unsigned long long>(i));
+            break;
+        }
+        E += S;
+    }
+    __syncthreads();
+    const int stop = static_cast<int>(*sh_stop);
+    return stop > 0 ? srt[stop - 1] : 0;
+}
+
+// Histogram add for one key per lane: the lanes that share the first hitting
+// lane's digit add once (the high digits of ~bits(S) are few, so most lanes
+// of a wavefront share one), the others add one each.
+__device__ __forceinline__ void hist_add(unsigned* hist, bool hit, unsigned dig) {
+    const unsigned long long hits = __ballot(hit);
+    if (hits) {
+        const int leader = __ffsll(static_cast<long long>(hits)) - 1;
+        const unsigned ld = __shfl(dig, leader, kWave);
+        const unsigned long long same = __ballot(hit && dig == ld);
+        if ((threadIdx.x & 63) == leader)
+            atomicAdd(&hist[ld], static_cast<unsigned>(__popcll(same)));
+        else if (hit && dig != ld)
+            atomicAdd(&hist[dig], 1u);
+    }
+}
+
+// Slot of this lane's key in a compacted list (one counter add per wavefront);
+// -1 for a lane that holds no key.
+__device__ __forceinline__ int compact_slot(unsigned* counter, bool take) {
+    const unsigned long long takes = __ballot(take);
+    if (!takes) return -1;
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll(static_cast<long long>(takes)) - 1;
+    unsigned base = 0;
+    if (lane == leader) base = atomicAdd(counter, static_cast<unsigned>(__popcll(takes)));
+    base = __shfl(base, leader, kWave);
+    const unsigned long long below = lane ? (takes & (~0ull >> (64 - lane))) : 0ull;
+    return take ? static_cast<int>(base + __popcll(below)) : -1;
+}
+
 __global__ __launch_bounds__(kThreads) void schedule_kernel(
     const float* __restrict__ conf, int B, int K, long long budget, Curve curve,
     int32_t* __restrict__ lengths, int64_t* __restrict__ row_offsets, float* __restrict__ survival,
     uint64_t* __restrict__ keys, uint64_t* __restrict__ sorted, int sort_cap) {
+    __shared__ uint64_t sh_sort[kSortLds];
     __shared__ unsigned hist[256];
     __shared__ unsigned long long sh_u64[kThreads / kWave];
     __shared__ double sh_f64[kThreads / kWave];
-    __shared__ unsigned sh_sel, sh_want, sh_ncand;
-    __shared__ unsigned long long sh_stop;
+    __shared__ unsigned sh_sel, sh_want, sh_cnt, sh_ncand;
+    __shared__ unsigned long long sh_stop, sh_theta;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const long long n_items = static_cast<long long>(B) * K;
 
-    // 1. survival products and keys
+    // 1. survival products and keys; L_b starts as the count of positive S in
+    // row b (the length when every positive item is taken)
     unsigned long long n_pos_local = 0;
+    int my_len = 0;  // L of request tid (used while B <= kThreads)
     for (int b = tid; b < B; b += kThreads) {
         float S = 1.0f;
+        int pos_b = 0;
         for (int k = 0; k < K; ++k) {
             const size_t o = static_cast<size_t>(b) * K + k;
             S = S * conf[o];
@@ -111,13 +266,35 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
             keys[o] = pos ? (static_cast<uint64_t>(0xFFFFFFFFu - __float_as_uint(S)) << 32) |
                                 static_cast<uint32_t>(k * B + b)
                           : kNoKey;
-            n_pos_local += pos;
+            pos_b += pos;
         }
-        lengths[b] = 0;
+        n_pos_local += pos_b;
+        lengths[b] = pos_b;
+        if (b == tid) my_len = pos_b;
     }
     const unsigned long long n_pos = block_sum<unsigned long long>(n_pos_local, sh_u64);
     const long long D = budget - B > 0 ? budget - B : 0;
     const long long dsel = D < static_cast<long long>(n_pos) ? D : static_cast<long long>(n_pos);
+    // every positive item is taken: L_b is already set
+    const bool take_all = dsel == static_cast<long long>(n_pos) && (curve.n <= 0 || dsel == 0);
+
+    // while a threshold search or a sort follows, up to 32768 keys keep their
+    // high word ~bits(S) in registers (key i in slot i / kThreads of thread
+    // i % kThreads; 0xFFFFFFFF = no key); the low word k * B + b follows from
+    // i = b * K + k where it is needed
+    const bool in_regs =
+        !take_all && dsel > 0 && n_items <= static_cast<long long>(kThreads) * kKeyRegs;
+    uint32_t kh[kKeyRegs];
+#pragma unroll
+    for (int j = 0; j < kKeyRegs; ++j) {
+        const long long i = tid + static_cast<long long>(j) * kThreads;
+        kh[j] = (in_regs && i < n_items) ? static_cast<uint32_t>(keys[i] >> 32) : 0xFFFFFFFFu;
+    }
+    auto full_key = [&](int j) -> uint64_t {  // key of register slot j (which holds one)
+        const unsigned i = static_cast<unsigned>(tid + j * kThreads);
+        const unsigned b = i / static_cast<unsigned>(K), k = i - b * static_cast<unsigned>(K);
+        return (static_cast<uint64_t>(kh[j]) << 32) | (k * static_cast<unsigned>(B) + b);
+    };
 
     // 2. threshold key: every candidate has key <= theta
     uint64_t theta;
@@ -130,37 +307,179 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
         unsigned want = static_cast<unsigned>(dsel - 1);  // 0-based rank
         for (int d = 7; d >= 0; --d) {
             for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
+            // the register words are marked as rewritten in every pass, so
+            // what is derived from them (per-slot masks and addresses, 32 of
+            // each) is not hoisted out of the loop into spilled registers
+            int tid_o = tid;
+            asm volatile("" : "+v"(tid_o));
+#pragma unroll
+            for (int j = 0; j < kKeyRegs; ++j) asm volatile("" : "+v"(kh[j]));
             __syncthreads();
-            for (long long i = tid; i < n_items; i += kThreads) {
-                const uint64_t key = keys[i];
-                if (key != kNoKey && (key & mask) == prefix)
-                    atomicAdd(&hist[(key >> (8 * d)) & 255u], 1u);
+            if (in_regs) {
+#pragma unroll
+                for (int j = 0; j < kKeyRegs; ++j) {
+                    if (static_cast<long long>(j) * kThreads >= n_items) continue;
+                    const bool has = kh[j] != 0xFFFFFFFFu;
+                    // bytes 4..7 are the high word; bytes 0..3 (reached only
+                    // when survival values tie) read the whole key again
+                    const uint64_t key =
+                        d >= 4 ? static_cast<uint64_t>(kh[j]) << 32
+                               : (has ? keys[tid_o + static_cast<long long>(j) * kThreads] : kNoKey);
+                    hist_add(hist, has && (key & mask) == prefix,
+                             static_cast<unsigned>(key >> (8 * d)) & 255u);
+                }
+            } else {
+                for (long long i0 = 0; i0 < n_items; i0 += kThreads) {
+                    const long long i = i0 + tid;
+                    const uint64_t key = i < n_items ? keys[i] : kNoKey;
+                    hist_add(hist, key != kNoKey && (key & mask) == prefix,
+                             static_cast<unsigned>(key >> (8 * d)) & 255u);
+                }
             }
             __syncthreads();
-            if (tid == 0) {
-                unsigned c = 0;
-                unsigned sel = 255;
-                for (unsigned t = 0; t < 256; ++t) {
-                    if (c + hist[t] > want) {
-                        sel = t;
-                        break;
-                    }
-                    c += hist[t];
+            // the bin that holds rank `want`: wavefront 0 scans 4 bins per lane
+            if (tid < kWave) {
+                const unsigned h0 = hist[4 * lane], h1 = hist[4 * lane + 1];
+                const unsigned h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+                const unsigned own = h0 + h1 + h2 + h3;
+                unsigned incl = own;
+                for (int dd = 1; dd < kWave; dd <<= 1) {
+                    const unsigned o = __shfl_up(incl, dd, kWave);
+                    if (lane >= dd) incl += o;
                 }
-                sh_sel = sel;
-                sh_want = want - c;
+                const unsigned excl = incl - own;
+                if (excl <= want && want < incl) {
+                    unsigned c = excl, sel = 4 * lane;
+                    if (c + h0 <= want) {
+                        c += h0;
+                        ++sel;
+                        if (c + h1 <= want) {
+                            c += h1;
+                            ++sel;
+                            if (c + h2 <= want) {
+                                c += h2;
+                                ++sel;
+                            }
+                        }
+                    }
+                    sh_sel = sel;
+                    sh_want = want - c;
+                    sh_cnt = hist[sel];
+                } else if (lane == kWave - 1 && incl <= want) {
+                    sh_sel = 255;  // unreachable: rank `want` lies among the prefix's keys
+                    sh_want = want - incl;
+                    sh_cnt = 0;
+                }
             }
             __syncthreads();
             prefix |= static_cast<uint64_t>(sh_sel) << (8 * d);
             mask |= 255ull << (8 * d);
             want = sh_want;
+            const unsigned cnt = sh_cnt;
             __syncthreads();
+            if (cnt == 1 && d > 0) {
+                // the selected bin holds one key: it is the threshold
+                if (in_regs) {
+                    const uint64_t hmask = mask & 0xFFFFFFFF00000000ull;
+#pragma unroll
+                    for (int j = 0; j < kKeyRegs; ++j) {
+                        if (kh[j] != 0xFFFFFFFFu &&
+                            ((static_cast<uint64_t>(kh[j]) << 32) & hmask) == (prefix & hmask)) {
+                            const uint64_t key = keys[tid_o + static_cast<long long>(j) * kThreads];
+                            if ((key & mask) == prefix) sh_theta = key;
+                        }
+                    }
+                } else {
+                    for (long long i = tid; i < n_items; i += kThreads) {
+                        const uint64_t key = keys[i];
+                        if (key != kNoKey && (key & mask) == prefix) sh_theta = key;
+                    }
+                }
+                __syncthreads();
+                prefix = sh_theta;
+                break;
+            }
         }
         theta = prefix;
     }
 
-    if (curve.n <= 0) {
-        // 3a. L_b = number of candidate keys of request b
+    if (curve.n > 0 && dsel > 0) {
+        // 3. sort the candidates; the strict-rise test sets the threshold
+        int npow = kThreads;
+        while (npow < dsel) npow <<= 1;
+        if (tid == 0) sh_ncand = 0;
+        __syncthreads();
+        if (npow <= kSortLds) {
+            if (in_regs) {
+                const uint32_t th = static_cast<uint32_t>(theta >> 32);
+#pragma unroll
+                for (int j = 0; j < kKeyRegs; ++j) {
+                    if (static_cast<long long>(j) * kThreads < n_items) {
+                        const uint32_t h = kh[j];
+                        bool take = h != 0xFFFFFFFFu && h <= th;
+                        uint64_t key = 0;
+                        if (take) {
+                            key = full_key(j);
+                            take = key <= theta;
+                        }
+                        const int slot = compact_slot(&sh_ncand, take);
+                        if (slot >= 0 && slot < kSortLds) sh_sort[slot] = key;
+                    }
+                }
+            } else {
+                for (long long i0 = 0; i0 < n_items; i0 += kThreads) {
+                    const long long i = i0 + tid;
+                    const uint64_t key = i < n_items ? keys[i] : kNoKey;
+                    const int slot = compact_slot(&sh_ncand, key != kNoKey && key <= theta);
+                    if (slot >= 0 && slot < kSortLds) sh_sort[slot] = key;
+                }
+            }
+            __syncthreads();
+            const int n = static_cast<int>(sh_ncand);  // == dsel
+            for (int i = n + tid; i < npow; i += kThreads) sh_sort[i] = kNoKey;
+            __syncthreads();
+            switch (npow / kThreads) {
+                case 1: sort_keys_lds<1>(sh_sort); break;
+                case 2: sort_keys_lds<2>(sh_sort); break;
+                case 4: sort_keys_lds<4>(sh_sort); break;
+                case 8: sort_keys_lds<8>(sh_sort); break;
+                default: sort_keys_lds<16>(sh_sort); break;
+            }
+            theta = curve_stop(sh_sort, n, B, curve, sh_f64, &sh_stop);
+        } else {
+            for (long long i0 = 0; i0 < n_items; i0 += kThreads) {
+                const long long i = i0 + tid;
+                const uint64_t key = i < n_items ? keys[i] : kNoKey;
+                const int slot = compact_slot(&sh_ncand, key != kNoKey && key <= theta);
+                if (slot >= 0) sorted[slot] = key;
+            }
+            __syncthreads();
+            const int n = static_cast<int>(sh_ncand);  // == dsel
+            for (int i = n + tid; i < npow && i < sort_cap; i += kThreads) sorted[i] = kNoKey;
+            __syncthreads();
+            for (int size = 2; size <= npow; size <<= 1) {
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    for (int i = tid; i < npow; i += kThreads) {
+                        const int partner = i ^ stride;
+                        if (partner > i) {
+                            const bool up = (i & size) == 0;
+                            const uint64_t x = sorted[i], y = sorted[partner];
+                            if ((x > y) == up) {
+                                sorted[i] = y;
+                                sorted[partner] = x;
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            theta = curve_stop(sorted, n, B, curve, sh_f64, &sh_stop);
+        }
+    }
+
+    // 4. otherwise L_b = number of candidate keys of request b (the taken
+    // items: keys at or below the threshold)
+    if (!take_all) {
         for (int b = tid; b < B; b += kThreads) {
             int L = 0;
             for (int k = 0; k < K; ++k) {
@@ -168,80 +487,35 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
                 L += (key != kNoKey && key <= theta);
             }
             lengths[b] = L;
-        }
-    } else if (dsel > 0) {
-        // 3b. sort the candidates, then the strict-rise test at every rank
-        if (tid == 0) sh_ncand = 0;
-        __syncthreads();
-        for (long long i = tid; i < n_items; i += kThreads) {
-            const uint64_t key = keys[i];
-            if (key != kNoKey && key <= theta) sorted[atomicAdd(&sh_ncand, 1u)] = key;
-        }
-        __syncthreads();
-        const int n = static_cast<int>(sh_ncand);  // == dsel
-        int npow = 1;
-        while (npow < n) npow <<= 1;
-        for (int i = n + tid; i < npow && i < sort_cap; i += kThreads) sorted[i] = kNoKey;
-        __syncthreads();
-        for (int size = 2; size <= npow; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < npow; i += kThreads) {
-                    const int partner = i ^ stride;
-                    if (partner > i) {
-                        const bool up = (i & size) == 0;
-                        const uint64_t x = sorted[i], y = sorted[partner];
-                        if ((x > y) == up) {
-                            sorted[i] = y;
-                            sorted[partner] = x;
-                        }
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        // prefix sums of S in rank order, chunked per thread
-        const int chunk = (n + kThreads - 1) / kThreads;
-        const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
-        double local = 0.0;
-        for (int i = lo; i < hi; ++i) local += static_cast<double>(key_survival(sorted[i]));
-        const double before = block_exclusive_scan<double>(local, sh_f64, nullptr);
-        if (tid == 0) sh_stop = static_cast<unsigned long long>(n);
-        __syncthreads();
-        double E = static_cast<double>(B) + before;
-        for (int i = lo; i < hi; ++i) {
-            const double S = static_cast<double>(key_survival(sorted[i]));
-            const double N = static_cast<double>(B) + i;
-            const double f_now = E / curve_tau(curve, N);
-            const double f_next = (E + S) / curve_tau(curve, N + 1.0);
-            if (!(f_next > f_now)) {
-                atomicMin(&sh_stop, static_cast<unsigned long long>(i));
-                break;
-            }
-            E += S;
-        }
-        __syncthreads();
-        const int stop = static_cast<int>(sh_stop);
-        for (int i = tid; i < stop; i += kThreads) {
-            const uint32_t low = static_cast<uint32_t>(sorted[i]);
-            atomicAdd(&lengths[low % static_cast<uint32_t>(B)], 1);
+            if (b == tid) my_len = L;
         }
     }
     __syncthreads();
 
-    // 4. row_offsets = exclusive scan of L_b + 1
-    const int chunk = (B + kThreads - 1) / kThreads;
-    const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
-    long long local = 0;
-    for (int b = lo; b < hi; ++b) local += lengths[b] + 1;
-    long long total = 0;
-    const long long before =
-        block_exclusive_scan<long long>(local, reinterpret_cast<long long*>(sh_u64), &total);
-    long long run = before;
-    for (int b = lo; b < hi; ++b) {
-        row_offsets[b] = run;
-        run += lengths[b] + 1;
+    // 5. row_offsets = exclusive scan of L_b + 1 (thread tid holds L of request
+    // tid while B <= kThreads; larger batches read the lengths back in chunks)
+    if (B <= kThreads) {
+        long long total = 0;
+        const long long v = tid < B ? my_len + 1 : 0;
+        const long long before =
+            block_exclusive_scan<long long>(v, reinterpret_cast<long long*>(sh_u64), &total);
+        if (tid < B) row_offsets[tid] = before;
+        if (tid == 0) row_offsets[B] = total;
+    } else {
+        const int chunk = (B + kThreads - 1) / kThreads;
+        const int lo = min(B, tid * chunk), hi = min(B, lo + chunk);
+        long long local = 0;
+        for (int b = lo; b < hi; ++b) local += lengths[b] + 1;
+        long long total = 0;
+        const long long before =
+            block_exclusive_scan<long long>(local, reinterpret_cast<long long*>(sh_u64), &total);
+        long long run = before;
+        for (int b = lo; b < hi; ++b) {
+            row_offsets[b] = run;
+            run += lengths[b] + 1;
+        }
+        if (tid == 0) row_offsets[B] = total;
     }
-    if (tid == 0) row_offsets[B] = total;
 }
 
 }  // namespace
