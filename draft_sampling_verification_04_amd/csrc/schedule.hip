@@ -17,10 +17,12 @@
 // found by an 8-pass byte-wise radix select and L_b counts keys at or below it.
 // With a curve the candidates are sorted (bitonic) and the strict-rise test is
 // evaluated at every rank from an fp64 prefix sum; the key at the stop rank
-// becomes the threshold.  Up to 16384 candidates are sorted in registers and
-// LDS (compare-exchange partners in the same wavefront swap by register
-// exchange, only strides across wavefronts pass through LDS); more are sorted
-// in workspace memory.
+// becomes the threshold.  Up to 16384 candidates (of at most 32768 items) are
+// sorted by their high words only, in registers and LDS (compare-exchange
+// partners in the same wavefront swap by register exchange, only strides
+// across wavefronts pass through LDS): the walk depends only on the S
+// sequence, and the exact threshold key is then selected among the keys that
+// share the stop item's S.  Larger inputs sort whole keys in workspace memory.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,7 +31,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr uint64_t kNoKey = ~0ull;
-constexpr int kSortLds = 16384;  // largest candidate count sorted in LDS (128 KB of keys)
+constexpr int kSortWords = 32768;  // LDS sort buffer: 128 KB (staging, high words)
+constexpr int kSortMax = 16384;    // most candidates sorted in LDS (16 per thread)
 constexpr int kKeyRegs = 32;     // keys per thread kept in registers while B * K <= 32768
 
 struct Curve {
@@ -93,48 +96,42 @@ __device__ T block_exclusive_scan(T v, T* sh /* [kThreads / kWave] */, T* total)
     return before + incl - v;
 }
 
-// Register exchange of a 64-bit value with lane ^ m (m a power of two < 64).
-__device__ __forceinline__ uint64_t lane_xor64(uint64_t x, int m) {
-    const uint32_t lo = static_cast<uint32_t>(x), hi = static_cast<uint32_t>(x >> 32);
-    uint32_t a, b;
+// Register exchange with lane ^ m (m a power of two < 64).
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int m) {
     switch (m) {
-        case 1: a = xlane<0>(lo); b = xlane<0>(hi); break;
-        case 2: a = xlane<1>(lo); b = xlane<1>(hi); break;
-        case 16: a = xlane<4>(lo); b = xlane<4>(hi); break;
-        case 32: a = xlane<5>(lo); b = xlane<5>(hi); break;
-        default: a = __shfl_xor(lo, m, kWave); b = __shfl_xor(hi, m, kWave); break;
+        case 1: return xlane<0>(x);
+        case 2: return xlane<1>(x);
+        case 16: return xlane<4>(x);
+        case 32: return xlane<5>(x);
+        default: return __shfl_xor(x, m, kWave);
     }
-    return (static_cast<uint64_t>(b) << 32) | a;
 }
-
-__device__ __forceinline__ uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a < b ? b : a; }
 
 // One bitonic stage of stride S < E inside a thread's E registers.
 template <int E, int S>
-__device__ __forceinline__ void stage_in_thread(uint64_t (&v)[E], int base, int size) {
+__device__ __forceinline__ void stage_in_thread(uint32_t (&v)[E], int base, int size) {
     if constexpr (S < E) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             if ((e & S) == 0) {
                 const bool up = ((base + e) & size) == 0;
-                const uint64_t a = v[e], b = v[e | S];
-                v[e] = up ? min64(a, b) : max64(a, b);
-                v[e | S] = up ? max64(a, b) : min64(a, b);
+                const uint32_t a = v[e], b = v[e | S];
+                v[e] = up ? min(a, b) : max(a, b);
+                v[e | S] = up ? max(a, b) : min(a, b);
             }
         }
     }
 }
 
-// Ascending bitonic sort of the E * kThreads keys in sh.  Thread t holds
+// Ascending bitonic sort of the E * kThreads words in sh.  Thread t holds
 // positions t E .. t E + E - 1 in registers; the partner of position i at a
 // stage of stride s is i ^ s, in the same thread for s < E, in lane ^ (s / E)
 // of the same wavefront for s < 64 E, otherwise read back through LDS.
 template <int E>
-__device__ void sort_keys_lds(uint64_t* sh) {
+__device__ void sort_words_lds(uint32_t* sh) {
     constexpr int npow = E * kThreads;
     const int base = threadIdx.x * E;
-    uint64_t v[E];
+    uint32_t v[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] = sh[base + e];
     for (int size = 2; size <= npow; size <<= 1) {
@@ -147,25 +144,26 @@ __device__ void sort_keys_lds(uint64_t* sh) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const int i = base + e;
-                    const uint64_t p = sh[i ^ stride];
+                    const uint32_t p = sh[i ^ stride];
                     const bool keep_min = ((i & stride) == 0) == ((i & size) == 0);
-                    v[e] = keep_min ? min64(v[e], p) : max64(v[e], p);
+                    v[e] = keep_min ? min(v[e], p) : max(v[e], p);
                 }
             } else if (stride >= E) {
                 const int m = stride / E;
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const int i = base + e;
-                    const uint64_t p = lane_xor64(v[e], m);
+                    const uint32_t p = lane_xor(v[e], m);
                     const bool keep_min = ((i & stride) == 0) == ((i & size) == 0);
-                    v[e] = keep_min ? min64(v[e], p) : max64(v[e], p);
+                    v[e] = keep_min ? min(v[e], p) : max(v[e], p);
                 }
             } else {
                 switch (stride) {
                     case 1: stage_in_thread<E, 1>(v, base, size); break;
                     case 2: stage_in_thread<E, 2>(v, base, size); break;
                     case 4: stage_in_thread<E, 4>(v, base, size); break;
-                    default: stage_in_thread<E, 8>(v, base, size); break;
+                    case 8: stage_in_thread<E, 8>(v, base, size); break;
+                    default: stage_in_thread<E, 16>(v, base, size); break;
                 }
             }
         }
@@ -176,23 +174,28 @@ __device__ void sort_keys_lds(uint64_t* sh) {
     __syncthreads();
 }
 
-// Strict-rise test over the n sorted candidates (ascending keys = descending
-// S): the first rank whose item does not raise (B + sum S) / tau(B + taken)
-// stops the walk.  Returns the threshold key (the last key taken, 0 = none).
-__device__ __forceinline__ uint64_t curve_stop(const uint64_t* srt, int n, int B,
-                                               const Curve& curve, double* sh_f64,
-                                               unsigned long long* sh_stop) {
+__device__ __forceinline__ float survival_of(uint64_t key) { return key_survival(key); }
+__device__ __forceinline__ float survival_of(uint32_t word) {
+    return __uint_as_float(0xFFFFFFFFu - word);
+}
+
+// Strict-rise test over the n sorted candidates (ascending keys or high words
+// = descending S): the first rank whose item does not raise
+// (B + sum S) / tau(B + taken) stops the walk.  Returns that rank (n if none).
+template <typename T>
+__device__ __forceinline__ int curve_stop(const T* srt, int n, int B, const Curve& curve,
+                                          double* sh_f64, unsigned long long* sh_stop) {
     const int tid = threadIdx.x;
     const int chunk = (n + kThreads - 1) / kThreads;
     const int lo = min(n, tid * chunk), hi = min(n, lo + chunk);
     double local = 0.0;
-    for (int i = lo; i < hi; ++i) local += static_cast<double>(key_survival(srt[i]));
+    for (int i = lo; i < hi; ++i) local += static_cast<double>(survival_of(srt[i]));
     const double before = block_exclusive_scan<double>(local, sh_f64, nullptr);
     if (tid == 0) *sh_stop = static_cast<unsigned long long>(n);
     __syncthreads();
     double E = static_cast<double>(B) + before;
     for (int i = lo; i < hi; ++i) {
-        const double S = static_cast<double>(key_survival(srt[i]));
+        const double S = static_cast<double>(survival_of(srt[i]));
         const double N = static_cast<double>(B) + i;
         const double f_now = E / curve_tau(curve, N);
         const double f_next = (E + S) / curve_tau(curve, N + 1.0);
@@ -204,7 +207,8 @@ __device__ __forceinline__ uint64_t curve_stop(const uint64_t* srt, int n, int B
     }
     __syncthreads();
     const int stop = static_cast<int>(*sh_stop);
-    return stop > 0 ? srt[stop - 1] : 0;
+    __syncthreads();
+    return stop;
 }
 
 // Histogram add for one key per lane: the lanes that share the first hitting
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
     const float* __restrict__ conf, int B, int K, long long budget, Curve curve,
     int32_t* __restrict__ lengths, int64_t* __restrict__ row_offsets, float* __restrict__ survival,
     uint64_t* __restrict__ keys, uint64_t* __restrict__ sorted, int sort_cap) {
-    __shared__ uint64_t sh_sort[kSortLds];
+    __shared__ uint64_t sh_sort[kSortWords / 2];
     __shared__ unsigned hist[256];
     __shared__ unsigned long long sh_u64[kThreads / kWave];
     __shared__ double sh_f64[kThreads / kWave];
@@ -252,25 +256,79 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
     const long long n_items = static_cast<long long>(B) * K;
 
     // 1. survival products and keys; L_b starts as the count of positive S in
-    // row b (the length when every positive item is taken)
+    // row b (the length when every positive item is taken).  While B * K
+    // floats fit in the sort buffer, conf is staged there so that the global
+    // loads and stores are coalesced and only the sequential products walk the
+    // rows (row b is stored rotated by b mod K, so that the lanes of a
+    // wavefront, one row each, spread over the banks); larger batches walk the
+    // rows in global memory.
     unsigned long long n_pos_local = 0;
     int my_len = 0;  // L of request tid (used while B <= kThreads)
-    for (int b = tid; b < B; b += kThreads) {
-        float S = 1.0f;
-        int pos_b = 0;
-        for (int k = 0; k < K; ++k) {
-            const size_t o = static_cast<size_t>(b) * K + k;
-            S = S * conf[o];
-            if (survival) survival[o] = S;
-            const bool pos = S > 0.0f;
-            keys[o] = pos ? (static_cast<uint64_t>(0xFFFFFFFFu - __float_as_uint(S)) << 32) |
-                                static_cast<uint32_t>(k * B + b)
-                          : kNoKey;
-            pos_b += pos;
+    uint32_t kh[kKeyRegs];  // see below
+#pragma unroll
+    for (int j = 0; j < kKeyRegs; ++j) kh[j] = 0xFFFFFFFFu;
+    const unsigned uK = static_cast<unsigned>(K > 0 ? K : 1);
+    const bool staged = n_items <= static_cast<long long>(kThreads) * kKeyRegs;
+    // stage slot of item (b, k)
+    auto slot_of = [&](unsigned b, unsigned k) -> unsigned {
+        unsigned c = k + (b - (b / uK) * uK);
+        if (c >= uK) c -= uK;
+        return b * uK + c;
+    };
+    if (staged) {
+        float* stage = reinterpret_cast<float*>(sh_sort);
+        for (long long o = tid; o < n_items; o += kThreads) {
+            const unsigned b = static_cast<unsigned>(o) / uK, k = static_cast<unsigned>(o) - b * uK;
+            stage[slot_of(b, k)] = conf[o];
         }
-        n_pos_local += pos_b;
-        lengths[b] = pos_b;
-        if (b == tid) my_len = pos_b;
+        __syncthreads();
+        for (int b = tid; b < B; b += kThreads) {
+            float S = 1.0f;
+            int pos_b = 0;
+            const unsigned base = static_cast<unsigned>(b) * uK;
+            unsigned c = static_cast<unsigned>(b) - (static_cast<unsigned>(b) / uK) * uK;
+            for (int k = 0; k < K; ++k) {
+                S = S * stage[base + c];
+                stage[base + c] = S;
+                pos_b += S > 0.0f;
+                if (++c == uK) c = 0;
+            }
+            n_pos_local += pos_b;
+            lengths[b] = pos_b;
+            if (b == tid) my_len = pos_b;
+        }
+        __syncthreads();
+        // B * K <= 32768: register slot j of thread tid is item tid + j * kThreads
+#pragma unroll
+        for (int j = 0; j < kKeyRegs; ++j) {
+            const unsigned o = static_cast<unsigned>(tid + j * kThreads);
+            if (static_cast<long long>(j) * kThreads < n_items && o < n_items) {
+                const unsigned b = o / uK, k = o - b * uK;
+                const float S = stage[slot_of(b, k)];
+                if (survival) survival[o] = S;
+                const uint32_t h = S > 0.0f ? 0xFFFFFFFFu - __float_as_uint(S) : 0xFFFFFFFFu;
+                keys[o] = h != 0xFFFFFFFFu ? (static_cast<uint64_t>(h) << 32) | (k * B + b) : kNoKey;
+                kh[j] = h;
+            }
+        }
+    } else {
+        for (int b = tid; b < B; b += kThreads) {
+            float S = 1.0f;
+            int pos_b = 0;
+            for (int k = 0; k < K; ++k) {
+                const size_t o = static_cast<size_t>(b) * K + k;
+                S = S * conf[o];
+                if (survival) survival[o] = S;
+                const bool pos = S > 0.0f;
+                keys[o] = pos ? (static_cast<uint64_t>(0xFFFFFFFFu - __float_as_uint(S)) << 32) |
+                                    static_cast<uint32_t>(k * B + b)
+                              : kNoKey;
+                pos_b += pos;
+            }
+            n_pos_local += pos_b;
+            lengths[b] = pos_b;
+            if (b == tid) my_len = pos_b;
+        }
     }
     const unsigned long long n_pos = block_sum<unsigned long long>(n_pos_local, sh_u64);
     const long long D = budget - B > 0 ? budget - B : 0;
@@ -280,15 +338,17 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
 
     // while a threshold search or a sort follows, up to 32768 keys keep their
     // high word ~bits(S) in registers (key i in slot i / kThreads of thread
-    // i % kThreads; 0xFFFFFFFF = no key); the low word k * B + b follows from
-    // i = b * K + k where it is needed
+    // i % kThreads; 0xFFFFFFFF = no key), filled above when staged and read
+    // back here otherwise; the low word k * B + b follows from i = b * K + k
+    // where it is needed
     const bool in_regs =
         !take_all && dsel > 0 && n_items <= static_cast<long long>(kThreads) * kKeyRegs;
-    uint32_t kh[kKeyRegs];
+    if (in_regs && !staged) {
 #pragma unroll
-    for (int j = 0; j < kKeyRegs; ++j) {
-        const long long i = tid + static_cast<long long>(j) * kThreads;
-        kh[j] = (in_regs && i < n_items) ? static_cast<uint32_t>(keys[i] >> 32) : 0xFFFFFFFFu;
+        for (int j = 0; j < kKeyRegs; ++j) {
+            const long long i = tid + static_cast<long long>(j) * kThreads;
+            kh[j] = i < n_items ? static_cast<uint32_t>(keys[i] >> 32) : 0xFFFFFFFFu;
+        }
     }
     auto full_key = [&](int j) -> uint64_t {  // key of register slot j (which holds one)
         const unsigned i = static_cast<unsigned>(tid + j * kThreads);
@@ -296,16 +356,14 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
         return (static_cast<uint64_t>(kh[j]) << 32) | (k * static_cast<unsigned>(B) + b);
     };
 
-    // 2. threshold key: every candidate has key <= theta
-    uint64_t theta;
-    if (dsel == 0) {
-        theta = 0;  // keys of positive S are > 0: nothing is taken
-    } else if (dsel == static_cast<long long>(n_pos)) {
-        theta = kNoKey - 1;
-    } else {
-        uint64_t prefix = 0, mask = 0;
-        unsigned want = static_cast<unsigned>(dsel - 1);  // 0-based rank
-        for (int d = 7; d >= 0; --d) {
+    // Key of rank `want` (0-based) among the keys with (key & mask) == prefix
+    // and key <= limit, by byte-wise radix passes from byte dtop down.  The
+    // limit is tested only in passes below byte 4, so a caller with a limit
+    // short of kNoKey - 1 starts at byte 3 (its prefix fixes the high word).
+    // regs: read the high words from registers (else every key from memory).
+    auto select_key = [&](uint64_t prefix, uint64_t mask, unsigned want, int dtop,
+                          uint64_t limit, bool regs) -> uint64_t {
+        for (int d = dtop; d >= 0; --d) {
             for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
             // the register words are marked as rewritten in every pass, so
             // what is derived from them (per-slot masks and addresses, 32 of
@@ -315,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
 #pragma unroll
             for (int j = 0; j < kKeyRegs; ++j) asm volatile("" : "+v"(kh[j]));
             __syncthreads();
-            if (in_regs) {
+            if (regs) {
 #pragma unroll
                 for (int j = 0; j < kKeyRegs; ++j) {
                     if (static_cast<long long>(j) * kThreads >= n_items) continue;
@@ -325,14 +383,14 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
                     const uint64_t key =
                         d >= 4 ? static_cast<uint64_t>(kh[j]) << 32
                                : (has ? keys[tid_o + static_cast<long long>(j) * kThreads] : kNoKey);
-                    hist_add(hist, has && (key & mask) == prefix,
+                    hist_add(hist, has && (key & mask) == prefix && (d >= 4 || key <= limit),
                              static_cast<unsigned>(key >> (8 * d)) & 255u);
                 }
             } else {
                 for (long long i0 = 0; i0 < n_items; i0 += kThreads) {
                     const long long i = i0 + tid;
                     const uint64_t key = i < n_items ? keys[i] : kNoKey;
-                    hist_add(hist, key != kNoKey && (key & mask) == prefix,
+                    hist_add(hist, key != kNoKey && (key & mask) == prefix && key <= limit,
                              static_cast<unsigned>(key >> (8 * d)) & 255u);
                 }
             }
@@ -378,29 +436,40 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
             const unsigned cnt = sh_cnt;
             __syncthreads();
             if (cnt == 1 && d > 0) {
-                // the selected bin holds one key: it is the threshold
-                if (in_regs) {
+                // the selected bin holds one key: it is the one
+                if (regs) {
                     const uint64_t hmask = mask & 0xFFFFFFFF00000000ull;
 #pragma unroll
                     for (int j = 0; j < kKeyRegs; ++j) {
                         if (kh[j] != 0xFFFFFFFFu &&
                             ((static_cast<uint64_t>(kh[j]) << 32) & hmask) == (prefix & hmask)) {
                             const uint64_t key = keys[tid_o + static_cast<long long>(j) * kThreads];
-                            if ((key & mask) == prefix) sh_theta = key;
+                            if ((key & mask) == prefix && key <= limit) sh_theta = key;
                         }
                     }
                 } else {
                     for (long long i = tid; i < n_items; i += kThreads) {
                         const uint64_t key = keys[i];
-                        if (key != kNoKey && (key & mask) == prefix) sh_theta = key;
+                        if (key != kNoKey && (key & mask) == prefix && key <= limit) sh_theta = key;
                     }
                 }
                 __syncthreads();
-                prefix = sh_theta;
-                break;
+                const uint64_t found = sh_theta;
+                __syncthreads();
+                return found;
             }
         }
-        theta = prefix;
+        return prefix;
+    };
+
+    // 2. threshold key: every candidate has key <= theta
+    uint64_t theta;
+    if (dsel == 0) {
+        theta = 0;  // keys of positive S are > 0: nothing is taken
+    } else if (dsel == static_cast<long long>(n_pos)) {
+        theta = kNoKey - 1;
+    } else {
+        theta = select_key(0, 0, static_cast<unsigned>(dsel - 1), 7, kNoKey - 1, in_regs);
     }
 
     if (curve.n > 0 && dsel > 0) {
@@ -409,43 +478,63 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
         while (npow < dsel) npow <<= 1;
         if (tid == 0) sh_ncand = 0;
         __syncthreads();
-        if (npow <= kSortLds) {
-            if (in_regs) {
-                const uint32_t th = static_cast<uint32_t>(theta >> 32);
+        if (in_regs && npow <= kSortMax) {
+            // B * K <= 32768 and at most 16384 candidates: their high words
+            // ~bits(S) are sorted in LDS.  The walk needs only the S sequence, which equal
+            // S values leave unchanged; the exact threshold key follows from
+            // the stop rank.
+            uint32_t* sh_w = reinterpret_cast<uint32_t*>(sh_sort);
+            const uint32_t th = static_cast<uint32_t>(theta >> 32);
 #pragma unroll
-                for (int j = 0; j < kKeyRegs; ++j) {
-                    if (static_cast<long long>(j) * kThreads < n_items) {
-                        const uint32_t h = kh[j];
-                        bool take = h != 0xFFFFFFFFu && h <= th;
-                        uint64_t key = 0;
-                        if (take) {
-                            key = full_key(j);
-                            take = key <= theta;
-                        }
-                        const int slot = compact_slot(&sh_ncand, take);
-                        if (slot >= 0 && slot < kSortLds) sh_sort[slot] = key;
-                    }
-                }
-            } else {
-                for (long long i0 = 0; i0 < n_items; i0 += kThreads) {
-                    const long long i = i0 + tid;
-                    const uint64_t key = i < n_items ? keys[i] : kNoKey;
-                    const int slot = compact_slot(&sh_ncand, key != kNoKey && key <= theta);
-                    if (slot >= 0 && slot < kSortLds) sh_sort[slot] = key;
+            for (int j = 0; j < kKeyRegs; ++j) {
+                if (static_cast<long long>(j) * kThreads < n_items) {
+                    const uint32_t h = kh[j];
+                    bool take = h != 0xFFFFFFFFu && h <= th;
+                    if (take && h == th) take = full_key(j) <= theta;
+                    const int slot = compact_slot(&sh_ncand, take);
+                    if (slot >= 0 && slot < kSortWords) sh_w[slot] = h;
                 }
             }
             __syncthreads();
             const int n = static_cast<int>(sh_ncand);  // == dsel
-            for (int i = n + tid; i < npow; i += kThreads) sh_sort[i] = kNoKey;
+            for (int i = n + tid; i < npow; i += kThreads) sh_w[i] = 0xFFFFFFFFu;
             __syncthreads();
             switch (npow / kThreads) {
-                case 1: sort_keys_lds<1>(sh_sort); break;
-                case 2: sort_keys_lds<2>(sh_sort); break;
-                case 4: sort_keys_lds<4>(sh_sort); break;
-                case 8: sort_keys_lds<8>(sh_sort); break;
-                default: sort_keys_lds<16>(sh_sort); break;
+                case 1: sort_words_lds<1>(sh_w); break;
+                case 2: sort_words_lds<2>(sh_w); break;
+                case 4: sort_words_lds<4>(sh_w); break;
+                case 8: sort_words_lds<8>(sh_w); break;
+                default: sort_words_lds<16>(sh_w); break;
             }
-            theta = curve_stop(sh_sort, n, B, curve, sh_f64, &sh_stop);
+            const int stop = curve_stop(sh_w, n, B, curve, sh_f64, &sh_stop);
+            if (stop == 0) {
+                theta = 0;
+            } else {
+                // the stop-th key: the candidates with a smaller high word, then
+                // rank `r` among those that share the stop item's high word
+                const uint32_t hs = sh_w[stop - 1];
+                int lo = 0, hi = stop - 1;  // first index holding hs
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (sh_w[mid] < hs) lo = mid + 1; else hi = mid;
+                }
+                const bool unique = lo == stop - 1 && (stop == n || sh_w[stop] != hs);
+                __syncthreads();
+                // (keys read back from memory: the register words end at the
+                // compaction, which leaves the sort its registers)
+                if (unique) {
+                    for (long long i = tid; i < n_items; i += kThreads) {
+                        const uint64_t key = keys[i];
+                        if (key != kNoKey && static_cast<uint32_t>(key >> 32) == hs && key <= theta)
+                            sh_theta = key;
+                    }
+                    __syncthreads();
+                    theta = sh_theta;
+                } else {
+                    theta = select_key(static_cast<uint64_t>(hs) << 32, 0xFFFFFFFF00000000ull,
+                                       static_cast<unsigned>(stop - 1 - lo), 3, theta, false);
+                }
+            }
         } else {
             for (long long i0 = 0; i0 < n_items; i0 += kThreads) {
                 const long long i = i0 + tid;
@@ -473,7 +562,8 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
                     __syncthreads();
                 }
             }
-            theta = curve_stop(sorted, n, B, curve, sh_f64, &sh_stop);
+            const int stop = curve_stop(sorted, n, B, curve, sh_f64, &sh_stop);
+            theta = stop > 0 ? sorted[stop - 1] : 0;
         }
     }
 
