@@ -172,6 +172,48 @@ def test_schedule_parity_random(dsp, orc, seed):
             np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
 
 
+@pytest.mark.parametrize("B,K,extra,conf_kind", [
+    (2048, 16, 12000, "beta"),    # 32768 items in registers, 12000 candidates: 16 per thread
+    (2048, 16, 12000, "ones"),    # every S equal: the stop falls inside one run of ties
+    (1500, 16, 9000, "levels"),   # few distinct confidences: many runs of equal S
+    (3000, 16, 20000, "beta"),    # 48000 items: survival walk and 64-bit sort in memory
+    (3000, 16, 20000, "levels"),
+])
+def test_schedule_large_parity(dsp, orc, B, K, extra, conf_kind):
+    """Scheduler sizes past the small-batch paths: more than 8192 candidates
+    sorted in LDS, more than 32768 items (keys and the candidate sort in
+    workspace memory), and equal survival values around the stop rank, where
+    the exact threshold key is chosen among keys that share the stop item's S.
+    Each case runs without a curve, with a flat curve and with two sloped ones."""
+    rng = np.random.default_rng(B + K + extra)
+    if conf_kind == "beta":
+        conf = rng.beta(5, 2, (B, K)).astype(np.float32)
+    elif conf_kind == "ones":
+        conf = np.ones((B, K), np.float32)
+    else:
+        conf = rng.choice(np.array([1.0, 0.75, 0.5], np.float32), (B, K))
+    budget = B + extra
+    c = torch.from_numpy(conf).cuda()
+    curves = [None, ([float(B), float(budget)], [1.0, 1.0]),
+              ([float(B + 64), float(B + 8192)], [1.0, 1.25]),
+              ([float(B), float(B + 2048), float(B + 4096)], [1.0, 1.5, 4.0])]
+    for curve in curves:
+        if curve is None:
+            L, offs, S = dsp.dspark_schedule(c, budget)
+            oL, ooffs, oS, n = orc.schedule(conf, budget)
+        else:
+            cn = np.array(curve[0], np.float32)
+            ct = np.array(curve[1], np.float32)
+            L, offs, S = dsp.dspark_schedule(c, budget, cn.tolist(), ct.tolist())
+            oL, ooffs, oS, n = orc.schedule(conf, budget, cn.astype(np.float64),
+                                            ct.astype(np.float64))
+        torch.cuda.synchronize()
+        print(conf_kind, B, K, budget, None if curve is None else curve[1], "taken", n)
+        np.testing.assert_array_equal(S.cpu().numpy(), oS)
+        np.testing.assert_array_equal(L.cpu().numpy(), oL)
+        np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+
+
 @pytest.mark.parametrize("jump", [1.05, 1.3, 2.0])
 def test_schedule_stair_step_curve_parity(dsp, orc, inputs, jump):
     """A stair-step latency curve over the whole selectable range (49 points
