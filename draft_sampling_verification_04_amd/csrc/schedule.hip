@@ -269,6 +269,11 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
     for (int j = 0; j < kKeyRegs; ++j) kh[j] = 0xFFFFFFFFu;
     const unsigned uK = static_cast<unsigned>(K > 0 ? K : 1);
     const bool staged = n_items <= static_cast<long long>(kThreads) * kKeyRegs;
+    const long long D = budget - B > 0 ? budget - B : 0;
+    // the budget holds every item and no curve can stop the walk: every
+    // positive item is taken, which is known before anything is counted, so
+    // no keys are written and no total is formed
+    const bool all_fit = curve.n <= 0 && D >= n_items;
     // stage slot of item (b, k)
     auto slot_of = [&](unsigned b, unsigned k) -> unsigned {
         unsigned c = k + (b - (b / uK) * uK);
@@ -306,9 +311,12 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
                 const unsigned b = o / uK, k = o - b * uK;
                 const float S = stage[slot_of(b, k)];
                 if (survival) survival[o] = S;
-                const uint32_t h = S > 0.0f ? 0xFFFFFFFFu - __float_as_uint(S) : 0xFFFFFFFFu;
-                keys[o] = h != 0xFFFFFFFFu ? (static_cast<uint64_t>(h) << 32) | (k * B + b) : kNoKey;
-                kh[j] = h;
+                if (!all_fit) {
+                    const uint32_t h = S > 0.0f ? 0xFFFFFFFFu - __float_as_uint(S) : 0xFFFFFFFFu;
+                    keys[o] = h != 0xFFFFFFFFu ? (static_cast<uint64_t>(h) << 32) | (k * B + b)
+                                               : kNoKey;
+                    kh[j] = h;
+                }
             }
         }
     } else {
@@ -320,9 +328,10 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
                 S = S * conf[o];
                 if (survival) survival[o] = S;
                 const bool pos = S > 0.0f;
-                keys[o] = pos ? (static_cast<uint64_t>(0xFFFFFFFFu - __float_as_uint(S)) << 32) |
-                                    static_cast<uint32_t>(k * B + b)
-                              : kNoKey;
+                if (!all_fit)
+                    keys[o] = pos ? (static_cast<uint64_t>(0xFFFFFFFFu - __float_as_uint(S)) << 32) |
+                                        static_cast<uint32_t>(k * B + b)
+                                  : kNoKey;
                 pos_b += pos;
             }
             n_pos_local += pos_b;
@@ -330,11 +339,13 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
             if (b == tid) my_len = pos_b;
         }
     }
-    const unsigned long long n_pos = block_sum<unsigned long long>(n_pos_local, sh_u64);
-    const long long D = budget - B > 0 ? budget - B : 0;
-    const long long dsel = D < static_cast<long long>(n_pos) ? D : static_cast<long long>(n_pos);
+    const unsigned long long n_pos =
+        all_fit ? 0ull : block_sum<unsigned long long>(n_pos_local, sh_u64);
+    const long long dsel =
+        all_fit ? 0 : (D < static_cast<long long>(n_pos) ? D : static_cast<long long>(n_pos));
     // every positive item is taken: L_b is already set
-    const bool take_all = dsel == static_cast<long long>(n_pos) && (curve.n <= 0 || dsel == 0);
+    const bool take_all =
+        all_fit || (dsel == static_cast<long long>(n_pos) && (curve.n <= 0 || dsel == 0));
 
     // while a threshold search or a sort follows, up to 32768 keys keep their
     // high word ~bits(S) in registers (key i in slot i / kThreads of thread
