@@ -36,28 +36,21 @@
  *   - random draws: Philox4x32-10 with key (seed lo32, seed hi32) and counter
  *     (v >> 2, position, request, tag); the draw for vocab index v is output
  *     word v & 3.  Tags: 0 draft Gumbel, 1 accept uniform (v = 0),
- *     2 residual / bonus Gumbel, 3 draft block Gumbel (v = block index),
- *     4 residual / bonus block Gumbel (v = block index).
+ *     2 residual / fallback / bonus Gumbel.
  *   - uniform u = ((w >> 9) + 0.5) * 2^-23, exact in fp32, in (0, 1).
  *   - Gumbel G = -log(-log u), evaluated in fp64 and rounded to fp32.
  *   - temperature T > 0 multiplies logits by the fp32 reciprocal 1/T on both
  *     the draft and the target side; T == 0 means greedy on both sides.
  *   - argmax ties go to the smallest index.
- *   - draft tokens (T > 0) are drawn by Gumbel-max in two levels: the
- *     vocabulary is cut into blocks of 64 consecutive entries, the block with
- *     the largest fp32(log-mass) + G (tag 3, keyed by the block index) wins,
- *     and the token is the Gumbel-argmax of z inside that block (tag 0, keyed
- *     by the entry).  This is an exact draw from softmax(z) for any partition
- *     (the first level picks a block with probability equal to its mass, the
- *     second an entry with its probability inside the block), and with
- *     V <= 64 it is the plain Gumbel-argmax.
- *   - the verifier's draws (the residual at the first rejection, the fallback
- *     to p_t and the bonus token) are made in two levels the same way, over
- *     the same 64-entry blocks, with block draws of tag 4 and entry draws of
- *     tag 2.  Residual: block mass sum of max(0, p_t - p_d) in fp64, block key
- *     fp32(log mass) + G for blocks with positive mass, then inside the
- *     winning block the Gumbel-argmax of fp32(log(p_t - p_d)) over its
- *     positive entries.  Fallback and bonus: the two-level draw of y = t / T.
+ *   - every draw is a plain Gumbel-max over the whole vocabulary, each entry
+ *     with its own key: draft token x_k = argmax_v fp32(z_v + G(tag 0, v));
+ *     after a rejection at row j the residual draw is argmax over the entries
+ *     with r_v = p_t(v) - p_d(v) > 0 (fp64) of fp32(log r_v) + G(tag 2, v),
+ *     falling back to argmax_v fp32(y_v + G(tag 2, v)) when no entry is
+ *     positive (rounding only); the bonus token is argmax_v fp32(y_v + G(tag 2,
+ *     v)) on row L + 1.  Gumbel-max is an exact softmax sample: the argmax of
+ *     log p_v + G_v over independent standard Gumbels G_v lands on v with
+ *     probability p_v.
  */
 #include <math.h>
 #include <stdint.h>
@@ -66,8 +59,7 @@
 
 #define ORACLE_API __attribute__((visibility("default")))
 
-enum { TAG_DRAFT = 0, TAG_ACCEPT = 1, TAG_RESAMPLE = 2, TAG_DRAFT_BLOCK = 3, TAG_VERIFY_BLOCK = 4 };
-enum { DRAFT_BLOCK = 64 };
+enum { TAG_DRAFT = 0, TAG_ACCEPT = 1, TAG_RESAMPLE = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* Philox4x32-10 (SC'11, section 3).  One round multiplies words 0 and 2 by
@@ -186,95 +178,27 @@ static int gumbel_argmax_range(const float* z, int lo, int hi, uint64_t seed, ui
     return best;
 }
 
-/* Softmax draw in two levels (see the readings above): block keys
- * fp32(log sum_{v in blk} exp z_v) + G(block_tag, blk), then the Gumbel-argmax
- * of z inside the winning block with the entry_tag draws.  *gap is the smaller
- * of the two levels' top-2 gaps, so a near tie at either level is reported. */
-static int gumbel_argmax_blocks_tags(const float* z, int V, uint64_t seed, uint32_t b,
-                                     uint32_t pos, uint32_t block_tag, uint32_t entry_tag,
-                                     double* gap) {
-    const int nb = (V + DRAFT_BLOCK - 1) / DRAFT_BLOCK;
-    int best = -1;
-    float best_key = -INFINITY, second_key = -INFINITY;
-    for (int blk = 0; blk < nb; ++blk) {
-        const int lo = blk * DRAFT_BLOCK;
-        const int n = (V - lo < DRAFT_BLOCK) ? V - lo : DRAFT_BLOCK;
-        float key = (float)log_sum_exp(z + lo, n) +
-                    oracle_gumbel(seed, b, pos, block_tag, (uint32_t)blk);
-        if (best < 0 || key > best_key) {
-            second_key = best_key;
-            best_key = key;
-            best = blk;
-        } else if (key > second_key) {
-            second_key = key;
-        }
-    }
-    const int lo = best * DRAFT_BLOCK;
-    const int hi = (V - lo < DRAFT_BLOCK) ? V : lo + DRAFT_BLOCK;
-    double g_entry;
-    const int x = gumbel_argmax_range(z, lo, hi, seed, b, pos, entry_tag, &g_entry);
-    if (gap) {
-        const double g_block = (double)best_key - (double)second_key;
-        *gap = g_block < g_entry ? g_block : g_entry;
-    }
-    return x;
-}
-
-/* The draft token draw: blocks with tag 3, entries with tag 0. */
-static int gumbel_argmax_blocks(const float* z, int V, uint64_t seed, uint32_t b, uint32_t pos,
-                                double* gap) {
-    return gumbel_argmax_blocks_tags(z, V, seed, b, pos, TAG_DRAFT_BLOCK, TAG_DRAFT, gap);
-}
-
-/* Residual draw in two levels: res[v] = p_t(v) - p_d(v) in fp64.  Blocks of 64
- * entries with positive mass sum_{v in blk, res > 0} res_v compete with key
- * fp32(log mass) + G(tag 4, blk); inside the winning block the token is the
- * argmax over its positive entries of fp32(log res_v) + G(tag 2, v).  Returns
+/* Residual draw: res[v] = p_t(v) - p_d(v) in fp64; the token is the argmax
+ * over the entries with res[v] > 0 of fp32(log res[v]) + G(tag 2, v).  Returns
  * -1 when no entry is positive (the caller then falls back to p_t). */
-static int residual_two_level(const double* res, int V, uint64_t seed, uint32_t b, uint32_t pos,
-                              double* gap) {
-    const int nb = (V + DRAFT_BLOCK - 1) / DRAFT_BLOCK;
+static int residual_gumbel_argmax(const double* res, int V, uint64_t seed, uint32_t b,
+                                  uint32_t pos, double* gap) {
     int best = -1;
-    float best_key = -INFINITY, second_key = -INFINITY;
-    for (int blk = 0; blk < nb; ++blk) {
-        const int lo = blk * DRAFT_BLOCK;
-        const int hi = (V - lo < DRAFT_BLOCK) ? V : lo + DRAFT_BLOCK;
-        double mass = 0.0;
-        for (int v = lo; v < hi; ++v)
-            if (res[v] > 0.0) mass += res[v];
-        if (!(mass > 0.0)) continue;
-        const float key =
-            (float)log(mass) + oracle_gumbel(seed, b, pos, TAG_VERIFY_BLOCK, (uint32_t)blk);
-        if (best < 0 || key > best_key) {
-            second_key = best_key;
-            best_key = key;
-            best = blk;
-        } else if (key > second_key) {
-            second_key = key;
-        }
-    }
-    if (best < 0) return -1;
-    const int lo = best * DRAFT_BLOCK;
-    const int hi = (V - lo < DRAFT_BLOCK) ? V : lo + DRAFT_BLOCK;
-    int x = -1;
-    float bv = -INFINITY, sv = -INFINITY;
-    for (int v = lo; v < hi; ++v) {
+    float best_val = -INFINITY, second_val = -INFINITY;
+    for (int v = 0; v < V; ++v) {
         if (!(res[v] > 0.0)) continue;
-        const float p = (float)log(res[v]) + oracle_gumbel(seed, b, pos, TAG_RESAMPLE, (uint32_t)v);
-        if (x < 0 || p > bv) {
-            sv = bv;
-            bv = p;
-            x = v;
-        } else if (p > sv) {
-            sv = p;
+        const float pert =
+            (float)log(res[v]) + oracle_gumbel(seed, b, pos, TAG_RESAMPLE, (uint32_t)v);
+        if (best < 0 || pert > best_val) {
+            second_val = best_val;
+            best_val = pert;
+            best = v;
+        } else if (pert > second_val) {
+            second_val = pert;
         }
     }
-    if (gap) {
-        const double g_block = (double)best_key - (double)second_key;
-        const double g_entry = (double)bv - (double)sv;
-        *gap = g_block < g_entry ? g_block : g_entry;
-    }
-    return x;
+    if (gap) *gap = (double)best_val - (double)second_val;
+    return best;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -318,7 +242,8 @@ ORACLE_API void oracle_target_probs(const float* t_row, int V, float T, double* 
 /* ------------------------------------------------------------------------ */
 /* Draft for one request ([yage] Markov head; [guide] 3.1 sequential head).
  * For k = 1..K: draft logits with the previous token (x_0 = prev0), then
- * x_k = two-level Gumbel-argmax of z (T > 0) or argmax of s (T == 0).
+ * x_k = Gumbel-argmax of z over the whole vocabulary (T > 0, tag-0 keys) or
+ * argmax of s (T == 0).
  * Outputs per position: token, log p_d(x_k) = z_{x_k} - lse_d, lse_d (for T == 0
  * lse_d is the row maximum and log p_d is 0: p_d is one-hot), and the top-2
  * gap of the values the argmax was taken over. */
@@ -337,7 +262,7 @@ ORACLE_API void oracle_draft_request(const float* base /* [K][V] */, const float
         double g;
         if (T > 0.0f) {
             double l = log_sum_exp(z, V);
-            x = gumbel_argmax_blocks(z, V, seed, b, pos, &g);
+            x = gumbel_argmax_range(z, 0, V, seed, b, pos, TAG_DRAFT, &g);
             lse[k] = (float)l;
             logp[k] = (float)((double)z[x] - l);
         } else {
@@ -376,9 +301,11 @@ ORACLE_API void oracle_draft_batch(const float* base /* [B][K][V] */, const floa
  *                iff  x_j == argmax t_j                          (T == 0)
  *   a = number of leading accepts (strict prefix)
  *   a < L : next ~ normalise(max(0, p_t - p_d)) at j* = a + 1, by Gumbel-max
- *           over log of the positive residual; if no residual mass is left
- *           (rounding only) next ~ p_t.  T == 0: next = argmax t_{j*}.
- *   a = L : next ~ p_t at row L + 1 (bonus).  T == 0: argmax t_{L+1}.
+ *           over log of the positive residual entries (tag 2); if no residual
+ *           mass is left (rounding only) next ~ p_t by Gumbel-max over y.
+ *           T == 0: next = argmax t_{j*}.
+ *   a = L : next ~ p_t at row L + 1 (bonus), Gumbel-max over y (tag 2).
+ *           T == 0: argmax t_{L+1}.
  *
  * p_d is recomputed here from the draft definition (it does not trust any
  * passed-in draft probability).
@@ -388,6 +315,9 @@ ORACLE_API void oracle_draft_batch(const float* base /* [B][K][V] */, const floa
  * maximum for T == 0).
  * accept_gap = min over the decided positions of |log u - log ratio|
  * (the top-2 target gap for T == 0); next_gap = top-2 gap of the final argmax.
+ * branch (nullable) says how next was drawn: 0 bonus (a = L), 1 residual (or
+ * the target argmax for T == 0), 2 fallback to p_t (rejected, but no entry of
+ * p_t - p_d is positive).
  */
 ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t prev0,
                                       const float* base /* [K][V] */, const float* A,
@@ -396,7 +326,7 @@ ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t p
                                       uint64_t seed, uint32_t b, int32_t* accepted,
                                       int32_t* next_token, float* row_lse_t,
                                       float* row_logratio, double* accept_gap,
-                                      double* next_gap) {
+                                      double* next_gap, int32_t* branch) {
     float* s = (float*)malloc(sizeof(float) * (size_t)V);
     float* z = (float*)malloc(sizeof(float) * (size_t)V);
     float* y = (float*)malloc(sizeof(float) * (size_t)V);
@@ -450,7 +380,7 @@ ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t p
         }
     }
 
-    int next;
+    int next, br;
     double ng;
     if (a < L) {
         const int js = a + 1;
@@ -463,25 +393,30 @@ ORACLE_API void oracle_verify_request(const int32_t* tokens /* [K] */, int32_t p
             double lse_t = log_sum_exp(y, V);
             for (int v = 0; v < V; ++v)
                 scratch[v] = exp((double)y[v] - lse_t) - exp((double)z[v] - lse_d);
-            next = residual_two_level(scratch, V, seed, b, (uint32_t)js, &ng);
-            if (next < 0)  /* no positive residual mass (rounding only) */
-                next = gumbel_argmax_blocks_tags(y, V, seed, b, (uint32_t)js, TAG_VERIFY_BLOCK,
-                                                 TAG_RESAMPLE, &ng);
+            next = residual_gumbel_argmax(scratch, V, seed, b, (uint32_t)js, &ng);
+            if (next >= 0) {
+                br = 1;
+            } else {  /* no positive residual mass (rounding only): draw from p_t */
+                next = gumbel_argmax_range(y, 0, V, seed, b, (uint32_t)js, TAG_RESAMPLE, &ng);
+                br = 2;
+            }
         } else {
             next = plain_argmax(t, V, &ng);
+            br = 1;
         }
     } else {
         const float* t = target + (size_t)L * (size_t)V;
         if (T > 0.0f) {
             for (int v = 0; v < V; ++v) y[v] = t[v] * it;
-            next = gumbel_argmax_blocks_tags(y, V, seed, b, (uint32_t)(L + 1), TAG_VERIFY_BLOCK,
-                                             TAG_RESAMPLE, &ng);
+            next = gumbel_argmax_range(y, 0, V, seed, b, (uint32_t)(L + 1), TAG_RESAMPLE, &ng);
         } else {
             next = plain_argmax(t, V, &ng);
         }
+        br = 0;
     }
     *accepted = a;
     *next_token = next;
+    if (branch) *branch = br;
     if (accept_gap) *accept_gap = min_gap;
     if (next_gap) *next_gap = ng;
     free(s);
@@ -498,7 +433,8 @@ ORACLE_API void oracle_verify_batch(const int32_t* tokens /* [B][K] */, const in
                                     const float* target, const int64_t* row_offset,
                                     const int32_t* L, const float* T, uint64_t seed,
                                     int32_t* accepted, int32_t* next_token, float* row_lse_t,
-                                    float* row_logratio, double* accept_gap, double* next_gap) {
+                                    float* row_logratio, double* accept_gap, double* next_gap,
+                                    int32_t* branch) {
     for (int b = 0; b < B; ++b) {
         const int Lb = L ? L[b] : K;
         const size_t ro = (size_t)row_offset[b];
@@ -506,7 +442,8 @@ ORACLE_API void oracle_verify_batch(const int32_t* tokens /* [B][K] */, const in
                               base + (size_t)b * (size_t)K * (size_t)V, A, W, V, r, K,
                               target + ro * (size_t)V, Lb, T[b], seed, (uint32_t)b,
                               accepted + b, next_token + b, row_lse_t + ro, row_logratio + ro,
-                              accept_gap ? accept_gap + b : NULL, next_gap ? next_gap + b : NULL);
+                              accept_gap ? accept_gap + b : NULL, next_gap ? next_gap + b : NULL,
+                              branch ? branch + b : NULL);
     }
 }
 

@@ -23,8 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dspark_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-TAG_DRAFT, TAG_ACCEPT, TAG_RESAMPLE, TAG_DRAFT_BLOCK = 0, 1, 2, 3
-DRAFT_BLOCK = 64
+TAG_DRAFT, TAG_ACCEPT, TAG_RESAMPLE = 0, 1, 2
+BRANCH_BONUS, BRANCH_RESIDUAL, BRANCH_FALLBACK = 0, 1, 2
 
 
 def build(force: bool = False) -> str:
@@ -75,10 +75,10 @@ def _declare(L):
     L.oracle_draft_batch.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _U64, _P, _P, _P, _P]
     L.oracle_draft_batch.restype = None
     L.oracle_verify_request.argtypes = [_P, ctypes.c_int32, _P, _P, _P, _I, _I, _I, _P, _I, _F,
-                                        _U64, _U32, _P, _P, _P, _P, _P, _P]
+                                        _U64, _U32, _P, _P, _P, _P, _P, _P, _P]
     L.oracle_verify_request.restype = None
     L.oracle_verify_batch.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _U64,
-                                      _P, _P, _P, _P, _P, _P]
+                                      _P, _P, _P, _P, _P, _P, _P]
     L.oracle_verify_batch.restype = None
     L.oracle_curve_tau.argtypes = [_P, _P, _I, _D]
     L.oracle_curve_tau.restype = _D
@@ -182,12 +182,15 @@ def verify_request(tokens, prev0, base, A, W, target_rows, L, T, seed, b):
     ratio = np.zeros(L + 1, np.float32)
     ag = np.zeros(1, np.float64)
     ng = np.zeros(1, np.float64)
+    br = np.zeros(1, np.int32)
     lib().oracle_verify_request(tkp, int(prev0), bp, ap, wp, V, r, K, trp, int(L), float(T),
                                 int(seed), int(b), acc.ctypes.data_as(_P), nxt.ctypes.data_as(_P),
                                 lse_t.ctypes.data_as(_P), ratio.ctypes.data_as(_P),
-                                ag.ctypes.data_as(_P), ng.ctypes.data_as(_P))
+                                ag.ctypes.data_as(_P), ng.ctypes.data_as(_P),
+                                br.ctypes.data_as(_P))
     return dict(accepted=int(acc[0]), next_token=int(nxt[0]), row_lse_t=lse_t,
-                row_logratio=ratio, accept_gap=float(ag[0]), next_gap=float(ng[0]))
+                row_logratio=ratio, accept_gap=float(ag[0]), next_gap=float(ng[0]),
+                branch=int(br[0]))
 
 
 def verify_batch(tokens, prev0, base, A, W, target, row_offsets, lengths, T, seed):
@@ -213,12 +216,14 @@ def verify_batch(tokens, prev0, base, A, W, target, row_offsets, lengths, T, see
     ratio = np.zeros(rows, np.float32)
     ag = np.zeros(B, np.float64)
     ng = np.zeros(B, np.float64)
+    br = np.zeros(B, np.int32)
     lib().oracle_verify_batch(tkp, pp, bp, ap, wp, B, K, V, r, trp, rop, lp, tp, int(seed),
                               acc.ctypes.data_as(_P), nxt.ctypes.data_as(_P),
                               lse_t.ctypes.data_as(_P), ratio.ctypes.data_as(_P),
-                              ag.ctypes.data_as(_P), ng.ctypes.data_as(_P))
+                              ag.ctypes.data_as(_P), ng.ctypes.data_as(_P),
+                              br.ctypes.data_as(_P))
     return dict(accepted=acc, next_token=nxt, row_lse_t=lse_t, row_logratio=ratio,
-                accept_gap=ag, next_gap=ng)
+                accept_gap=ag, next_gap=ng, branch=br)
 
 
 # ---------------------------------------------------------------------- schedule

@@ -55,7 +55,7 @@ def test_dense_factor_matches_matrix_product(orc):
 
 
 def test_w_zero_is_independent_parallel_drafting(orc):
-    base, A, _ = _rand_problem(3, V=53, K=4)
+    base, A, _ = _rand_problem(3, V=1200, K=4)
     W = np.zeros((A.shape[1], base.shape[1]), np.float32)
     T, seed, b = 0.8, 99, 6
     it = np.float32(1.0) / np.float32(T)
@@ -161,67 +161,62 @@ def _draws(orc, base_k, A, W, prev, T, n, seed):
     return tok[:, 0], gap[:, 0]
 
 
-def test_two_level_draw_is_an_exact_softmax_sample(orc):
-    """Draft draws over three blocks (64 + 64 + 22 entries) follow softmax(z):
-    per entry, and per block (the first level picks a block with its mass)."""
-    V, r, n = 150, 4, 300000
+def _chi2_pvalue(counts, p, min_expect=20.0):
+    """Chi-square p-value of counts against probabilities p, with the bins
+    expected below min_expect lumped into one."""
+    n = counts.sum()
+    e = p * n
+    big = e >= min_expect
+    obs = np.append(counts[big], counts[~big].sum())
+    exp = np.append(e[big], e[~big].sum())
+    keep = exp > 0
+    obs, exp = obs[keep], exp[keep]
+    return stats.chi2.sf(((obs - exp) ** 2 / exp).sum(), len(obs) - 1)
+
+
+def test_draw_is_an_exact_softmax_sample_over_many_entries(orc):
+    """Gumbel-max with one key per entry is an exact draw from softmax(z):
+    100k independent request streams over 300 entries pass a chi-square test
+    against the exact p_d.  The same statistic rejects a plausible mistake
+    (the Gumbel's outer sign dropped: z + log(-log u), built from the oracle's
+    own uniforms), so the test is sharp enough to see one."""
+    V, r, n = 300, 4, 100_000
     rng = np.random.default_rng(21)
     base = rng.normal(0, 0.7, V).astype(np.float32)
     A = rng.normal(0, 0.5, (V, r)).astype(np.float32)
     W = rng.normal(0, 0.5, (r, V)).astype(np.float32)
-    T = 0.9
-    tok, _ = _draws(orc, base, A, W, 3, T, n, seed=5)
-    p = orc.draft_probs(base, A, W, 3, T)
-    counts = np.bincount(tok, minlength=V)
-    expect = p * n
-    assert expect.min() > 20
-    chi2 = ((counts - expect) ** 2 / expect).sum()
-    assert stats.chi2.sf(chi2, V - 1) > 1e-3
-    blocks = np.arange(V) // 64
-    cb = np.bincount(blocks[tok], minlength=3)
-    eb = np.array([p[blocks == j].sum() for j in range(3)]) * n
-    chi2b = ((cb - eb) ** 2 / eb).sum()
-    assert stats.chi2.sf(chi2b, 2) > 1e-3
-
-
-@pytest.mark.parametrize("V", [64, 65])
-def test_single_populated_block_is_the_plain_gumbel_argmax(orc, V):
-    """With V = 64 there is one block; with V = 65 and the last entry at a
-    logit of -1e30 the second block has no mass.  Either way the draw is the
-    Gumbel-argmax of z over the first 64 entries with the tag-0 draws."""
-    rng = np.random.default_rng(V)
-    base = rng.normal(0, 1.5, (2, V)).astype(np.float32)
-    if V == 65:
-        base[:, 64] = -1e30
-    r = 4
-    A = rng.normal(0, 0.5, (V, r)).astype(np.float32)
-    W = np.zeros((r, V), np.float32)  # no bias: z = base / T
-    T, seed, b = 1.3, 41, 9
+    T, prev, seed = 0.9, 3, 5
+    tok, _ = _draws(orc, base, A, W, prev, T, n, seed)
+    p = orc.draft_probs(base, A, W, prev, T)
+    assert (p * n >= 20).sum() > 250  # nearly every entry is its own bin
+    assert _chi2_pvalue(np.bincount(tok, minlength=V), p) > 1e-3
+    # the planted mistake, on 5000 streams: argmax z + log(-log u) instead of z + G
     it = np.float32(1.0) / np.float32(T)
-    tok, _, _, _ = orc.draft_request(base, A, W, 0, T, seed, b)
-    for k in range(2):
-        z = base[k, :64] * it
-        g = np.array([orc.gumbel(seed, b, k + 1, 0, v) for v in range(64)], np.float32)
-        assert tok[k] == int(np.argmax(z + g))
+    M = (A[prev].astype(np.float64) @ W.astype(np.float64)).astype(np.float32)
+    z = (base + M) * it
+    m = 5000
+    wrong = np.empty(m, np.int64)
+    for b in range(m):
+        u = np.array([orc.uniform(seed, b, 1, 0, v) for v in range(V)], np.float64)
+        wrong[b] = int(np.argmax(z + np.log(-np.log(u))))
+    assert _chi2_pvalue(np.bincount(wrong, minlength=V), p) < 1e-6
 
 
-def test_mass_in_one_block_draws_inside_it(orc):
-    """Blocks with no mass (logits -1e30) are never chosen, and inside the one
-    populated block the draw is its Gumbel-argmax: a plain Gumbel-max over a
-    sub-range of the vocabulary."""
+def test_mass_in_one_range_draws_inside_it(orc):
+    """Entries with no mass (logits -1e30) are never drawn; lse is that of the
+    populated range (scipy)."""
     V, r = 300, 4
     rng = np.random.default_rng(8)
     base = np.full((3, V), -1e30, np.float32)
-    lo, hi = 128, 192  # block 2
+    lo, hi = 97, 181
     base[:, lo:hi] = rng.normal(0, 1.0, (3, hi - lo)).astype(np.float32)
     A = rng.normal(0, 0.5, (V, r)).astype(np.float32)
     W = np.zeros((r, V), np.float32)
-    T, seed, b = 0.8, 13, 4
+    T, seed = 0.8, 13
     it = np.float32(1.0) / np.float32(T)
-    tok, logp, lse, _ = orc.draft_request(base, A, W, 0, T, seed, b)
+    for b in range(40):
+        tok, logp, lse, _ = orc.draft_request(base, A, W, 0, T, seed, b)
+        assert ((lo <= tok) & (tok < hi)).all()
     for k in range(3):
-        assert lo <= tok[k] < hi
         z = base[k, lo:hi] * it
-        g = np.array([orc.gumbel(seed, b, k + 1, 0, v) for v in range(lo, hi)], np.float32)
-        assert tok[k] == lo + int(np.argmax(z + g))
         np.testing.assert_allclose(lse[k], logsumexp(z.astype(np.float64)), rtol=1e-6)

@@ -46,7 +46,8 @@ def _draft_problem(seed, V, K, r=3):
 
 
 @pytest.mark.parametrize("V,K,T", [(4, 2, 1.0), (5, 3, 0.7), (3, 3, 1.0), (6, 1, 1.3),
-                                   (4, 3, 0.0), (5, 2, 0.0)])
+                                   (4, 3, 0.0), (5, 2, 0.0), (8, 3, 1.0), (8, 3, 0.6),
+                                   (8, 3, 0.0)])
 def test_lossless_by_exact_enumeration(orc, V, K, T):
     base, A, W = _draft_problem(10 * V + K, V, K)
     tgt = PrefixTargets(V, seed=V * 31 + K, shift=base[0] * 0.5)
@@ -247,7 +248,7 @@ def _chi2_ok(counts, p, min_expect=20.0):
     return stats.chi2.sf(chi2, len(obs) - 1) > 1e-3
 
 
-def _three_block_case(seed_rng):
+def _residual_case(seed_rng):
     V, r = 150, 4
     rng = np.random.default_rng(seed_rng)
     base = rng.normal(0, 1.0, (1, V)).astype(np.float32)
@@ -257,12 +258,11 @@ def _three_block_case(seed_rng):
     return V, base, A, W, rows
 
 
-def test_two_level_residual_over_several_blocks(orc):
-    """After a rejection at position 1 the next token is drawn in two levels
-    (block mass of max(0, p_t - p_d), then inside the block) over three blocks
-    of 64 + 64 + 22 entries; it must follow normalise(max(0, p_t - p_d)) per
-    entry and per block."""
-    V, base, A, W, rows = _three_block_case(33)
+def test_residual_draw_over_many_entries(orc):
+    """After a rejection at position 1 the next token is the Gumbel-max over the
+    positive entries of p_t - p_d (150 entries, 40k seeded draft-then-verify
+    trials): it must follow normalise(max(0, p_t - p_d))."""
+    V, base, A, W, rows = _residual_case(33)
     T, prev = 1.0, 3
     pd = orc.draft_probs(base[0], A, W, prev, T)
     pt = orc.target_probs(rows[0], T)
@@ -273,28 +273,68 @@ def test_two_level_residual_over_several_blocks(orc):
         tok, _, _, _ = orc.draft_request(base, A, W, prev, T, seed, 0)
         out = orc.verify_request(tok, prev, base, A, W, rows, 1, T, seed, 0)
         if out["accepted"] == 0:
+            assert out["branch"] == orc.BRANCH_RESIDUAL
             counts[out["next_token"]] += 1
+        else:
+            assert out["branch"] == orc.BRANCH_BONUS
     assert counts.sum() > 10000
     assert _chi2_ok(counts, res)
-    blocks = np.arange(V) // 64
-    cb = np.bincount(blocks, weights=counts, minlength=3)
-    eb = np.array([res[blocks == j].sum() for j in range(3)])
-    assert _chi2_ok(cb, eb)
+    assert counts[res == 0].sum() == 0  # never an entry where p_t <= p_d
 
 
-def test_two_level_bonus_over_several_blocks(orc):
-    """With L = 0 the next token is the bonus draw from target row 1, in two
-    levels over three blocks; it must follow p_t per entry and per block."""
-    V, base, A, W, rows = _three_block_case(34)
+def test_bonus_draw_over_many_entries(orc):
+    """With L = 0 the next token is the bonus draw from target row 1 (150
+    entries, 30k trials); it must follow p_t."""
+    V, base, A, W, rows = _residual_case(34)
     T, prev = 0.8, 5
     pt = orc.target_probs(rows[1], T)
     counts = np.zeros(V, np.int64)
     tok = np.zeros(1, np.int32)
     for seed in range(30000):
         out = orc.verify_request(tok, prev, base, A, W, rows[1:2], 0, T, seed, 0)
+        assert out["branch"] == orc.BRANCH_BONUS
         counts[out["next_token"]] += 1
     assert _chi2_ok(counts, pt)
-    blocks = np.arange(V) // 64
-    cb = np.bincount(blocks, weights=counts, minlength=3)
-    eb = np.array([pt[blocks == j].sum() for j in range(3)])
-    assert _chi2_ok(cb, eb)
+
+
+def fallback_case(V=40, seed=17):
+    """A rejection whose residual p_t - p_d has no positive entry in fp64.
+
+    Target row 1 equals the draft row except at the drafted token x, whose
+    logit is -200 in the draft and -201 in the target: its mass (e^-200) is far
+    below the fp64 resolution of either normaliser, so the two log-normalisers
+    are bit-identical, p_t(v) == p_d(v) for every v != x, and p_t(x) < p_d(x).
+    The accept ratio is exactly e^-1.  In exact arithmetic the residual law is
+    p_t restricted to v != x, which is p_t to within e^-200: the fallback to
+    p_t is the exact-arithmetic answer."""
+    rng = np.random.default_rng(seed)
+    base = rng.normal(0, 1, (1, V)).astype(np.float32)
+    x = 7
+    base[0, x] = -200.0
+    A = np.zeros((V, 2), np.float32)
+    W = np.zeros((2, V), np.float32)
+    target = np.stack([base[0], rng.normal(0, 1, V).astype(np.float32)])
+    target[0, x] = -201.0
+    return base, A, W, target, x
+
+
+def test_residual_fallback_branch(orc):
+    V = 40
+    base, A, W, target, x = fallback_case(V)
+    T, tok, N = 1.0, np.array([x], np.int32), 20000
+    counts = np.zeros(V, np.int64)
+    n_rej = 0
+    for seed in range(N):
+        out = orc.verify_request(tok, 0, base, A, W, target, 1, T, seed, 0)
+        assert out["row_logratio"][0] == -1.0
+        if out["accepted"] == 0:
+            assert out["branch"] == orc.BRANCH_FALLBACK
+            counts[out["next_token"]] += 1
+            n_rej += 1
+        else:
+            assert out["branch"] == orc.BRANCH_BONUS
+    p_rej = 1.0 - np.exp(-1.0)
+    assert abs(n_rej / N - p_rej) < 5 * np.sqrt(p_rej * (1 - p_rej) / N)
+    pt = orc.target_probs(target[0], T)
+    assert counts[x] == 0
+    assert _chi2_ok(counts, pt)
