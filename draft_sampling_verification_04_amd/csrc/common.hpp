@@ -16,17 +16,9 @@ constexpr int kWave = 64;
 constexpr uint32_t kTagDraft = 0;
 constexpr uint32_t kTagAccept = 1;
 constexpr uint32_t kTagResample = 2;
-constexpr uint32_t kTagDraftBlock = 3;
-// Draft tokens are drawn by Gumbel-max in two levels: blocks of kDraftBlock
-// consecutive vocabulary entries compete with key log(block mass) + G (tag 3,
-// counter word = block index), then the token is the Gumbel-argmax of the
-// logits inside the winning block (tag 0, word = entry).  Exact in distribution
-// for any partition; only the winning block needs per-entry draws.
-constexpr int kDraftBlock = 64;
-// The verifier's residual, fallback and bonus draws use the same 64-entry
-// blocks: block keys with tag-4 draws (word = block index), then tag-2 draws
-// (word = entry) inside the winning block.
-constexpr uint32_t kTagVerifyBlock = 4;
+// Every draw is a Gumbel-max over the whole vocabulary with one key per entry:
+// draft x_k = argmax_v z_v + G(tag 0, v); residual, fallback and bonus draws
+// use tag 2.  Keys are formed in base 2 (see entry_l2).
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -39,6 +31,8 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
 }
+
+__device__ __forceinline__ float inv_temperature(float T) { return 1.0f / T; }
 
 // ---------------------------------------------------------------- Philox
 // Philox4x32-10 (Salmon et al., SC'11, section 3): ten rounds of two 32x32->64
@@ -92,30 +86,144 @@ __device__ __forceinline__ float uniform_of(uint32_t w) {
     return f - 0x1.fffffep-1f;
 }
 
-__device__ __forceinline__ float gumbel_of(uint32_t w) {
-    return -logf(-logf(uniform_of(w)));
+// Philox4x32-10 for the counters (q, pos, b, tag) of one (request, position,
+// tag) with only the first counter word q varying, as when a lane walks the
+// vocabulary: the parts of rounds 1-3 that depend on pos, b, tag and the key
+// alone are computed once (philox_row), so one block of four draws
+// (philox_row_block) costs 37 VALU operations instead of 40.  The rounds are the
+// ones of philox10, written out with those parts folded in.
+struct PhiloxRow {
+    uint32_t k0, k1;   // key words (seed low, seed high)
+    uint32_t c3k;      // round 1: tag ^ k1
+    uint32_t x0, x1k;  // round 1 outputs 0 and 1 (x1 already xored with round 2's k0)
+    uint32_t h0k, l0;  // round 2: hi(M0 x0) ^ round 2's k1, lo(M0 x0)
+    uint32_t l0k;      // round 3: lo(M0 x0) ^ round 3's k1
+};
+
+__device__ __forceinline__ PhiloxRow philox_row(uint64_t seed, uint32_t b, uint32_t pos,
+                                                uint32_t tag) {
+    PhiloxRow r;
+    r.k0 = static_cast<uint32_t>(seed);
+    r.k1 = static_cast<uint32_t>(seed >> 32);
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * b;
+    r.x0 = static_cast<uint32_t>(p1 >> 32) ^ pos ^ r.k0;
+    r.x1k = static_cast<uint32_t>(p1) ^ (r.k0 + 0x9E3779B9u);
+    r.c3k = tag ^ r.k1;
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * r.x0;
+    r.h0k = static_cast<uint32_t>(p0 >> 32) ^ (r.k1 + 0xBB67AE85u);
+    r.l0 = static_cast<uint32_t>(p0);
+    r.l0k = r.l0 ^ (r.k1 + 2u * 0xBB67AE85u);
+    return r;
 }
 
-// Same Gumbel from the hardware base-2 logarithm.  Both logarithm arguments
-// are normal floats (u >= 2^-24 and -ln u >= 5.9e-8), so no denormal handling
-// is needed; the result agrees with the fp64 value to a few fp32 ulps.
-__device__ __forceinline__ float gumbel_fast(uint32_t w) {
-    const float a = -__builtin_amdgcn_logf(uniform_of(w)) * kLn2;
-    return -__builtin_amdgcn_logf(a) * kLn2;
+// Draws for vocabulary entries 4 q .. 4 q + 3 (word v & 3 of block q = v >> 2).
+__device__ __forceinline__ u32x4 philox_row_block(const PhiloxRow& r, uint32_t q) {
+    // round 1: x0, x1 come from (pos, b); x2, x3 from q
+    const uint64_t a0 = static_cast<uint64_t>(0xD2511F53u) * q;
+    const uint32_t x2 = static_cast<uint32_t>(a0 >> 32) ^ r.c3k;
+    const uint32_t x3 = static_cast<uint32_t>(a0);
+    // round 2: M0 x0 is fixed
+    const uint64_t a1 = static_cast<uint64_t>(0xCD9E8D57u) * x2;
+    uint32_t c0 = static_cast<uint32_t>(a1 >> 32) ^ r.x1k;
+    uint32_t c1 = static_cast<uint32_t>(a1);
+    uint32_t c2 = x3 ^ r.h0k;
+    uint32_t c3 = r.l0;
+    // round 3: the previous word 3 (lo(M0 x0)) is fixed
+    {
+        const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+        const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+        c0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, r.k0 + 2u * 0x9E3779B9u);
+        c1 = static_cast<uint32_t>(p1);
+        c2 = static_cast<uint32_t>(p0 >> 32) ^ r.l0k;
+        c3 = static_cast<uint32_t>(p0);
+    }
+    uint32_t k0 = r.k0 + 3u * 0x9E3779B9u, k1 = r.k1 + 3u * 0xBB67AE85u;
+#pragma unroll
+    for (int i = 3; i < 10; ++i) {
+        const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+        const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+        const uint32_t n0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3(static_cast<uint32_t>(p0 >> 32), c3, k1);
+        c1 = static_cast<uint32_t>(p1);
+        c3 = static_cast<uint32_t>(p0);
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return {c0, c1, c2, c3};
 }
 
-// Tag-3 draws of draft blocks 4 (blk / 4) .. 4 (blk / 4) + 3: block blk takes
-// word blk % 4 of Philox block blk / 4.
-__device__ __forceinline__ u32x4 block_draws(uint64_t seed, uint32_t b, uint32_t pos,
-                                             uint32_t blk) {
-    return philox_block(seed, b, pos, kTagDraftBlock, blk >> 2);
+// Per-lane constants of the entry key.  A sampled lane (T > 0) forms
+// key = s c2 - log2(-log2 u) with c2 = log2(e) / T: log2(e) (z + G) plus a
+// constant shared by the row, so it orders entries as z + G does.  A greedy
+// lane (T == 0) that runs the same code (a wavefront mixing both) takes c2 = 1
+// and u = 1/2, so -log2(-log2 u) = 0 and its key is s itself: the argmax.
+struct KeyLane {
+    float c2;
+    float umul, uoff;  // u = f umul + uoff from f = 1 + (w >> 9) 2^-23
+};
+
+__device__ __forceinline__ KeyLane key_lane(float T) {
+    if (T > 0.0f) return {inv_temperature(T) * kLog2e, 1.0f, -0x1.fffffep-1f};
+    return {1.0f, 0.0f, 0.5f};
 }
 
-// Base-2 Gumbel -log2(-log2 u) of a draft block's draw word: log2(e) G up to a
-// constant shared by every block of the row.
-__device__ __forceinline__ float block_gumbel2(uint32_t word) {
-    const float l1 = __builtin_amdgcn_logf(uniform_of(word));
-    return -__builtin_amdgcn_logf(-l1);
+// log2(-log2 u) of a draw word; -log2(-log2 u) = log2(e) G - log2(log2 e).
+// Both logarithm arguments are normal floats (u >= 2^-24, -log2 u >= 8.6e-8).
+__device__ __forceinline__ float entry_l2(uint32_t w, const KeyLane& kl) {
+    const float f = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9));
+    const float l1 = __builtin_amdgcn_logf(fmaf(f, kl.umul, kl.uoff));
+    return __builtin_amdgcn_logf(-l1);
+}
+
+// Residual and fallback keys of the verifier's draw after a rejection at row
+// j* (and the bonus draw of a listed full acceptance, which is the fallback
+// draw over row L_b + 1).  Per entry, in base 2 with c2 = log2(e) / T:
+//   a  = log2 p_t = t c2 - lse_t log2(e)
+//   dm = log2 p_d - log2 p_t = (s - t) c2 + (lse_t - lse_d) log2(e)
+//   fallback  kf = a - log2(-log2 u)
+//   residual  kr = kf + log2(1 - 2^dm)      (entries with p_t > p_d, dm < 0)
+// with the entry's tag-2 draw: log2(e) (y + G) and log2(e) (log(p_t - p_d) + G)
+// up to constants shared by the row.  dm is formed from the logit difference so
+// that a target row equal to the draft row gives every such entry the same dm.
+struct ResRow {
+    float c2;    // log2(e) / T
+    float lt2;   // lse_t log2(e)
+    float dl;    // (lse_t - lse_d) log2(e)
+    bool bonus;  // a listed full acceptance: fallback keys only
+    KeyLane kl;
+    PhiloxRow ph;
+};
+
+struct ResBest {
+    float br, bf;  // best residual / fallback key
+    int ir, jf;    // and its entry
+};
+
+__device__ __forceinline__ ResBest res_empty() {
+    return {-INFINITY, -INFINITY, 0x7fffffff, 0x7fffffff};
+}
+
+// One entry (s = base + bias, tv = target logit, w = its draw word); entries
+// arrive in increasing order (strict comparisons keep the smallest on ties).
+__device__ __forceinline__ void residual_entry(ResBest& rb, float sv, float tv, uint32_t w, int v,
+                                               const ResRow& R) {
+    const float a = fmaf(tv, R.c2, -R.lt2);
+    const float dm = fmaf(sv - tv, R.c2, R.dl);
+    const float kf = a - entry_l2(w, R.kl);
+    // past V both logits are -inf: a = kf = -inf and dm is NaN (no residual key)
+    const float kr = (dm < 0.0f && !R.bonus)
+                         ? kf + __builtin_amdgcn_logf(1.0f - __builtin_amdgcn_exp2f(dm))
+                         : -INFINITY;
+    if (kr > rb.br) {
+        rb.br = kr;
+        rb.ir = v;
+    }
+    if (kf > rb.bf) {
+        rb.bf = kf;
+        rb.jf = v;
+    }
 }
 
 // ---------------------------------------------------------------- row state
@@ -239,8 +347,6 @@ __device__ __forceinline__ RowState load_partial(PartialBuf p, size_t slot) {
     const float4 v = p.v[slot];
     return {v.x, v.y, v.z, v.w, p.idx[slot]};
 }
-
-__device__ __forceinline__ float inv_temperature(float T) { return 1.0f / T; }
 
 // Token ids and lengths come from device memory the host cannot check; they are
 // clamped before they index anything.

@@ -4,20 +4,18 @@
 // Per draft position k (sequential, x_k feeds position k+1):
 //   bias_v = A[x_{k-1}, :] . W[:, v]     rank-r transition lookup
 //   z_v    = (base[b, k, v] + bias_v) * (1/T_b)
-//   x_k    ~ softmax(z) by Gumbel-max in two levels (T > 0): the 64-entry
-//            block with the largest log(mass) + G (tag 3) wins, then
-//            x_k = argmax over its entries of z_v + G_v (tag 0)
+//   x_k    = argmax_v z_v + G_v          (T > 0: Gumbel-max, one tag-0 draw per entry)
 //          = argmax_v base + bias        (T == 0)
 //   lse_d  = log sum_v exp(z_v),  log p_d(x_k) = z_{x_k} - lse_d
 //
 // Each position is two launches: a strip kernel that produces, per request and
 // vocabulary strip (or part of strips), an online-softmax partial with the best
-// block key (RowState), and a combine kernel that folds them into lse_d and the
-// winning block, draws x_k inside that block and writes log p_d.  The strip
-// kernel exists in two forms: a VALU form for any factor dtype and rank, and an
-// MFMA form (draft_mfma.hip) for bf16 factors.
+// entry key (RowState), and a combine kernel that folds them into lse_d and
+// x_k and writes log p_d.  The strip kernel exists in two forms: a VALU form
+// for any factor dtype and rank, and an MFMA form (draft_mfma.hip) for bf16
+// factors.  Keys are base 2: s c - log2(-log2 u) with c = log2(e) / T orders
+// entries as z + G does (KeyLane).
 #include <algorithm>
-#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -30,6 +28,7 @@ constexpr int kValuRows = 8;  // requests per workgroup of the VALU strip kernel
 // VALU strip kernel: workgroup = (8 requests) x (1024 vocabulary entries); each
 // thread owns 4 consecutive entries (one Philox block) for all 8 requests and
 // accumulates their transition bias in fp32 from factor rows staged in LDS.
+// The partial's key is the best entry key, its index that entry.
 template <typename LT, typename FT>
 __global__ __launch_bounds__(256) void draft_strip_valu(
     const LT* __restrict__ base, const FT* __restrict__ A, const FT* __restrict__ W,
@@ -86,9 +85,9 @@ __global__ __launch_bounds__(256) void draft_strip_valu(
         for (int t = 0; t < 4; ++t)
             s[t] = (v0 + t < V) ? to_f32(br[t]) + acc[g][t] : -INFINITY;
         if (T > 0.0f) {
-            // the thread's softmax partial over its 4 entries, then the key of
-            // its draft block (16 consecutive threads hold the block's 64
-            // entries): log of the block mass plus the block's Gumbel
+            // the thread's softmax partial over its 4 entries (on the z scale)
+            // and the best of their keys s c - log2(-log2 u) (one Philox block)
+            const KeyLane kl = key_lane(T);
             const float it = inv_temperature(T);
             float m = -INFINITY;
 #pragma unroll
@@ -101,31 +100,22 @@ __global__ __launch_bounds__(256) void draft_strip_valu(
             }
             st.m = m;
             st.s = sum;
-            float bm = m, bs = sum;
+            if (v0 < V) {
+                const u32x4 rnd = philox_block(seed, b, k + 1, kTagDraft, v0 >> 2);
 #pragma unroll
-            for (int o = 1; o < kDraftBlock / 4; o <<= 1) {
-                const float om = __shfl_xor(bm, o, kWave);
-                const float os = __shfl_xor(bs, o, kWave);
-                const float mm = fmaxf(bm, om);
-                if (mm != -INFINITY) {
-                    bs = ((bm == -INFINITY) ? 0.0f : bs * expf(bm - mm)) +
-                         ((om == -INFINITY) ? 0.0f : os * expf(om - mm));
-                    bm = mm;
+                for (int t = 0; t < 4; ++t) {
+                    const float key = fmaf(s[t], kl.c2, -entry_l2(pick(rnd, t), kl));
+                    if (v0 + t < V && key > st.pert) {
+                        st.pert = key;
+                        st.idx = v0 + t;
+                    }
                 }
-            }
-            if (bm != -INFINITY) {
-                const int blk = v0 / kDraftBlock;
-                const u32x4 rnd = philox_block(seed, b, k + 1, kTagDraftBlock, blk >> 2);
-                st.pert = bm + logf(bs) + gumbel_of(pick(rnd, blk & 3));
-                st.zb = 0.0f;
-                st.idx = blk * kDraftBlock;
             }
         } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 if (v0 + t < V && beats(s[t], v0 + t, st.pert, st.idx)) {
                     st.pert = s[t];
-                    st.zb = s[t];
                     st.idx = v0 + t;
                 }
             }
@@ -142,61 +132,26 @@ __global__ __launch_bounds__(256) void draft_strip_valu(
     }
 }
 
-__device__ __forceinline__ uint32_t dword_of4(const uint4& q, int i) {
-    return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
-}
-
-// One step of a wavefront argmax (largest key, smallest entry on ties) that
-// carries a value with the winner; see xlane.
-template <int STEP>
-__device__ __forceinline__ void argmax_step(float& key, int& idx, float& val) {
-    const float ok = xlane_f<STEP>(key);
-    const int oi = xlane_i<STEP>(idx);
-    const float ov = xlane_f<STEP>(val);
-    if (beats(ok, oi, key, idx)) {
-        key = ok;
-        idx = oi;
-        val = ov;
-    }
-}
-
-// Fold the partials of each row and draw its token (one wavefront per row,
-// one wavefront per workgroup, so that the rows spread over every CU's memory
-// pipeline).  Rows are requests at step k (k >= 0: partial row
-// b, output b K + k, previous token prev[b prev_stride]) or, for parallel
-// drafting (k < 0, no factors), every (request, position) row q = b K + k'.
-// T == 0: the partial's argmax.  T > 0: the partial's winner is a draft block;
-// the token is the Gumbel-argmax of z = (base + bias) / T over its 64 entries
-// with the tag-0 draws (base-2 keys s c - log2(-log2 u), c = log2(e) / T, which
-// order entries as z + G does).  Lane j holds entry block start + j; the bias
-// of the block's entries is recomputed here (for bf16 factors with 16-byte
-// aligned rows: lane 8 c + p sums ranks p r/8 .. (p+1) r/8 - 1 for entries
-// 8 c .. 8 c + 7 with 16-byte loads, then the 8 rank groups are added across
-// lanes; PER = r / 8 fixed at compile time lets every load be issued before
-// the first is used).  Writes x, lse_d = m + log s (the row maximum for T == 0)
-// and log p_d(x) = z_x - lse_d (0 for T == 0).
-template <typename LT, typename FT, int PER>
+// Fold the partials of each row into its token (one wavefront per row, one
+// wavefront per workgroup, so that the rows spread over every CU's memory
+// pipeline).  Rows are requests at step k (k >= 0: partial row b, output
+// b K + k) or, for parallel drafting (k < 0, no factors), every (request,
+// position) row q = b K + k'.  The winner of the merged partials is x_k (the
+// largest key, smallest entry on ties).  T == 0: its key is the logit, so
+// lse_d is the row maximum and log p_d = 0.  T > 0: lse_d = m + log s, and
+// z_x log2(e) = key + log2(-log2 u_x), the winner's own draw recomputed here
+// (the key is that sum rounded once), so log p_d = z_x - lse_d needs no logit
+// or bias load.
 __global__ __launch_bounds__(kWave) void draft_combine(
-    PartialBuf part, int n_parts, const LT* __restrict__ base, const FT* __restrict__ A,
-    const FT* __restrict__ W, const int32_t* __restrict__ prev, int prev_stride,
-    const float* __restrict__ temperature, uint64_t seed, int n_rows, int K, int V, int r, int k,
-    bool vec_ok, int32_t* __restrict__ tokens, float* __restrict__ logp, float* __restrict__ lse) {
+    PartialBuf part, int n_parts, const float* __restrict__ temperature, uint64_t seed,
+    int n_rows, int K, int k, int32_t* __restrict__ tokens, float* __restrict__ logp,
+    float* __restrict__ lse) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x;
     if (row >= n_rows) return;  // whole wavefront
     const int b = (k >= 0) ? row : row / K;
     const int pos = (k >= 0) ? k + 1 : row % K + 1;
     const size_t o = (k >= 0) ? static_cast<size_t>(b) * K + k : static_cast<size_t>(row);
-    const int c = lane >> 3, g = lane & 7;
-    // the factor slice of this lane's rank group does not depend on the merge
-    constexpr bool kFast = PER > 0 && std::is_same<FT, bf16_t>::value;
-    uint4 afr[kFast ? PER / 8 : 1];
-    if (kFast && A != nullptr) {
-        const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
-        const uint4* ap = reinterpret_cast<const uint4*>(A + static_cast<size_t>(p) * r + g * PER);
-#pragma unroll
-        for (int j = 0; j < PER / 8; ++j) afr[j] = ap[j];
-    }
     RowState st = row_empty();
     {
         const size_t pr = static_cast<size_t>(row) * n_parts;
@@ -211,107 +166,23 @@ __global__ __launch_bounds__(kWave) void draft_combine(
         for (; s < n_parts; s += kWave) row_merge(st, load_partial(part, pr + s));
     }
     wave_reduce_row(st);  // every lane holds the row's state
+    if (lane != 0) return;
     const float T = temperature[b];
+    tokens[o] = st.idx;
     if (!(T > 0.0f)) {
-        if (lane == 0) {
-            tokens[o] = st.idx;
-            if (lse) lse[o] = st.pert;
-            if (logp) logp[o] = 0.0f;
-        }
+        if (lse) lse[o] = st.pert;
+        if (logp) logp[o] = 0.0f;
         return;
     }
     const float l = st.m + logf(st.s);
-    const int v0 = min(max(st.idx, 0), V - 1) & ~(kDraftBlock - 1);  // winning block
-    const int v = v0 + lane;
-    float bias = 0.0f;
-    if constexpr (kFast) {
-        if (A != nullptr) {
-            // bf16 factors, r = 8 PER, V % 8 == 0, 16-byte aligned A and W
-            const int vc = min(v0 + 8 * c, V - 8);  // entries past V are never drawn
-            uint4 w8[kFast ? PER : 1];
-#pragma unroll
-            for (int j = 0; j < PER; ++j)
-                w8[j] = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(g * PER + j) * V +
-                                                        vc);
-            float part8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const uint32_t ad = dword_of4(afr[j >> 3], (j & 7) >> 1);
-                const float a = __uint_as_float((j & 1) ? (ad & 0xFFFF0000u) : (ad << 16));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t dw = dword_of4(w8[j], e >> 1);
-                    part8[e] = fmaf(a, __uint_as_float((e & 1) ? (dw & 0xFFFF0000u) : (dw << 16)),
-                                    part8[e]);
-                }
-            }
-            // sum over the 8 lanes of the rank groups (lanes 8 c .. 8 c + 7)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<0>(part8[e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<1>(part8[e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<2>(part8[e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (e == g) bias = part8[e];
-        }
-    } else if (A != nullptr) {
-        const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
-        const FT* arow = A + static_cast<size_t>(p) * r;
-        if (vec_ok) {
-            // 16-byte rows: r % 8 == 0, V % 8 == 0, 16-byte aligned A and W
-            const int per = r >> 3;
-            const int vc = min(v0 + 8 * c, V - 8);  // entries past V are never drawn
-            float part8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            for (int i = g * per; i < (g + 1) * per; ++i) {
-                const float a = to_f32(arow[i]);
-                const uint4 w8 = *reinterpret_cast<const uint4*>(W + static_cast<size_t>(i) * V + vc);
-                const uint32_t d[4] = {w8.x, w8.y, w8.z, w8.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t dw = d[e >> 1];
-                    part8[e] = fmaf(a, __uint_as_float((e & 1) ? (dw & 0xFFFF0000u) : (dw << 16)),
-                                    part8[e]);
-                }
-            }
-            // sum over the 8 lanes of the rank groups (lanes 8 c .. 8 c + 7)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<0>(part8[e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<1>(part8[e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part8[e] += xlane_f<2>(part8[e]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (e == g) bias = part8[e];
-        } else if (v < V) {
-            for (int i = 0; i < r; ++i)
-                bias = fmaf(to_f32(arow[i]), to_f32(W[static_cast<size_t>(i) * V + v]), bias);
-        }
-    }
-    const float it = inv_temperature(T);
-    float key = -INFINITY, sv = 0.0f;
-    if (v < V) {
-        sv = to_f32(base[o * V + v]) + bias;
-        const u32x4 rnd = philox_block(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(pos),
-                                       kTagDraft, static_cast<uint32_t>(v) >> 2);
-        const float l1 = __builtin_amdgcn_logf(uniform_of(pick(rnd, v & 3)));
-        key = sv * (it * kLog2e) - __builtin_amdgcn_logf(-l1);
-    }
-    // wave argmax, smallest entry on ties
-    int bv = (v < V) ? v : 0x7fffffff;
-    float bsv = sv;
-    argmax_step<0>(key, bv, bsv);
-    argmax_step<1>(key, bv, bsv);
-    argmax_step<2>(key, bv, bsv);
-    argmax_step<3>(key, bv, bsv);
-    argmax_step<4>(key, bv, bsv);
-    argmax_step<5>(key, bv, bsv);
-    if (lane == 0) {
-        tokens[o] = bv;
-        if (lse) lse[o] = l;
-        if (logp) logp[o] = bsv * it - l;
+    if (lse) lse[o] = l;
+    if (logp) {
+        const KeyLane kl = key_lane(T);
+        const uint32_t x = static_cast<uint32_t>(st.idx);
+        const u32x4 rnd =
+            philox_block(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(pos), kTagDraft,
+                         x >> 2);
+        logp[o] = (st.pert + entry_l2(pick(rnd, static_cast<int>(x & 3u)), kl)) * kLn2 - l;
     }
 }
 
@@ -326,40 +197,16 @@ void launch_valu_strip(const DraftArgs& a, const int32_t* prev, int prev_stride,
                        a.K, a.V, a.r, k, part, n_strips);
 }
 
-bool aligned16_ptr(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-template <typename LT, typename FT>
-void launch_combine_t(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k,
-                      const int32_t* prev, int prev_stride) {
-    const bool vec_ok = a.A != nullptr && a.factor_dt == DSPARK_BF16 && a.r % 8 == 0 &&
-                        a.V % 8 == 0 && aligned16_ptr(a.A) && aligned16_ptr(a.W);
-    const dim3 grid(static_cast<unsigned>(n_rows));
-    if (vec_ok && a.r == 256 && std::is_same<FT, bf16_t>::value)
-        hipLaunchKernelGGL((draft_combine<LT, FT, 32>), grid, dim3(kWave), 0, a.stream, part,
-                           n_parts, static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
-                           static_cast<const FT*>(a.W), prev, prev_stride, a.temperature, a.seed,
-                           n_rows, a.K, a.V, a.r, k, vec_ok, a.tokens, a.logp, a.lse);
-    else
-        hipLaunchKernelGGL((draft_combine<LT, FT, 0>), grid, dim3(kWave), 0, a.stream, part,
-                           n_parts, static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
-                           static_cast<const FT*>(a.W), prev, prev_stride, a.temperature, a.seed,
-                           n_rows, a.K, a.V, a.r, k, vec_ok, a.tokens, a.logp, a.lse);
+void launch_combine(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k) {
+    hipLaunchKernelGGL(draft_combine, dim3(static_cast<unsigned>(n_rows)), dim3(kWave), 0,
+                       a.stream, part, n_parts, a.temperature, a.seed, n_rows, a.K, k, a.tokens,
+                       a.logp, a.lse);
 }
 
 }  // namespace
 
-hipError_t launch_draft_combine(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k,
-                                const int32_t* prev, int prev_stride) {
-    const bool lb = a.logit_dt == DSPARK_BF16;
-    const bool fb = a.A == nullptr || a.factor_dt == DSPARK_BF16;
-    if (lb && fb)
-        launch_combine_t<bf16_t, bf16_t>(a, part, n_parts, n_rows, k, prev, prev_stride);
-    else if (lb)
-        launch_combine_t<bf16_t, float>(a, part, n_parts, n_rows, k, prev, prev_stride);
-    else if (fb)
-        launch_combine_t<float, bf16_t>(a, part, n_parts, n_rows, k, prev, prev_stride);
-    else
-        launch_combine_t<float, float>(a, part, n_parts, n_rows, k, prev, prev_stride);
+hipError_t launch_draft_combine(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k) {
+    launch_combine(a, part, n_parts, n_rows, k);
     return hipGetLastError();
 }
 
@@ -451,7 +298,7 @@ hipError_t launch_draft(const DraftArgs& a) {
         prof_end(strip_scope.slot, a.stream);
         strip_scope.slot = -1;
         ProfScope combine_scope(DSPARK_KERNEL_DRAFT_COMBINE, a.stream);
-        e = launch_draft_combine(a, ws.part, n_parts, a.B, k, prev, prev_stride);
+        e = launch_draft_combine(a, ws.part, n_parts, a.B, k);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -167,100 +167,96 @@ __device__ __forceinline__ void bias_tiles(f32x16 (&acc)[4], const uint16_t* w_s
 }
 
 // ------------------------------------------------------------------ draft
-// Key of the 64-entry draft block whose entries lanes l and l ^ 32 share (32
-// each): each lane's base-2 log-mass is mcb + log2(sum) (mcb = -inf: the lane
-// holds no entry below V); the block's log2-mass plus its base-2 Gumbel.
-// The pair exchanges its partials with gfx950's lane swap (no LDS round
-// trip): afterwards every lane holds the values of lanes l % 32 and l % 32 + 32,
-// in that order, so both lanes of the pair compute the same key.
-__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                    false, false);
-    lo = __uint_as_float(r[0]);
-    hi = __uint_as_float(r[1]);
+// Running state of a lane over the entries it visits: the online-softmax
+// partial in base 2 (m2 = the largest s c2 seen, s = sum of 2^(s c2 - m2)) and
+// the best entry key (s c2 - log2(-log2 u), see KeyLane) with its entry.  A
+// greedy lane's key is its logit, and its softmax fields are unused.  lane_row
+// turns the state into the row partial the combine merges (m on the z scale;
+// zb is not carried: the combine recovers z of the winner from its key).
+struct LaneRun {
+    float m2;
+    float s;
+    float key;
+    int idx;
+};
+
+__device__ __forceinline__ LaneRun lane_empty() { return {-INFINITY, 0.0f, -INFINITY, 0x7fffffff}; }
+
+__device__ __forceinline__ RowState lane_row(const LaneRun& r) {
+    return {r.m2 == -INFINITY ? -INFINITY : r.m2 * kLn2, r.s, r.key, 0.0f, r.idx};
 }
 
-__device__ __forceinline__ float block_key2(float mcb, float sum, uint32_t word) {
-    float m0, m1, s0, s1;
-    lane_pair(mcb, m0, m1);
-    lane_pair(sum, s0, s1);
-    const float M = fmaxf(m0, m1);
-    if (M == -INFINITY) return -INFINITY;
-    const float S = (m0 == -INFINITY ? 0.0f : s0 * __builtin_amdgcn_exp2f(m0 - M)) +
-                    (m1 == -INFINITY ? 0.0f : s1 * __builtin_amdgcn_exp2f(m1 - M));
-    return M + __builtin_amdgcn_logf(S) + block_gumbel2(word);
+// Fold a chunk's softmax partial (chunk maximum mx of s, sum of 2^(s c2 - mc)
+// with mc = mx c2, or mx = -inf for a chunk with no entry below V) and its best
+// key into the lane state.  Chunks arrive in increasing entry order, so a
+// strict comparison keeps the smallest entry on ties.
+__device__ __forceinline__ void fold_chunk(LaneRun& run, float mx, float mc, float sum, float hb,
+                                           int hi) {
+    const float mh = (mx == -INFINITY) ? -INFINITY : mc;
+    const float M = fmaxf(run.m2, mh);
+    if (M != -INFINITY) {
+        // exp2(-inf) = 0 drops a side that holds no entry yet
+        run.s = run.s * __builtin_amdgcn_exp2f(run.m2 - M) + sum * __builtin_amdgcn_exp2f(mh - M);
+        run.m2 = M;
+    }
+    if (hb > run.key) {
+        run.key = hb;
+        run.idx = hi;
+    }
 }
 
-// Epilogue of one lane (one request, 64 entries vh + entry_of(i, t)): the
-// accumulators become s = base + bias (-inf past V).  For T > 0 the strip is
-// two draft blocks of 64 entries, half of each in this lane and half in lane
-// l ^ 32; per block the lane forms its softmax partial (max and sum of
-// exp((s - max) / T), on the z = s / T scale), the pair merges the two halves
-// into the block's log-mass, and the block key log2(mass) + base-2 Gumbel
-// (tag 3) competes in the running state with the block start as index.  With
-// c = log2(e) / T the block log2-mass is m c + log2(sum of 2^((s - m) c)), so
-// key = log2(e) (log mass + G) + log2(e) ln ln 2: it orders blocks as the
-// natural-log form does.  The combine step draws the entry inside the winning
-// block.  For T == 0 the lane keeps the argmax of s, visiting entries in
-// increasing v so that a strict comparison keeps the smallest index.
-__device__ __forceinline__ RowState draft_epilogue(f32x16 (&acc)[4], const uint4 (&bl)[8], int vh,
-                                                   float T, uint64_t seed, int b, uint32_t pos) {
-    const bool greedy = !(T > 0.0f);
-    // the lane's entries of draft block j (strip entries 64 j .. 64 j + 63) are
-    // accumulators i = 8 j .. 8 j + 7 of every tile
-    float mxb[2] = {-INFINITY, -INFINITY};
+// Epilogue of the runtime-rank kernel for one lane (one request, 64 entries
+// vh + entry_of(i, t)): s = base + bias (-inf past V), then per entry the
+// softmax term and the key (KeyLane); the four tiles of accumulator i are the
+// four consecutive entries of one Philox block.  A greedy lane only takes the
+// argmax of s.
+__device__ __forceinline__ void draft_epilogue(LaneRun& run, f32x16 (&acc)[4], const uint4 (&bl)[8],
+                                               int vh, bool greedy, const KeyLane& kl,
+                                               const PhiloxRow& ph) {
+    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float sv = logit_at(bl, i, t) + acc[t][i];
             acc[t][i] = sv;
-            mxb[i >> 3] = fmaxf(mxb[i >> 3], sv);
+            mx = fmaxf(mx, sv);
         }
     }
-    RowState st = row_empty();
-    if (!greedy) {
-        const float it = inv_temperature(T);
-        const float c2 = it * kLog2e;
-        // the strip's blocks 2 s' and 2 s' + 1 share Philox counter s' / 2
-        const u32x4 rb = block_draws(seed, b, pos, vh >> 6);
+    float hb = -INFINITY;
+    int hi = 0;
+    if (greedy) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            // a lane of the tail strip may hold no entry below V (mx = -inf)
-            const float mx = mxb[j];
-            const float mc = (mx == -INFINITY) ? 0.0f : mx * c2;
-            float sum = 0.0f;
+        for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int i = 8 * j; i < 8 * j + 8; ++i)
-#pragma unroll
-                for (int t = 0; t < 4; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, -mc));
-            RowState sb;
-            sb.m = mx * it;
-            sb.s = sum;
-            sb.pert = block_key2((mx == -INFINITY) ? -INFINITY : mc, sum,
-                                 pick(rb, ((vh >> 6) + j) & 3));
-            sb.zb = 0.0f;
-            sb.idx = (vh & ~(kDraftBlock - 1)) + kDraftBlock * j;
-            row_merge(st, sb);
-        }
-    } else {
-        float best = -INFINITY;
-        int be = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (acc[t][i] > best) {
-                    best = acc[t][i];
-                    be = entry_of(i, t);
+            for (int t = 0; t < 4; ++t)
+                if (acc[t][i] > hb) {
+                    hb = acc[t][i];
+                    hi = entry_of(i, t);
                 }
+        if (hb > run.key) {
+            run.key = hb;
+            run.idx = vh + hi;
+        }
+        return;
+    }
+    const float mc = (mx == -INFINITY) ? 0.0f : mx * kl.c2;
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const u32x4 rnd = philox_row_block(ph, static_cast<uint32_t>((vh + entry_of(i, 0)) >> 2));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float sv = acc[t][i];
+            sum += __builtin_amdgcn_exp2f(fmaf(sv, kl.c2, -mc));
+            const float key = fmaf(sv, kl.c2, -entry_l2(pick(rnd, t), kl));
+            if (key > hb) {
+                hb = key;
+                hi = entry_of(i, t);
             }
         }
-        st.pert = best;
-        st.zb = best;
-        st.idx = vh + be;
     }
-    return st;
+    fold_chunk(run, mx, mc, sum, hb, vh + hi);
 }
 
 // One workgroup per (part, request group), persistent over the strips
@@ -285,6 +281,10 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
     const int b = active ? order[slot] : 0;
     const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
     const float T = temperature[b];
+    const bool greedy = !(T > 0.0f);
+    const KeyLane kl = key_lane(T);
+    const PhiloxRow ph = philox_row(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(k + 1),
+                                    kTagDraft);
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
     const uint16_t* brow = base + (static_cast<size_t>(b) * K + k) * V;
     const int buf_elems = r * kPitch;
@@ -293,7 +293,7 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
     stage_w<NWAVES>(w_sh, W, r, V, s * kStripV);
     uint4 bl[8];
     load_lane_logits(bl, brow, s * kStripV + 16 * kh, V, s * kStripV + kStripV > V);
-    RowState run = row_empty();
+    LaneRun lr = lane_empty();
     int buf = 0;
     for (;;) {
         // this strip's W (all waves' shares) and logits have landed, and every
@@ -314,7 +314,7 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
             load_lane_logits(bn, brow, sn * kStripV + 16 * kh, V, sn * kStripV + kStripV > V);
         }
         // lane entries: strip start + 16 kh + entry_of(i, t)
-        row_merge(run, draft_epilogue(acc, bl, s * kStripV + 16 * kh, T, seed, b, k + 1));
+        draft_epilogue(lr, acc, bl, s * kStripV + 16 * kh, greedy, kl, ph);
         if (!more) break;
 #pragma unroll
         for (int c = 0; c < 8; ++c) bl[c] = bn[c];
@@ -322,6 +322,7 @@ void draft_strip_mfma(const uint16_t* __restrict__ base, const uint16_t* __restr
         s = sn;
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
+    RowState run = lane_row(lr);
     row_merge(run, xlane_row<5>(run));
     if (active && kh == 0)
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
@@ -478,78 +479,64 @@ __device__ __forceinline__ void logit_tail(uint4 (&q)[8], int v0, int kh, int V)
     }
 }
 
-// Running state of a lane over the halves and strips it visits.  Sampled
-// (T > 0): the online-softmax partial of the lane's own entries in base 2 (m2 =
-// the largest z log2(e) seen, s = the sum of 2^(z log2(e) - m2)) and the best
-// draft-block key with its block start.  Greedy (T == 0): the largest logit
-// (key) and its entry.  lane_row turns it into the row state the combine
-// merges (m on the z scale).
-struct LaneRun {
-    float m2;
-    float s;
-    float key;
-    int idx;
-};
-
-__device__ __forceinline__ LaneRun lane_empty() { return {-INFINITY, 0.0f, -INFINITY, 0x7fffffff}; }
-
-__device__ __forceinline__ RowState lane_row(const LaneRun& r, bool sampled) {
-    return {r.m2 == -INFINITY ? -INFINITY : r.m2 * kLn2, r.s, r.key, sampled ? 0.0f : r.key,
-            r.idx};
-}
-
-// One half (entries vh + offsets of acc_from_logits' layout) into the running
-// state.  acc holds s = base + bias; `word` is the tag-3 draw of its draft block.
-__device__ __forceinline__ void epilogue_half(LaneRun& run, const f32x16 (&acc)[2], int vh,
-                                              float T, uint32_t word) {
+// One half (entries vh + 16 a + 4 tt + w, with acc_from_logits' layout: run
+// a = i / 4, tt = t ^ (a % 2), w = i % 4) into the running state.  acc holds
+// s = base + bias.  Sampled form (any wavefront with a sampled lane): per entry
+// the softmax term and the key s c2 - log2(-log2 u) with its own tag-0 draw
+// (KeyLane: greedy lanes get the key s); the four entries w = 0..3 of one
+// (a, tt) are one Philox block.  Entries are visited in increasing order.
+__device__ __forceinline__ void sample_half(LaneRun& run, const f32x16 (&acc)[2], int vh,
+                                            const KeyLane& kl, const PhiloxRow& ph) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
         for (int t = 0; t < 2; ++t) mx = fmaxf(mx, acc[t][i]);
-    if (T > 0.0f) {
-        // sampled: this half is one draft block (entries vh & ~63 .. + 63, half
-        // of them in the partner lane); its key enters the running state with
-        // the block start as index, and the online-softmax sum covers the lane's
-        // own entries
-        const float c2 = inv_temperature(T) * kLog2e;
-        const float mc = (mx == -INFINITY) ? -INFINITY : mx * c2;
-        const float mr = (mx == -INFINITY) ? 0.0f : mc;
-        float sum = 0.0f;
+    const float mc = (mx == -INFINITY) ? 0.0f : mx * kl.c2;
+    float sum = 0.0f, hb = -INFINITY;
+    int hi = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+    for (int a = 0; a < 4; ++a) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[t][i], c2, -mr));
-        const float key = block_key2(mc, sum, word);
-        const int blk = vh & ~(kDraftBlock - 1);
-        const float M = fmaxf(run.m2, mc);
-        if (M != -INFINITY) {
-            // exp2(-inf) = 0 drops a side that holds no entry yet
-            run.s = run.s * __builtin_amdgcn_exp2f(run.m2 - M) + sum * __builtin_amdgcn_exp2f(mc - M);
-            run.m2 = M;
-        }
-        if (beats(key, blk, run.key, run.idx)) {
-            run.key = key;
-            run.idx = blk;
-        }
-    } else {
-        // the first entry (in increasing order) that holds the largest logit:
-        // entries 16 a + 4 tt + w, visited from the last one down
-        int be = 0;
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = tt ^ (a & 1);
+            const u32x4 rnd =
+                philox_row_block(ph, static_cast<uint32_t>(vh >> 2) + 4 * a + tt);
 #pragma unroll
-        for (int a = 3; a >= 0; --a) {
-#pragma unroll
-            for (int tt = 1; tt >= 0; --tt) {
-                const int t = tt ^ (a & 1);
-#pragma unroll
-                for (int w = 3; w >= 0; --w)
-                    if (acc[t][4 * a + w] == mx) be = 16 * a + 4 * tt + w;
+            for (int w = 0; w < 4; ++w) {
+                const float sv = acc[t][4 * a + w];
+                sum += __builtin_amdgcn_exp2f(fmaf(sv, kl.c2, -mc));
+                const float key = fmaf(sv, kl.c2, -entry_l2(pick(rnd, w), kl));
+                if (key > hb) {
+                    hb = key;
+                    hi = 16 * a + 4 * tt + w;
+                }
             }
         }
-        if (beats(mx, vh + be, run.key, run.idx)) {
-            run.key = mx;
-            run.idx = vh + be;
-        }
+    }
+    fold_chunk(run, mx, mc, sum, hb, vh + hi);
+}
+
+// Greedy form (every lane of the wavefront has T == 0): the first entry, in
+// increasing order, that holds the largest logit.
+__device__ __forceinline__ void greedy_half(LaneRun& run, const f32x16 (&acc)[2], int vh) {
+    float hb = -INFINITY;
+    int hi = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float sv = acc[tt ^ (a & 1)][4 * a + w];
+                if (sv > hb) {
+                    hb = sv;
+                    hi = 16 * a + 4 * tt + w;
+                }
+            }
+    if (hb > run.key) {
+        run.key = hb;
+        run.idx = vh + hi;
     }
 }
 
@@ -560,13 +547,14 @@ __device__ __forceinline__ void epilogue_half(LaneRun& run, const f32x16 (&acc)[
 // issues the MFMA loop without first waiting for the next strip's W (with one
 // dynamically indexed LDS array it has to wait for every outstanding direct
 // load before the first LDS read).  Returns false after the last strip.
-template <int NWAVES, int KS>
+template <int NWAVES, int KS, bool GREEDY>
 __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int& s, uint4 (&bl)[8],
                                          uint4 (&bn)[8], LaneRun& run,
                                          const uint16_t* __restrict__ W,
                                          const uint16_t* brow, const uint4 (&afr)[KS],
-                                         const int (&tro)[2][2], float T, uint64_t seed, int b,
-                                         int k, int V, int kh, int n_strips, int n_parts) {
+                                         const int (&tro)[2][2], const KeyLane& kl,
+                                         const PhiloxRow& ph, int V, int kh, int n_strips,
+                                         int n_parts) {
     // this strip's W (all waves' shares) and logits have landed, and every
     // wave is done with the other buffer
     __builtin_amdgcn_s_waitcnt(0);
@@ -578,9 +566,6 @@ __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int
         stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
         load_logit_chunks(bn, brow, sn * kStripV, kh, V, 0, 2);
     }
-    // draft blocks 2 s and 2 s + 1: words 2 (s % 2) and 2 (s % 2) + 1 of one
-    // Philox block
-    const u32x4 rb = block_draws(seed, b, k + 1, 2 * s);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         f32x16 acc[2];
@@ -588,7 +573,10 @@ __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int
         acc_from_logits(acc, half_of(bl, h));
         bias_half<KS>(acc, wt, afr);
         if (more) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 2 + 4 * h, 4 + 4 * h);
-        epilogue_half(run, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
+        if constexpr (GREEDY)
+            greedy_half(run, acc, s * kStripV + 64 * h + 8 * kh);
+        else
+            sample_half(run, acc, s * kStripV + 64 * h + 8 * kh, kl, ph);
         if (more && h == 0) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 4, 6);
     }
     if (!more) return false;
@@ -624,6 +612,11 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
     const int b = active ? order[slot] : 0;
     const int p = clamp_token(prev[static_cast<size_t>(b) * prev_stride], V);
     const float T = temperature[b];
+    const KeyLane kl = key_lane(T);
+    const PhiloxRow ph = philox_row(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(k + 1),
+                                    kTagDraft);
+    // one epilogue per wavefront: the greedy one when no lane samples
+    const bool wave_greedy = __all(!active || !(T > 0.0f));
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
     const uint16_t* brow = base + (static_cast<size_t>(b) * K + k) * V;
     uint4 afr[KS];  // r == 16 KS
@@ -638,13 +631,21 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
     load_strip_logits(bl0, brow, s * kStripV, kh, V);
     LaneRun lr = lane_empty();
     // strips alternate between w_a and w_b, and their logits between bl0 and bl1
-    while (rk_strip<NWAVES, KS>(w_a, w_b, s, bl0, bl1, lr, W, brow, afr, tro, T, seed, b, k, V,
-                                kh, n_strips, n_parts) &&
-           rk_strip<NWAVES, KS>(w_b, w_a, s, bl1, bl0, lr, W, brow, afr, tro, T, seed, b, k, V,
-                                kh, n_strips, n_parts)) {
+    if (wave_greedy) {
+        while (rk_strip<NWAVES, KS, true>(w_a, w_b, s, bl0, bl1, lr, W, brow, afr, tro, kl, ph, V,
+                                          kh, n_strips, n_parts) &&
+               rk_strip<NWAVES, KS, true>(w_b, w_a, s, bl1, bl0, lr, W, brow, afr, tro, kl, ph, V,
+                                          kh, n_strips, n_parts)) {
+        }
+    } else {
+        while (rk_strip<NWAVES, KS, false>(w_a, w_b, s, bl0, bl1, lr, W, brow, afr, tro, kl, ph,
+                                           V, kh, n_strips, n_parts) &&
+               rk_strip<NWAVES, KS, false>(w_b, w_a, s, bl1, bl0, lr, W, brow, afr, tro, kl, ph,
+                                           V, kh, n_strips, n_parts)) {
+        }
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
-    RowState run = lane_row(lr, T > 0.0f);
+    RowState run = lane_row(lr);
     row_merge(run, xlane_row<5>(run));
     if (active && kh == 0)
         store_partial(part, static_cast<size_t>(b) * n_parts + blockIdx.x, run);
@@ -653,8 +654,8 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
 // ------------------------------------------ parallel drafting (no Markov head)
 // With no transition factors the draft distribution of position k is
 // softmax(base_k / T) on its own, so all B K rows are drawn in one launch:
-// the same half-strip sampler (epilogue_half) on zero bias, lanes walking the
-// strips of their row.  Slot s is row (order[s / K], s % K); partials are
+// the same half-strip sampler (sample_half / greedy_half) on zero bias, lanes
+// walking the strips of their row.  Slot s is row (order[s / K], s % K); partials are
 // stored per row.
 template <int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES)
@@ -671,20 +672,26 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
     const int k = sl - (sl / K) * K;
     const int row = b * K + k;
     const float T = temperature[b];
+    const KeyLane kl = key_lane(T);
+    const PhiloxRow ph = philox_row(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(k + 1),
+                                    kTagDraft);
+    const bool wave_greedy = __all(!active || !(T > 0.0f));
     const uint16_t* brow = base + static_cast<size_t>(row) * V;
     LaneRun lr = lane_empty();
     for (int s = blockIdx.x; s < n_strips; s += n_parts) {
         uint4 bl[8];
         load_strip_logits(bl, brow, s * kStripV, kh, V);
-        const u32x4 rb = block_draws(seed, b, k + 1, 2 * s);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             f32x16 acc[2];
             acc_from_logits(acc, half_of(bl, h));
-            epilogue_half(lr, acc, s * kStripV + 64 * h + 8 * kh, T, pick(rb, 2 * (s & 1) + h));
+            if (wave_greedy)
+                greedy_half(lr, acc, s * kStripV + 64 * h + 8 * kh);
+            else
+                sample_half(lr, acc, s * kStripV + 64 * h + 8 * kh, kl, ph);
         }
     }
-    RowState run = lane_row(lr, T > 0.0f);
+    RowState run = lane_row(lr);
     row_merge(run, xlane_row<5>(run));
     if (active && kh == 0) store_partial(part, static_cast<size_t>(row) * n_parts + blockIdx.x, run);
 }
@@ -692,17 +699,21 @@ void draft_rows_parallel(const uint16_t* __restrict__ base, const float* __restr
 // --------------------------------------------------------------- residual
 // For every request whose first rejection is at j* = a_b + 1 (sampled, T > 0):
 // recompute the draft logits at j* (previous token x_{j*-1}), read the target
-// row, and make the first level of the draws from normalise(max(0, p_t - p_d))
-// and, as the fallback for a residual without positive mass, from p_t: per
-// 64-entry block the masses of max(0, p_t - p_d) and of p_t, and the block
-// keys log2 mass - log2(-log2 u) with the block's tag-4 draw (position j*).
-// verify_residual_combine then draws inside the winning block.  Rejected
-// requests are listed in `list` (count entries), and so are sampled requests
-// that accepted every drafted token: their bonus token is exactly that
-// fallback draw over row L_b + 1.  With c = log2(e) / T: a = log2 p_t =
-// t c - lse_t log2(e) and d = log2 p_d = s c - lse_d log2(e); the block keys
-// are log2(e) (log mass + G) up to a constant shared by the row, so they order
-// blocks as the natural-log forms do.
+// row, and draw from normalise(max(0, p_t - p_d)) and, as the fallback for a
+// residual without positive mass, from p_t: per entry the keys
+//   fallback  kf = log2 p_t - log2(-log2 u)
+//   residual  kr = kf + log2(1 - p_d / p_t)   (entries with p_t > p_d only)
+// with the entry's tag-2 draw at position j*, kept as two running argmaxes.
+// In base 2 with c = log2(e) / T: a = log2 p_t = t c - lse_t log2(e), and
+// dm = log2 p_d - log2 p_t = (s - t) c + (lse_t - lse_d) log2(e), formed from
+// the logit difference so that a target row equal to the draft row gives the
+// same dm for every such entry.  These keys are log2(e) (log r + G) and
+// log2(e) (y + G) up to constants shared by the row.  Rejected requests are
+// listed in `list` (count entries), and so are sampled requests that accepted
+// every drafted token: their bonus token is exactly the fallback draw over
+// row L_b + 1, and they take no residual key.
+// verify_residual_combine merges the partials into the next token.  The key
+// arithmetic is residual_entry (common.hpp).
 // Persistent like the draft kernel: one workgroup per (part, slot group) walks
 // the strips part, part + n_parts, ... with W double-buffered in LDS.
 template <int NWAVES>
@@ -736,9 +747,14 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     const int p = clamp_token((jd == 1) ? prev_token[b]
                                         : tokens[static_cast<size_t>(b) * K + jd - 2],
                               V);
-    const float c2 = inv_temperature(temperature[b]) * kLog2e;
-    const float ld2 = draft_lse[static_cast<size_t>(b) * K + jd - 1] * kLog2e;
-    const float lt2 = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1] * kLog2e;
+    const float T = temperature[b];
+    ResRow R;
+    R.c2 = inv_temperature(T) * kLog2e;
+    R.lt2 = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1] * kLog2e;
+    R.dl = R.lt2 - draft_lse[static_cast<size_t>(b) * K + jd - 1] * kLog2e;
+    R.bonus = bonus;
+    R.kl = key_lane(T);
+    R.ph = philox_row(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(js), kTagResample);
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
     const uint16_t* brow = base + (static_cast<size_t>(b) * K + jd - 1) * V;
     const uint16_t* trow = target + (row_off[b] + js - 1) * static_cast<int64_t>(V);
@@ -746,7 +762,7 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
 
     int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
     stage_w<NWAVES>(w_sh, W, r, V, s * kStripV);
-    RowState sr = row_empty(), sf = row_empty();
+    ResBest best = res_empty();
     int buf = 0;
     for (;;) {
         __builtin_amdgcn_s_waitcnt(0);  // this strip's W (all waves' shares) has landed
@@ -770,51 +786,23 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
         bias_tiles(acc, w_sh + buf * buf_elems, arow, r, lane);
         // requested after the MFMA loop's factor loads (in-order load counter)
         if (more) stage_w<NWAVES>(w_sh + (buf ^ 1) * buf_elems, W, r, V, sn * kStripV);
-        // the strip's two 64-entry blocks: accumulators 8 j .. 8 j + 7 of every
-        // tile hold this lane's 32 entries of block j (the partner lane l ^ 32
-        // holds the other 32); both blocks take words of one tag-4 draw block
-        const u32x4 rb = philox_block(seed, b, js, kTagVerifyBlock, s >> 1);
-        float br = -INFINITY, bf = -INFINITY;
-        int ir = 0x7fffffff, jf = 0x7fffffff;
+        // accumulator i of tile t is entry vh + entry_of(i, t); the four tiles
+        // of accumulator i are the four entries of one Philox block
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            // linear block masses of the residual max(0, p_t - p_d) and of p_t
-            // (entries past V have a = d = -inf and add nothing)
-            float mr = 0.0f, mf = 0.0f;
+        for (int i = 0; i < 16; ++i) {
+            const u32x4 rnd =
+                philox_row_block(R.ph, static_cast<uint32_t>((vh + entry_of(i, 0)) >> 2));
 #pragma unroll
-            for (int i = 8 * j; i < 8 * j + 8; ++i) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float d = fmaf(logit_at(bl, i, t) + acc[t][i], c2, -ld2);
-                    const float a = fmaf(logit_at(tl, i, t), c2, -lt2);
-                    const float pt = __builtin_amdgcn_exp2f(a);
-                    mr += fmaxf(pt - __builtin_amdgcn_exp2f(d), 0.0f);
-                    mf += pt;
-                }
-            }
-            float r0, r1, f0, f1;
-            lane_pair(mr, r0, r1);
-            lane_pair(mf, f0, f1);
-            const float g2 = block_gumbel2(pick(rb, 2 * (s & 1) + j));
-            const int blk = v0 + kDraftBlock * j;
-            const float mrb = r0 + r1, mfb = f0 + f1;
-            const float kr = (!bonus && mrb > 0.0f) ? __builtin_amdgcn_logf(mrb) + g2 : -INFINITY;
-            const float kf = (mfb > 0.0f) ? __builtin_amdgcn_logf(mfb) + g2 : -INFINITY;
-            if (kr > br) {
-                br = kr;
-                ir = blk;
-            }
-            if (kf > bf) {
-                bf = kf;
-                jf = blk;
-            }
+            for (int t = 0; t < 4; ++t)
+                residual_entry(best, logit_at(bl, i, t) + acc[t][i], logit_at(tl, i, t),
+                               pick(rnd, t), vh + entry_of(i, t), R);
         }
-        row_merge(sr, RowState{-INFINITY, 0.0f, br, br, ir});
-        row_merge(sf, RowState{-INFINITY, 0.0f, bf, bf, jf});
         if (!more) break;
         buf ^= 1;
         s = sn;
     }
+    RowState sr{-INFINITY, 0.0f, best.br, 0.0f, best.ir};
+    RowState sf{-INFINITY, 0.0f, best.bf, 0.0f, best.jf};
     row_merge(sr, xlane_row<5>(sr));
     row_merge(sf, xlane_row<5>(sf));
     if (active && kh == 0) {
@@ -906,52 +894,33 @@ __device__ __forceinline__ void tail_half(uint4 (&q)[4], int v0, int h, int kh, 
     }
 }
 
-// Block masses and keys of one half (one 64-entry block; see
-// residual_strip_mfma): acc holds s = base + bias, tq the target logits in the
-// same entry layout (acc_from_logits).
-__device__ __forceinline__ void residual_half(const f32x16 (&acc)[2], const uint4 (&tq)[4],
-                                              float c2, float ld2, float lt2, bool bonus,
-                                              uint32_t word, int blk, float& br, int& ir,
-                                              float& bf, int& jf) {
-    float mr = 0.0f, mf = 0.0f;
+// Keys of one half (see residual_strip_mfma): acc holds s = base + bias, tq
+// the target logits in the same entry layout (acc_from_logits): entry
+// vh + 16 a + 4 tt + w is accumulator 4 a + w of tile tt ^ (a % 2) and element
+// 4 tt + w of chunk a.
+__device__ __forceinline__ void residual_half(ResBest& rb, const f32x16 (&acc)[2],
+                                              const uint4 (&tq)[4], int vh, const ResRow& R) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int a = 0; a < 4; ++a) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint32_t dw = dword_of(tq[i >> 2], 2 * (t ^ ((i >> 2) & 1)) + ((i & 3) >> 1));
-            const float tv = __uint_as_float((i & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
-            const float d = fmaf(acc[t][i], c2, -ld2);
-            const float a = fmaf(tv, c2, -lt2);
-            const float pt = __builtin_amdgcn_exp2f(a);
-            mr += fmaxf(pt - __builtin_amdgcn_exp2f(d), 0.0f);
-            mf += pt;
+        for (int tt = 0; tt < 2; ++tt) {
+            const u32x4 rnd = philox_row_block(R.ph, static_cast<uint32_t>(vh >> 2) + 4 * a + tt);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t dw = dword_of(tq[a], 2 * tt + (w >> 1));
+                const float tv = __uint_as_float((w & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
+                residual_entry(rb, acc[tt ^ (a & 1)][4 * a + w], tv, pick(rnd, w),
+                               vh + 16 * a + 4 * tt + w, R);
+            }
         }
-    }
-    float r0, r1, f0, f1;
-    lane_pair(mr, r0, r1);
-    lane_pair(mf, f0, f1);
-    const float g2 = block_gumbel2(word);
-    const float mrb = r0 + r1, mfb = f0 + f1;
-    const float kr = (!bonus && mrb > 0.0f) ? __builtin_amdgcn_logf(mrb) + g2 : -INFINITY;
-    const float kf = (mfb > 0.0f) ? __builtin_amdgcn_logf(mfb) + g2 : -INFINITY;
-    if (kr > br) {
-        br = kr;
-        ir = blk;
-    }
-    if (kf > bf) {
-        bf = kf;
-        jf = blk;
     }
 }
 
 struct ResLane {
     const uint16_t* brow;
     const uint16_t* trow;
-    float c2, ld2, lt2;
-    bool bonus;
-    int b, js;
-    float br, bf;
-    int ir, jf;
+    ResRow R;
+    ResBest best;
 };
 
 // One strip: this strip's W is in `cur`, the next strip's goes into `nxt`;
@@ -962,8 +931,8 @@ __device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t*
                                                   uint4 (&b0)[4], uint4 (&t0)[4], ResLane& L,
                                                   const uint16_t* __restrict__ W,
                                                   const uint4 (&afr)[KS], const int (&tro)[2][2],
-                                                  uint64_t seed, int V, int kh, int n_strips,
-                                                  int n_parts, bool busy) {
+                                                  int V, int kh, int n_strips, int n_parts,
+                                                  bool busy) {
     // this strip's W (all waves' shares) and half-0 logits have landed, and
     // every wave is done with the other buffer
     __builtin_amdgcn_s_waitcnt(0);
@@ -984,7 +953,6 @@ __device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t*
     uint4 b1[4], t1[4];
     load_half(b1, L.brow, v0, 1, kh, V);  // before the next W: its wait does not include it
     if (more) stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
-    const u32x4 rb = philox_block(seed, L.b, L.js, kTagVerifyBlock, s >> 1);
     f32x16 acc[2];
     {
         const uint16_t* const wt[2] = {cur + tro[0][0], cur + tro[0][1]};
@@ -992,8 +960,7 @@ __device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t*
         bias_half<KS>(acc, wt, afr);
     }
     if (more) load_half(b0, L.brow, sn * kStripV, 0, kh, V);
-    residual_half(acc, t0, L.c2, L.ld2, L.lt2, L.bonus, pick(rb, 2 * (s & 1)), v0, L.br, L.ir,
-                  L.bf, L.jf);
+    residual_half(L.best, acc, t0, v0 + 8 * kh, L.R);
     load_half(t1, L.trow, v0, 1, kh, V);
     if (more) load_half(t0, L.trow, sn * kStripV, 0, kh, V);
     tail_half(b1, v0, 1, kh, V);
@@ -1003,8 +970,7 @@ __device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t*
         bias_half<KS>(acc, wt, afr);
     }
     tail_half(t1, v0, 1, kh, V);
-    residual_half(acc, t1, L.c2, L.ld2, L.lt2, L.bonus, pick(rb, 2 * (s & 1) + 1),
-                  v0 + kDraftBlock, L.br, L.ir, L.bf, L.jf);
+    residual_half(L.best, acc, t1, v0 + 64 + 8 * kh, L.R);
     if (!more) return false;
     s = sn;
     return true;
@@ -1033,23 +999,24 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     const bool busy = slot0 + (threadIdx.x >> 6) * 32 < count;
     // lanes past the list run request list[0]'s rows and store nothing
     ResLane L;
-    L.b = list[active ? slot : 0];
-    L.js = accepted[L.b] + 1;
+    const int b = list[active ? slot : 0];
+    const int js = accepted[b] + 1;
     // js > L_b: a listed full acceptance (its bonus is the fallback draw over
     // row L_b + 1); its draft side reads row 1 as an in-range stand-in
-    L.bonus = L.js > (lengths ? clamp_len(lengths[L.b], K) : K);
-    const int jd = L.bonus ? 1 : L.js;
-    const int p = clamp_token(
-        (jd == 1) ? prev_token[L.b] : tokens[static_cast<size_t>(L.b) * K + jd - 2], V);
-    L.c2 = inv_temperature(temperature[L.b]) * kLog2e;
-    L.ld2 = draft_lse[static_cast<size_t>(L.b) * K + jd - 1] * kLog2e;
-    L.lt2 = lse_tab[static_cast<size_t>(L.b) * (K + 1) + L.js - 1] * kLog2e;
-    L.brow = base + (static_cast<size_t>(L.b) * K + jd - 1) * V;
-    L.trow = target + (row_off[L.b] + L.js - 1) * static_cast<int64_t>(V);
-    L.br = -INFINITY;
-    L.bf = -INFINITY;
-    L.ir = 0x7fffffff;
-    L.jf = 0x7fffffff;
+    const bool bonus = js > (lengths ? clamp_len(lengths[b], K) : K);
+    const int jd = bonus ? 1 : js;
+    const int p =
+        clamp_token((jd == 1) ? prev_token[b] : tokens[static_cast<size_t>(b) * K + jd - 2], V);
+    const float T = temperature[b];
+    L.R.c2 = inv_temperature(T) * kLog2e;
+    L.R.lt2 = lse_tab[static_cast<size_t>(b) * (K + 1) + js - 1] * kLog2e;
+    L.R.dl = L.R.lt2 - draft_lse[static_cast<size_t>(b) * K + jd - 1] * kLog2e;
+    L.R.bonus = bonus;
+    L.R.kl = key_lane(T);
+    L.R.ph = philox_row(seed, static_cast<uint32_t>(b), static_cast<uint32_t>(js), kTagResample);
+    L.brow = base + (static_cast<size_t>(b) * K + jd - 1) * V;
+    L.trow = target + (row_off[b] + js - 1) * static_cast<int64_t>(V);
+    L.best = res_empty();
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
     uint4 afr[KS];
     uint4 b0[4], t0[4];
@@ -1065,17 +1032,19 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
         load_half(b0, L.brow, s * kStripV, 0, kh, V);
         load_half(t0, L.trow, s * kStripV, 0, kh, V);
     }
-    while (residual_rk_strip<NWAVES, KS>(w_a, w_b, s, b0, t0, L, W, afr, tro, seed, V, kh,
-                                         n_strips, n_parts, busy) &&
-           residual_rk_strip<NWAVES, KS>(w_b, w_a, s, b0, t0, L, W, afr, tro, seed, V, kh,
-                                         n_strips, n_parts, busy)) {
+    while (residual_rk_strip<NWAVES, KS>(w_a, w_b, s, b0, t0, L, W, afr, tro, V, kh, n_strips,
+                                         n_parts, busy) &&
+           residual_rk_strip<NWAVES, KS>(w_b, w_a, s, b0, t0, L, W, afr, tro, V, kh, n_strips,
+                                         n_parts, busy)) {
     }
-    // both lanes of a pair hold the same keys
+    // lanes l and l + 32 hold the two halves of every strip for one request
+    RowState sr{-INFINITY, 0.0f, L.best.br, 0.0f, L.best.ir};
+    RowState sf{-INFINITY, 0.0f, L.best.bf, 0.0f, L.best.jf};
+    row_merge(sr, xlane_row<5>(sr));
+    row_merge(sf, xlane_row<5>(sf));
     if (active && kh == 0) {
-        store_partial(res, static_cast<size_t>(slot) * n_parts + blockIdx.x,
-                      RowState{-INFINITY, 0.0f, L.br, L.br, L.ir});
-        store_partial(fall, static_cast<size_t>(slot) * n_parts + blockIdx.x,
-                      RowState{-INFINITY, 0.0f, L.bf, L.bf, L.jf});
+        store_partial(res, static_cast<size_t>(slot) * n_parts + blockIdx.x, sr);
+        store_partial(fall, static_cast<size_t>(slot) * n_parts + blockIdx.x, sf);
     }
 }
 
@@ -1217,7 +1186,7 @@ hipError_t launch_draft_parallel(const DraftArgs& a, PartialBuf part, size_t par
                        a.temperature, order, a.seed, a.B, a.K, a.V, part, n_strips, parts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_draft_combine(a, part, parts, static_cast<int>(rows), -1, nullptr, 0);
+    return launch_draft_combine(a, part, parts, static_cast<int>(rows), -1);
 }
 
 bool mfma_supported(const DraftArgs& a) {

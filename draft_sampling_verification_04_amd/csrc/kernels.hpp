@@ -60,11 +60,10 @@ size_t draft_workspace_bytes(int B, int K, int V, int r);
 bool draft_uses_mfma(const DraftArgs& a);
 bool parallel_supported(const DraftArgs& a);
 hipError_t launch_draft(const DraftArgs& a);
-// Fold the per-row partials and draw each row's token (draft.hip): k >= 0 is
-// step k of the Markov head (rows = requests, previous tokens prev[b
-// prev_stride]); k < 0 is parallel drafting (rows = B K, no factors).
-hipError_t launch_draft_combine(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k,
-                                const int32_t* prev, int prev_stride);
+// Fold the per-row partials into each row's token (draft.hip): k >= 0 is step
+// k of the Markov head (rows = requests); k < 0 is parallel drafting (rows =
+// B K, no factors).
+hipError_t launch_draft_combine(const DraftArgs& a, PartialBuf part, int n_parts, int n_rows, int k);
 
 struct VerifyArgs {
     const int32_t* tokens;

@@ -8,23 +8,24 @@
 //   accept x_j  iff  log u_j < log p_t(x_j) - log p_d(x_j)   (T > 0)
 //               iff  x_j == argmax t_j                        (T == 0)
 //   a_b = leading accepts;  a_b < L_b: next ~ normalise(max(0, p_t - p_d)) at
-//   j* = a_b + 1 (Gumbel-max over log of the positive residual, falling back to
-//   p_t when no residual mass is left);  a_b = L_b: next ~ p_t of row L_b + 1.
+//   j* = a_b + 1 (Gumbel-max over log of the positive residual entries, falling
+//   back to p_t when no residual mass is left);  a_b = L_b: next ~ p_t of row
+//   L_b + 1.  Every draw takes one tag-2 Philox draw per vocabulary entry.
 //
 // Launches: (1) one workgroup per (request, row) streams the target row once
-// with 16-byte loads: log-normaliser, accept bit, argmax, and the bonus
-// Gumbel-max on row L_b + 1; (2) one thread per request finds the first
-// rejection and lists the requests that need a residual draw; (3) the listed
-// requests recompute their draft row at j* (rank-r bias on MFMA for bf16, VALU
-// otherwise) and stream the target row j* again, split in vocabulary strips;
-// (4) the strips are folded into the next token.
+// with 16-byte loads: log-normaliser, accept bit, argmax, and (when no residual
+// kernel runs) the bonus Gumbel-max on row L_b + 1; (2) one thread per request
+// finds the first rejection and lists the requests that need a draw; (3) the
+// listed requests recompute their draft row at j* (rank-r bias on MFMA for
+// bf16, VALU otherwise) and stream the target row j* again, split in
+// vocabulary strips, keeping the best residual and fallback keys; (4) the
+// strips are folded into the next token.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dspark {
 namespace {
 
-constexpr int kCombThreads = 1024;  // verify_residual_combine: 16 wavefronts share the bias
 constexpr int kResRows = 8;  // rejected requests per workgroup of the VALU residual kernel
 
 struct VerifyWs {
@@ -105,20 +106,6 @@ __device__ __forceinline__ void row_chunk(const LT* row, int v0, int V, float (&
     }
 }
 
-// One step of a wavefront argmax (largest key, smallest entry on ties) that
-// carries a value with the winner; see xlane.
-template <int STEP>
-__device__ __forceinline__ void argmax_step(float& key, int& idx, float& val) {
-    const float ok = xlane_f<STEP>(key);
-    const int oi = xlane_i<STEP>(idx);
-    const float ov = xlane_f<STEP>(val);
-    if (beats(ok, oi, key, idx)) {
-        key = ok;
-        idx = oi;
-        val = ov;
-    }
-}
-
 // verify_rows: one 512-thread workgroup per visited row with two 16-byte loads
 // in flight per lane (measured best among 64 / 256 / 512 / 1024 threads and
 // one, two or four loads per lane).
@@ -133,7 +120,6 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
     int K, int V, int64_t n_rows, bool bonus_draw, float* __restrict__ row_lse_t,
     float* __restrict__ row_logratio, VerifyWs ws, int j_lo, int span) {
     __shared__ RowState red[kVRowThreads / kWave];
-    __shared__ int sh_blk;
     const int64_t id = blockIdx.x;
     // the residual list starts empty; verify_resolve appends to it after the
     // last launch of this kernel
@@ -165,9 +151,7 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
         // argmax of t, smallest index on ties (visited in increasing v per thread)
         float best = -INFINITY;
         int bi = 0x7fffffff;
-        // the 8 threads of a 64-entry block run the same iterations
-        for (int c0 = threadIdx.x * 8; c0 - 8 * static_cast<int>(threadIdx.x & 7) < V;
-             c0 += kVRowThreads * 8 * kVRowUnroll) {
+        for (int c0 = threadIdx.x * 8; c0 < V; c0 += kVRowThreads * 8 * kVRowUnroll) {
             float xs[kVRowUnroll][8];
 #pragma unroll
             for (int u = 0; u < kVRowUnroll; ++u) {
@@ -194,12 +178,14 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
         // s = sum 2^((t - m) c) with c = log2(e) / T
         const float it = inv_temperature(T);
         const float c = it * kLog2e;
+        const KeyLane kl = key_lane(T);
+        const PhiloxRow ph = draw ? philox_row(seed, static_cast<uint32_t>(b),
+                                               static_cast<uint32_t>(j), kTagResample)
+                                  : PhiloxRow{};
         float m = -INFINITY, s = 0.0f;
         float best = -INFINITY;
         int bi = 0x7fffffff;
-        // the 8 threads of a 64-entry block run the same iterations
-        for (int c0 = threadIdx.x * 8; c0 - 8 * static_cast<int>(threadIdx.x & 7) < V;
-             c0 += kVRowThreads * 8 * kVRowUnroll) {
+        for (int c0 = threadIdx.x * 8; c0 < V; c0 += kVRowThreads * 8 * kVRowUnroll) {
           float xs[kVRowUnroll][8];
 #pragma unroll
           for (int u = 0; u < kVRowUnroll; ++u) {
@@ -221,31 +207,20 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
             const float mc = (m == -INFINITY) ? 0.0f : m * c;
 #pragma unroll
             for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[e], c, -mc));
-            if (draw) {
-                // two-level bonus draw, first level: the chunk's 64-entry block
-                // is the chunks of threads 8 q .. 8 q + 7; its key is
-                // log2-mass + base-2 Gumbel (tag 4, word = block index)
-                float bm = cm;
-                bm = fmaxf(bm, xlane_f<0>(bm));
-                bm = fmaxf(bm, xlane_f<1>(bm));
-                bm = fmaxf(bm, xlane_f<2>(bm));
-                const float bmc = (bm == -INFINITY) ? 0.0f : bm * c;
-                float bs = 0.0f;
+            if (draw && v0 < V) {
+                // bonus draw: key t c - log2(-log2 u) per entry (tag 2), two
+                // Philox blocks per chunk; entries past V read -inf
 #pragma unroll
-                for (int e = 0; e < 8; ++e) bs += __builtin_amdgcn_exp2f(fmaf(x[e], c, -bmc));
-                bs += xlane_f<0>(bs);
-                bs += xlane_f<1>(bs);
-                bs += xlane_f<2>(bs);
-                const int blk = v0 >> 6;
-                const float key =
-                    (bm == -INFINITY)
-                        ? -INFINITY
-                        : bmc + __builtin_amdgcn_logf(bs) +
-                              block_gumbel2(pick(
-                                  philox_block(seed, b, j, kTagVerifyBlock, blk >> 2), blk & 3));
-                if (key > best) {
-                    best = key;
-                    bi = blk * kDraftBlock;
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 rnd = philox_row_block(ph, static_cast<uint32_t>(v0 >> 2) + h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float key = fmaf(x[4 * h + e], c, -entry_l2(pick(rnd, e), kl));
+                        if (key > best) {
+                            best = key;
+                            bi = v0 + 4 * h + e;
+                        }
+                    }
                 }
             }
           }
@@ -258,31 +233,6 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
         st.idx = bi;
     }
     st = block_reduce_row<kVRowThreads>(st, red);
-    if (draw && !greedy) {
-        // second level: the Gumbel-argmax of y = t / T inside the winning block
-        // (tag 2, word = entry), lane q of wavefront 0 taking entry blk + q
-        if (threadIdx.x == 0) sh_blk = st.idx;
-        __syncthreads();
-        if (threadIdx.x < kWave) {
-            const int blk = sh_blk;
-            const bool ok = blk >= 0 && blk < V;
-            const int v = ok ? blk + static_cast<int>(threadIdx.x) : V;
-            float key = -INFINITY;
-            if (v < V) {
-                const float y = to_f32(trow[v]) * inv_temperature(T);
-                key = y + gumbel_fast(pick(philox_block(seed, b, j, kTagResample, v >> 2), v & 3));
-            }
-            int bv = (v < V) ? v : 0x7fffffff;
-            float unused = 0.0f;
-            argmax_step<0>(key, bv, unused);
-            argmax_step<1>(key, bv, unused);
-            argmax_step<2>(key, bv, unused);
-            argmax_step<3>(key, bv, unused);
-            argmax_step<4>(key, bv, unused);
-            argmax_step<5>(key, bv, unused);
-            if (threadIdx.x == 0) st.idx = bv;
-        }
-    }
     if (threadIdx.x == 0) {
         const size_t slot = static_cast<size_t>(b) * (K + 1) + (j - 1);
         const float lse_t = greedy ? st.pert : st.m + logf(st.s);
@@ -344,7 +294,8 @@ __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_ro
 }
 
 // Residual strip kernel, VALU form (fp32 inputs, or shapes the MFMA form does
-// not take): workgroup = (8 rejected requests) x (1024 vocabulary entries).
+// not take): workgroup = (8 rejected requests) x (1024 vocabulary entries);
+// each thread keeps the best residual and fallback keys of its 4 entries.
 template <typename LT, typename FT>
 __global__ __launch_bounds__(256) void verify_residual_valu(
     const LT* __restrict__ base, const FT* __restrict__ A, const FT* __restrict__ W,
@@ -401,50 +352,28 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
         if (g >= nrows) break;
         const int b = ws.list[slot0 + g];
         const int js = accepted[b] + 1;
-        const float it = inv_temperature(temperature[b]);
-        const float lse_d = draft_lse[static_cast<size_t>(b) * K + js - 1];
-        const float lse_t = ws.lse[static_cast<size_t>(b) * (K + 1) + js - 1];
-        // masses of the thread's 4 entries: residual max(0, p_t - p_d) and p_t
-        float mr = 0.0f, mf = 0.0f;
+        const float T = temperature[b];
+        // keys of the thread's 4 entries (one Philox block), see residual_entry
+        ResRow R;
+        R.c2 = inv_temperature(T) * kLog2e;
+        R.lt2 = ws.lse[static_cast<size_t>(b) * (K + 1) + js - 1] * kLog2e;
+        R.dl = R.lt2 - draft_lse[static_cast<size_t>(b) * K + js - 1] * kLog2e;
+        R.bonus = false;
+        R.kl = key_lane(T);
+        ResBest best = res_empty();
         if (v0 < V) {
             const LT* br = base + (static_cast<size_t>(b) * K + js - 1) * V + v0;
             const LT* tr = target + (row_off[b] + js - 1) * static_cast<int64_t>(V) + v0;
+            const u32x4 rnd = philox_block(seed, b, js, kTagResample, v0 >> 2);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 if (v0 + t >= V) continue;
-                const float z = (to_f32(br[t]) + acc[g][t]) * it;
-                const float y = to_f32(tr[t]) * it;
-                const float pt = expf(y - lse_t);
-                const float res = pt - expf(z - lse_d);
-                if (res > 0.0f) mr += res;
-                mf += pt;
+                residual_entry(best, to_f32(br[t]) + acc[g][t], to_f32(tr[t]), pick(rnd, t),
+                               v0 + t, R);
             }
         }
-        // the 16 threads of a 64-entry block (v0 / 64 is shared) sum their
-        // masses; every one of them forms the block keys (tag-4 draw)
-        mr += xlane_f<0>(mr);
-        mf += xlane_f<0>(mf);
-        mr += xlane_f<1>(mr);
-        mf += xlane_f<1>(mf);
-        mr += xlane_f<2>(mr);
-        mf += xlane_f<2>(mf);
-        mr += xlane_f<3>(mr);
-        mf += xlane_f<3>(mf);
-        RowState sr = row_empty();
-        RowState sf = row_empty();
-        if (v0 < V) {
-            const int blk = v0 >> 6;
-            const float gb = gumbel_of(
-                pick(philox_block(seed, b, js, kTagVerifyBlock, blk >> 2), blk & 3));
-            if (mr > 0.0f) {
-                sr.pert = logf(mr) + gb;
-                sr.idx = blk * kDraftBlock;
-            }
-            if (mf > 0.0f) {
-                sf.pert = logf(mf) + gb;
-                sf.idx = blk * kDraftBlock;
-            }
-        }
+        RowState sr{-INFINITY, 0.0f, best.br, 0.0f, best.ir};
+        RowState sf{-INFINITY, 0.0f, best.bf, 0.0f, best.jf};
         wave_reduce_row(sr);
         wave_reduce_row(sf);
         if ((tid & 63) == 0) {
@@ -467,130 +396,35 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
     }
 }
 
-// Fold the residual strips of each listed request into its next token.
-
-// Merge the block partials of each listed request, then draw inside the
-// winning block: the residual block when the residual has mass, else the
-// fallback (p_t) block, which for a listed full acceptance is its bonus.  Lane
-// j of wavefront 0 takes entry blk + j with the tag-2 draw of that entry; a
-// residual entry needs log2 p_d, so the draft bias of the block's entries is
-// recomputed first, the rank loop split over the workgroup's wavefronts.
-// Keys in base 2 order entries as the natural-log forms do (see
-// residual_strip_mfma): residual log2 r - log2(-log2 u) over entries with
-// p_t > p_d, fallback log2 p_t - log2(-log2 u).
-template <typename LT, typename FT>
-__global__ __launch_bounds__(kCombThreads) void verify_residual_combine(
-    VerifyWs ws, int n_strips, const LT* __restrict__ base, const FT* __restrict__ A,
-    const FT* __restrict__ W, const LT* __restrict__ target, const int64_t* __restrict__ row_off,
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ prev_token,
-    const float* __restrict__ draft_lse, const float* __restrict__ temperature,
-    const int32_t* __restrict__ accepted, uint64_t seed, int K, int V, int r,
-    int32_t* __restrict__ next_token) {
-    constexpr int NW = kCombThreads / kWave;
-    __shared__ RowState red_r[NW], red_f[NW];
-    __shared__ float bias_sh[NW][kDraftBlock];
-    __shared__ int sh_blk, sh_residual;
+// Fold the residual strips of each listed request into its next token: the
+// winner of the residual keys when any entry had positive residual mass, else
+// the winner of the fallback keys (for a listed full acceptance, its bonus).
+// One wavefront per listed request.
+__global__ __launch_bounds__(kWave) void verify_residual_combine(VerifyWs ws, int n_strips,
+                                                                 int32_t* __restrict__ next_token) {
     const int slot = blockIdx.x;
     if (slot >= *ws.count) return;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    // both block states in one pass: per wavefront in registers, then the NW
-    // wavefront states by wavefront 0
+    const int lane = threadIdx.x;
     RowState sr = row_empty();
     RowState sf = row_empty();
-    for (int s = threadIdx.x; s < n_strips; s += kCombThreads) {
-        row_merge(sr, load_partial(ws.res, static_cast<size_t>(slot) * n_strips + s));
-        row_merge(sf, load_partial(ws.fall, static_cast<size_t>(slot) * n_strips + s));
+    const size_t o = static_cast<size_t>(slot) * n_strips;
+    int s = lane;
+    for (; s + kWave < n_strips; s += 2 * kWave) {
+        const RowState r0 = load_partial(ws.res, o + s), r1 = load_partial(ws.res, o + s + kWave);
+        const RowState f0 = load_partial(ws.fall, o + s),
+                       f1 = load_partial(ws.fall, o + s + kWave);
+        row_merge(sr, r0);
+        row_merge(sr, r1);
+        row_merge(sf, f0);
+        row_merge(sf, f1);
+    }
+    for (; s < n_strips; s += kWave) {
+        row_merge(sr, load_partial(ws.res, o + s));
+        row_merge(sf, load_partial(ws.fall, o + s));
     }
     wave_reduce_row(sr);
     wave_reduce_row(sf);
-    if (lane == 0) {
-        red_r[wave] = sr;
-        red_f[wave] = sf;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        sr = (lane < NW) ? red_r[lane] : row_empty();
-        sf = (lane < NW) ? red_f[lane] : row_empty();
-        wave_reduce_row(sr);
-        wave_reduce_row(sf);
-        if (lane == 0) {
-            sh_residual = sr.pert > -INFINITY;
-            sh_blk = sh_residual ? sr.idx : sf.idx;
-        }
-    }
-    __syncthreads();
-    const bool residual = sh_residual != 0;
-    const int blk = sh_blk;
-    const int b = ws.list[slot];
-    const int js = accepted[b] + 1;
-    // a block start in [0, V) (no partial with a key leaves the index at
-    // 0x7fffffff: then nothing is read and next_token gets that index)
-    const bool blk_ok = blk >= 0 && blk < V;
-    const int v = blk_ok ? blk + lane : V;
-    const bool in = v < V;
-    // the entry's target logit (and draft base logit) go out before the bias
-    // barrier, so that their latency overlaps the factor loads
-    float tv = 0.0f, bv0 = 0.0f;
-    if (wave == 0 && in) {
-        tv = to_f32(target[(row_off[b] + js - 1) * static_cast<int64_t>(V) + v]);
-        if (residual) bv0 = to_f32(base[(static_cast<size_t>(b) * K + js - 1) * V + v]);
-    }
-    if (residual) {
-        // draft bias of entry v: ranks wave, wave + NW, ... of A[x_{js-1}] . W[:, v]
-        const int p = clamp_token(
-            (js == 1) ? prev_token[b] : tokens[static_cast<size_t>(b) * K + js - 2], V);
-        // each wavefront's ranks are loaded 16 at a time (one round trip
-        // for r <= 16 NW), then added up
-        float part = 0.0f;
-        if (in) {
-            const FT* arow = A + static_cast<size_t>(p) * r;
-            int i = wave;
-            for (; i + 15 * NW < r; i += 16 * NW) {
-                float av[16], wv[16];
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    av[q] = to_f32(arow[i + q * NW]);
-                    wv[q] = to_f32(W[static_cast<size_t>(i + q * NW) * V + v]);
-                }
-#pragma unroll
-                for (int q = 0; q < 16; ++q) part = fmaf(av[q], wv[q], part);
-            }
-            for (; i < r; i += NW)
-                part = fmaf(to_f32(arow[i]), to_f32(W[static_cast<size_t>(i) * V + v]), part);
-        }
-        bias_sh[wave][lane] = part;
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    const float c2 = inv_temperature(temperature[b]) * kLog2e;
-    const float lt2 = ws.lse[static_cast<size_t>(b) * (K + 1) + js - 1] * kLog2e;
-    float key = -INFINITY;
-    if (in) {
-        const float a = fmaf(tv, c2, -lt2);
-        const float l1 = __builtin_amdgcn_logf(
-            uniform_of(pick(philox_block(seed, b, js, kTagResample, v >> 2), v & 3)));
-        const float g2 = __builtin_amdgcn_logf(-l1);  // log2(-log2 u)
-        if (residual) {
-            float bias = 0.0f;
-            for (int w = 0; w < NW; ++w) bias += bias_sh[w][lane];
-            const float ld2 = draft_lse[static_cast<size_t>(b) * K + js - 1] * kLog2e;
-            const float d = fmaf(bv0 + bias, c2, -ld2);
-            if (a > d) key = a + __builtin_amdgcn_logf(1.0f - __builtin_amdgcn_exp2f(d - a)) - g2;
-        } else {
-            key = a - g2;
-        }
-    }
-    // wavefront argmax, smallest entry on ties
-    int bv = in ? v : 0x7fffffff;
-    float unused = 0.0f;
-    argmax_step<0>(key, bv, unused);
-    argmax_step<1>(key, bv, unused);
-    argmax_step<2>(key, bv, unused);
-    argmax_step<3>(key, bv, unused);
-    argmax_step<4>(key, bv, unused);
-    argmax_step<5>(key, bv, unused);
-    if (lane == 0) next_token[b] = bv;
+    if (lane == 0) next_token[ws.list[slot]] = (sr.pert > -INFINITY) ? sr.idx : sf.idx;
 }
 
 struct WsLayout {
@@ -614,16 +448,6 @@ WsLayout verify_layout(int B, int K, int V) {
     l.fall_i = o; o += align256(np * 4);
     l.total = o;
     return l;
-}
-
-template <typename LT, typename FT>
-void launch_residual_combine(const VerifyArgs& a, const VerifyWs& ws, int n_strips) {
-    hipLaunchKernelGGL((verify_residual_combine<LT, FT>), dim3(static_cast<unsigned>(a.B)),
-                       dim3(kCombThreads), 0, a.stream, ws, n_strips,
-                       static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
-                       static_cast<const FT*>(a.W), static_cast<const LT*>(a.target), a.row_off,
-                       a.tokens, a.prev_token, a.draft_lse, a.temperature, a.accepted, a.seed,
-                       a.K, a.V, a.r, a.next_token);
 }
 
 template <typename LT, typename FT>
@@ -738,14 +562,8 @@ hipError_t launch_verify(const VerifyArgs& a) {
     prof_end(res_scope.slot, a.stream);
     res_scope.slot = -1;
     ProfScope combine_scope(DSPARK_KERNEL_RESIDUAL_COMBINE, a.stream);
-    if (a.logit_dt == DSPARK_BF16 && a.factor_dt == DSPARK_BF16)
-        launch_residual_combine<bf16_t, bf16_t>(a, ws, n_strips);
-    else if (a.logit_dt == DSPARK_BF16)
-        launch_residual_combine<bf16_t, float>(a, ws, n_strips);
-    else if (a.factor_dt == DSPARK_BF16)
-        launch_residual_combine<float, bf16_t>(a, ws, n_strips);
-    else
-        launch_residual_combine<float, float>(a, ws, n_strips);
+    hipLaunchKernelGGL(verify_residual_combine, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0,
+                       a.stream, ws, n_strips, a.next_token);
     return hipGetLastError();
 }
 
