@@ -116,42 +116,55 @@ __device__ __forceinline__ PhiloxRow philox_row(uint64_t seed, uint32_t b, uint3
     return r;
 }
 
-// Draws for vocabulary entries 4 q .. 4 q + 3 (word v & 3 of block q = v >> 2).
-__device__ __forceinline__ u32x4 philox_row_block(const PhiloxRow& r, uint32_t q) {
+// The block for counter word q in stages, so that a caller can spread its
+// rounds over other work: philox_head runs rounds 1-3 (where the fixed parts
+// of the counter are folded in), philox_round(i) round i = 4..10 with the key
+// advanced i - 1 times.
+struct PhiloxState {
+    uint32_t c0, c1, c2, c3;
+};
+
+__device__ __forceinline__ PhiloxState philox_head(const PhiloxRow& r, uint32_t q) {
     // round 1: x0, x1 come from (pos, b); x2, x3 from q
     const uint64_t a0 = static_cast<uint64_t>(0xD2511F53u) * q;
     const uint32_t x2 = static_cast<uint32_t>(a0 >> 32) ^ r.c3k;
     const uint32_t x3 = static_cast<uint32_t>(a0);
     // round 2: M0 x0 is fixed
     const uint64_t a1 = static_cast<uint64_t>(0xCD9E8D57u) * x2;
-    uint32_t c0 = static_cast<uint32_t>(a1 >> 32) ^ r.x1k;
-    uint32_t c1 = static_cast<uint32_t>(a1);
-    uint32_t c2 = x3 ^ r.h0k;
-    uint32_t c3 = r.l0;
+    const uint32_t c0 = static_cast<uint32_t>(a1 >> 32) ^ r.x1k;
+    const uint32_t c1 = static_cast<uint32_t>(a1);
+    const uint32_t c2 = x3 ^ r.h0k;
     // round 3: the previous word 3 (lo(M0 x0)) is fixed
-    {
-        const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
-        const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
-        c0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, r.k0 + 2u * 0x9E3779B9u);
-        c1 = static_cast<uint32_t>(p1);
-        c2 = static_cast<uint32_t>(p0 >> 32) ^ r.l0k;
-        c3 = static_cast<uint32_t>(p0);
-    }
-    uint32_t k0 = r.k0 + 3u * 0x9E3779B9u, k1 = r.k1 + 3u * 0xBB67AE85u;
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+    return {xor3(static_cast<uint32_t>(p1 >> 32), c1, r.k0 + 2u * 0x9E3779B9u),
+            static_cast<uint32_t>(p1), static_cast<uint32_t>(p0 >> 32) ^ r.l0k,
+            static_cast<uint32_t>(p0)};
+}
+
+__device__ __forceinline__ void philox_round(PhiloxState& p, const PhiloxRow& r, int i) {
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * p.c0;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * p.c2;
+    const uint32_t n0 =
+        xor3(static_cast<uint32_t>(p1 >> 32), p.c1, r.k0 + static_cast<uint32_t>(i - 1) * 0x9E3779B9u);
+    const uint32_t n2 =
+        xor3(static_cast<uint32_t>(p0 >> 32), p.c3, r.k1 + static_cast<uint32_t>(i - 1) * 0xBB67AE85u);
+    p.c1 = static_cast<uint32_t>(p1);
+    p.c3 = static_cast<uint32_t>(p0);
+    p.c0 = n0;
+    p.c2 = n2;
+}
+
+__device__ __forceinline__ uint32_t state_word(const PhiloxState& p, int w) {
+    return w == 0 ? p.c0 : (w == 1 ? p.c1 : (w == 2 ? p.c2 : p.c3));
+}
+
+// Draws for vocabulary entries 4 q .. 4 q + 3 (word v & 3 of block q = v >> 2).
+__device__ __forceinline__ u32x4 philox_row_block(const PhiloxRow& r, uint32_t q) {
+    PhiloxState p = philox_head(r, q);
 #pragma unroll
-    for (int i = 3; i < 10; ++i) {
-        const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
-        const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
-        const uint32_t n0 = xor3(static_cast<uint32_t>(p1 >> 32), c1, k0);
-        const uint32_t n2 = xor3(static_cast<uint32_t>(p0 >> 32), c3, k1);
-        c1 = static_cast<uint32_t>(p1);
-        c3 = static_cast<uint32_t>(p0);
-        c0 = n0;
-        c2 = n2;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
-    return {c0, c1, c2, c3};
+    for (int i = 4; i <= 10; ++i) philox_round(p, r, i);
+    return {p.c0, p.c1, p.c2, p.c3};
 }
 
 // Per-lane constants of the entry key.  A sampled lane (T > 0) forms

@@ -33,6 +33,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kStripV = kMfmaStrip;  // 128 vocabulary entries per strip
+// s_waitcnt operand (gfx9 encoding): vector-memory count <= 4, export and LDS
+// counts not waited on
+constexpr int kWaitVm4 = 4 | (7 << 4) | (15 << 8);
 constexpr int kPitch = kStripV;  // LDS row pitch in bf16 elements (256 bytes)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8, q); }
@@ -188,21 +191,21 @@ __device__ __forceinline__ RowState lane_row(const LaneRun& r) {
 
 // Fold a chunk's softmax partial (chunk maximum mx of s, sum of 2^(s c2 - mc)
 // with mc = mx c2, or mx = -inf for a chunk with no entry below V) and its best
-// key into the lane state.  Chunks arrive in increasing entry order, so a
-// strict comparison keeps the smallest entry on ties.
+// key into the lane state (ties to the smaller entry: the two MFMA tiles of a
+// half interleave in entry order).
 __device__ __forceinline__ void fold_chunk(LaneRun& run, float mx, float mc, float sum, float hb,
                                            int hi) {
+    // select-only (no branch), so that the fold stays in the scheduling region
+    // of the MFMAs it is interleaved with; with M = -inf both sides hold no
+    // entry and exp2(-inf) = 0 keeps the sum at 0
     const float mh = (mx == -INFINITY) ? -INFINITY : mc;
     const float M = fmaxf(run.m2, mh);
-    if (M != -INFINITY) {
-        // exp2(-inf) = 0 drops a side that holds no entry yet
-        run.s = run.s * __builtin_amdgcn_exp2f(run.m2 - M) + sum * __builtin_amdgcn_exp2f(mh - M);
-        run.m2 = M;
-    }
-    if (hb > run.key) {
-        run.key = hb;
-        run.idx = hi;
-    }
+    const float Mr = (M == -INFINITY) ? 0.0f : M;
+    run.s = run.s * __builtin_amdgcn_exp2f(run.m2 - Mr) + sum * __builtin_amdgcn_exp2f(mh - Mr);
+    run.m2 = M;
+    const bool take = beats(hb, hi, run.key, run.idx);
+    run.key = take ? hb : run.key;
+    run.idx = take ? hi : run.idx;
 }
 
 // Epilogue of the runtime-rank kernel for one lane (one request, 64 entries
@@ -379,6 +382,27 @@ __device__ __forceinline__ void stage_w_tr(uint16_t* w_sh, const uint16_t* __res
     }
 }
 
+// The same with the rank fixed at compile time (r = 16 KS, 4 KS a multiple of
+// NWAVES): each wave issues exactly 4 KS / NWAVES direct loads, so the
+// compiler can count the loads issued after any earlier one and wait for that
+// one alone (with a runtime trip count it waits for every outstanding load).
+template <int NWAVES, int KS>
+__device__ __forceinline__ void stage_w_tr_fixed(uint16_t* w_sh, const uint16_t* __restrict__ W,
+                                                 int V, int v0) {
+    static_assert((4 * KS) % NWAVES == 0, "whole rank rows per wave");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = tr_granule_flip((lane & 15) ^ tr_row_swizzle(lane >> 4));
+    const int v = min(v0 + 8 * g, V - 8);
+    const uint16_t* src = W + static_cast<size_t>(lane >> 4) * V + v;
+#pragma unroll
+    for (int i = 0; i < 4 * KS / NWAVES; ++i) {
+        const int j = wave + i * NWAVES;
+        __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(4 * j) * V,
+                                         w_sh + 4 * j * kPitch, 16, 0, 0);
+    }
+}
+
 // Element offset in a strip buffer of the row piece this lane names for half h,
 // tile t, rank step 0: lane = 32 kh + 16 gm + 4 u + q reads rank row 8 kh + u
 // at entry 64 h + 32 gm + 16 (q / 2) + 8 (q % 2) + 4 (t ^ (q / 2)) (granule
@@ -540,59 +564,275 @@ __device__ __forceinline__ void greedy_half(LaneRun& run, const f32x16 (&acc)[2]
     }
 }
 
+// Eight bf16 -inf: the logit chunk that stands in for chunks past V.
+__device__ uint4 kNegInfChunk = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+
+// Chunks a = 0..3 of half h of a lane's strip logits (entries v0 + 64 h +
+// 16 a + 8 kh .. + 7).  A chunk past V is read from kNegInfChunk, so entries
+// past V carry the logit -inf with no fix-up after the loads land (a fix-up
+// would make the waits for these loads coarser than they need to be).
+__device__ __forceinline__ void load_half(uint4 (&q)[4], const uint16_t* row, int v0, int h,
+                                          int kh, int V) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int v = v0 + 64 * h + 16 * a + 8 * kh;
+        const uint4* p = (v < V) ? reinterpret_cast<const uint4*>(row + v) : &kNegInfChunk;
+        q[a] = *p;
+    }
+}
+
+// The -inf fix-up for chunks past V, for callers that load with the row's
+// last chunk standing in (the residual kernel).
+__device__ __forceinline__ void tail_half(uint4 (&q)[4], int v0, int h, int kh, int V) {
+    if (v0 + kStripV > V) {
+        const uint32_t ninf2 = 0xFF80FF80u;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            if (v0 + 64 * h + 16 * a + 8 * kh >= V) q[a] = make_uint4(ninf2, ninf2, ninf2, ninf2);
+    }
+}
+
+// ------------------------------------------- rank 256: one MFMA tile at a time
+// Tile t of a half is accumulator set acc[t] of acc_from_logits' layout: its
+// accumulator i = 4 a + w holds entry vh + 16 a + 4 (t ^ (a % 2)) + w, element
+// 4 (t ^ (a % 2)) + w of logit chunk a.  The sixteen entries of a tile are four
+// Philox blocks, visited in increasing order.
+
+__device__ __forceinline__ void tile_from_logits(f32x16& acc, const uint4 (&q)[4], int t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t dw = dword_of(q[i >> 2], 2 * (t ^ ((i >> 2) & 1)) + ((i & 3) >> 1));
+        acc[i] = __uint_as_float((i & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
+    }
+}
+
+template <int KS>
+__device__ __forceinline__ void bias_tile(f32x16& acc, const uint16_t* wt,
+                                          const uint4 (&afr)[KS]) {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        const uint2 lo = lds_tr16(wt + kk * 16 * kPitch);
+        const uint2 hi = lds_tr16(wt + kk * 16 * kPitch + 4 * kPitch);
+        const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(afr[kk]), acc, 0, 0,
+                                                      0);
+    }
+}
+
+__device__ __forceinline__ void sample_tile(LaneRun& run, const f32x16& acc, int vh, int t,
+                                            const KeyLane& kl, const PhiloxRow& ph) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
+    const float mc = (mx == -INFINITY) ? 0.0f : mx * kl.c2;
+    float sum = 0.0f, hb = -INFINITY;
+    int hi = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int o = 16 * a + 4 * (t ^ (a & 1));
+        const u32x4 rnd = philox_row_block(ph, static_cast<uint32_t>((vh + o) >> 2));
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float sv = acc[4 * a + w];
+            sum += __builtin_amdgcn_exp2f(fmaf(sv, kl.c2, -mc));
+            const float key = fmaf(sv, kl.c2, -entry_l2(pick(rnd, w), kl));
+            if (key > hb) {
+                hb = key;
+                hi = o + w;
+            }
+        }
+    }
+    fold_chunk(run, mx, mc, sum, hb, vh + hi);
+}
+
+__device__ __forceinline__ void greedy_tile(LaneRun& run, const f32x16& acc, int vh, int t) {
+    float hb = -INFINITY;
+    int hi = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            if (acc[4 * a + w] > hb) {
+                hb = acc[4 * a + w];
+                hi = 16 * a + 4 * (t ^ (a & 1)) + w;
+            }
+    if (beats(hb, vh + hi, run.key, run.idx)) {
+        run.key = hb;
+        run.idx = vh + hi;
+    }
+}
+
+// Software pipeline of the rank-256 draft kernel, one unit per MFMA tile (a
+// strip is four: half 0 tiles 0 and 1, half 1 tiles 0 and 1).  Unit u runs the
+// KS bias MFMAs of its own tile into one accumulator set and, in the same
+// instruction stream, the per-entry sampling of unit u - 1 from the other set.
+// A wavefront issues in order, so MFMAs grouped in a phase of their own stall
+// it (each waits for the matrix core and for its transposing LDS reads) while
+// its VALU work waits behind them; the unit is therefore cut into KS slices
+// fenced by sched_barrier, slice kk holding the MFMA of rank step kk (its
+// operands read two slices earlier), entry kk % 4 of Philox block kk / 4 and a
+// quarter of the rounds of the next block.  Measured on its own (two
+// wavefronts per SIMD, operands in LDS) this takes 4.3K cycles per pair of
+// tiles against 4.75K with the MFMAs in a phase of their own and 3.8K for the
+// sampling alone.  Pipelining per tile rather than per half keeps two
+// accumulator sets at 32 registers.
+template <int KS, bool GREEDY, bool SAMPLE>
+__device__ __forceinline__ void rk_unit(f32x16& accm, const uint16_t* wt, const uint4 (&afr)[KS],
+                                        const f32x16& accs, LaneRun& run, int vs, int ts,
+                                        const KeyLane& kl, const PhiloxRow& ph) {
+    static_assert(KS == 16, "the slice schedule covers 16 rank steps (four Philox blocks)");
+    constexpr bool kSample = SAMPLE && !GREEDY;
+    uint2 lo[3], hi[3];
+    lo[0] = lds_tr16(wt);
+    hi[0] = lds_tr16(wt + 4 * kPitch);
+    lo[1] = lds_tr16(wt + 16 * kPitch);
+    hi[1] = lds_tr16(wt + 16 * kPitch + 4 * kPitch);
+    float mx = -INFINITY, mc = 0.0f, sum = 0.0f, hb = -INFINITY;
+    int he = 0;
+    PhiloxState cur{}, nxt{};
+    if constexpr (kSample) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, accs[i]);
+        mc = (mx == -INFINITY) ? 0.0f : mx * kl.c2;
+        nxt = philox_head(ph, static_cast<uint32_t>((vs + 4 * ts) >> 2));
+#pragma unroll
+        for (int i = 4; i <= 10; ++i) philox_round(nxt, ph, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 2 < KS) {
+            lo[(kk + 2) % 3] = lds_tr16(wt + (kk + 2) * 16 * kPitch);
+            hi[(kk + 2) % 3] = lds_tr16(wt + (kk + 2) * 16 * kPitch + 4 * kPitch);
+        }
+        const uint4 a = make_uint4(lo[kk % 3].x, lo[kk % 3].y, hi[kk % 3].x, hi[kk % 3].y);
+        accm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(afr[kk]), accm, 0, 0,
+                                                       0);
+        if constexpr (kSample) {
+            // entry w of block g (tile entries 16 g + 4 (ts ^ (g % 2)) + w)
+            const int g = kk >> 2, w = kk & 3;
+            if (w == 0) cur = nxt;
+            const int o = 16 * g + 4 * (ts ^ (g & 1));
+            const float sv = accs[4 * g + w];
+            sum += __builtin_amdgcn_exp2f(fmaf(sv, kl.c2, -mc));
+            const float key = fmaf(sv, kl.c2, -entry_l2(state_word(cur, w), kl));
+            if (key > hb) {
+                hb = key;
+                he = o + w;
+            }
+            // a quarter of block g + 1's rounds
+            if (g < 3) {
+                const int gn = g + 1;
+                if (w == 0) {
+                    nxt = philox_head(ph, static_cast<uint32_t>((vs + 16 * gn + 4 * (ts ^ (gn & 1))) >> 2));
+                    philox_round(nxt, ph, 4);
+                } else {
+                    philox_round(nxt, ph, 2 * w + 3);
+                    philox_round(nxt, ph, 2 * w + 4);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kSample) fold_chunk(run, mx, mc, sum, hb, vs + he);
+    if constexpr (SAMPLE && GREEDY) greedy_tile(run, accs, vs, ts);
+}
+
 // One strip of draft_strip_mfma_rk: this strip's W is in `cur`, the next
 // strip's goes into `nxt`.  The caller alternates two static LDS arrays, so
 // every LDS access here names one array: the compiler then sees that the
 // transposing reads of `cur` cannot alias the direct loads into `nxt`, and
-// issues the MFMA loop without first waiting for the next strip's W (with one
-// dynamically indexed LDS array it has to wait for every outstanding direct
-// load before the first LDS read).  Returns false after the last strip.
-template <int NWAVES, int KS, bool GREEDY>
-__device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int& s, uint4 (&bl)[8],
-                                         uint4 (&bn)[8], LaneRun& run,
-                                         const uint16_t* __restrict__ W,
+// issues the MFMAs without first waiting for the next strip's W.  L0 / L1
+// hold this strip's half-0 / half-1 logits on entry and the next strip's on
+// return (each is reloaded once both of its tiles are unpacked); accB holds the
+// previous strip's last tile (unsampled) on entry, and this strip's on return.
+// FIRST: no previous tile to sample.  Returns false after the last strip.
+template <int NWAVES, int KS, bool GREEDY, bool FIRST>
+__device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int& s, uint4 (&L0)[4],
+                                         uint4 (&L1)[4], f32x16& accA, f32x16& accB, int& vsB,
+                                         LaneRun& run, const uint16_t* __restrict__ W,
                                          const uint16_t* brow, const uint4 (&afr)[KS],
                                          const int (&tro)[2][2], const KeyLane& kl,
                                          const PhiloxRow& ph, int V, int kh, int n_strips,
                                          int n_parts) {
-    // this strip's W (all waves' shares) and logits have landed, and every
-    // wave is done with the other buffer
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    logit_tail(bl, s * kStripV, kh, V);
+    // This strip's W (all waves' shares) and half-0 logits have landed, and
+    // every wave is done with the other buffer.  The wave's loads were issued
+    // in the order W, half-0 logits, half-1 logits (the slices' scheduling
+    // fences keep them there), so waiting until at most the four half-1 loads
+    // are outstanding covers the first two: those were requested about four
+    // tiles ago, the half-1 logits one tile ago, and they are first used two
+    // tiles from now.  The bare barrier (no release fence, which would wait
+    // for every outstanding load) is enough: each wave has waited for its own
+    // direct-to-LDS loads of this strip, every LDS read of the other buffer has
+    // been consumed by an MFMA before it, and the empty asm keeps the compiler
+    // from moving memory accesses across it.
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int v0 = s * kStripV;
     const int sn = s + n_parts;
     const bool more = sn < n_strips;
-    if (more) {
-        stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
-        load_logit_chunks(bn, brow, sn * kStripV, kh, V, 0, 2);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        f32x16 acc[2];
-        const uint16_t* const wt[2] = {cur + tro[h][0], cur + tro[h][1]};
-        acc_from_logits(acc, half_of(bl, h));
-        bias_half<KS>(acc, wt, afr);
-        if (more) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 2 + 4 * h, 4 + 4 * h);
-        if constexpr (GREEDY)
-            greedy_half(run, acc, s * kStripV + 64 * h + 8 * kh);
-        else
-            sample_half(run, acc, s * kStripV + 64 * h + 8 * kh, kl, ph);
-        if (more && h == 0) load_logit_chunks(bn, brow, sn * kStripV, kh, V, 4, 6);
-    }
+    // the next strip's W and logits (after the last strip: this one's again,
+    // into the unused buffer and registers, so that every path issues the
+    // same loads and the waits can count them)
+    const int vn = more ? sn * kStripV : v0;
+    stage_w_tr_fixed<NWAVES, KS>(nxt, W, V, vn);
+    const int vh0 = v0 + 8 * kh, vh1 = v0 + 64 + 8 * kh;
+    tile_from_logits(accA, L0, 0);
+    rk_unit<KS, GREEDY, !FIRST>(accA, cur + tro[0][0], afr, accB, run, vsB, 1, kl, ph);
+    tile_from_logits(accB, L0, 1);
+    load_half(L0, brow, vn, 0, kh, V);
+    rk_unit<KS, GREEDY, true>(accB, cur + tro[0][1], afr, accA, run, vh0, 0, kl, ph);
+    tile_from_logits(accA, L1, 0);
+    rk_unit<KS, GREEDY, true>(accA, cur + tro[1][0], afr, accB, run, vh0, 1, kl, ph);
+    tile_from_logits(accB, L1, 1);
+    load_half(L1, brow, vn, 1, kh, V);
+    rk_unit<KS, GREEDY, true>(accB, cur + tro[1][1], afr, accA, run, vh1, 0, kl, ph);
+    vsB = vh1;
     if (!more) return false;
     s = sn;
     return true;
+}
+
+template <int NWAVES, int KS, bool GREEDY>
+__device__ __forceinline__ void rk_strips(uint16_t* w_a, uint16_t* w_b, int s, LaneRun& run,
+                                          const uint16_t* __restrict__ W, const uint16_t* brow,
+                                          const uint4 (&afr)[KS], const int (&tro)[2][2],
+                                          const KeyLane& kl, const PhiloxRow& ph, int V, int kh,
+                                          int n_strips, int n_parts) {
+    stage_w_tr_fixed<NWAVES, KS>(w_a, W, V, s * kStripV);
+    uint4 L0[4], L1[4];
+    load_half(L0, brow, s * kStripV, 0, kh, V);
+    load_half(L1, brow, s * kStripV, 1, kh, V);
+    f32x16 accA, accB;
+    int vsB = 0;
+    // strips alternate between w_a and w_b
+    if (rk_strip<NWAVES, KS, GREEDY, true>(w_a, w_b, s, L0, L1, accA, accB, vsB, run, W, brow,
+                                           afr, tro, kl, ph, V, kh, n_strips, n_parts)) {
+        while (rk_strip<NWAVES, KS, GREEDY, false>(w_b, w_a, s, L0, L1, accA, accB, vsB, run, W,
+                                                   brow, afr, tro, kl, ph, V, kh, n_strips,
+                                                   n_parts) &&
+               rk_strip<NWAVES, KS, GREEDY, false>(w_a, w_b, s, L0, L1, accA, accB, vsB, run, W,
+                                                   brow, afr, tro, kl, ph, V, kh, n_strips,
+                                                   n_parts)) {
+        }
+    }
+    // the last tile (half 1, tile 1)
+    if constexpr (GREEDY)
+        greedy_tile(run, accB, vsB, 1);
+    else
+        sample_tile(run, accB, vsB, 1, kl, ph);
 }
 
 // One workgroup per (part, request group), persistent over the strips part,
 // part + n_parts, ...: the factor fragments of each lane's request are loaded
 // once and stay in registers, so the MFMA loops issue no vector-memory loads.
 // The next strip's W (into the other LDS array) is requested as soon as a
-// strip starts, and its logits (into registers) two chunks at a time between
-// the strip's phases: issued all at once, the 16 loads of 8 waves queue behind
-// each other in the CU's memory pipeline and stall the waves that issue last.  Each lane folds the
-// halves and strips it visits into one running state, so a request gets
-// n_parts partials per step.
+// strip starts, and each half's logits as soon as the registers of the same
+// half of the current strip are free.  Each lane folds the halves and strips
+// it visits into one running state, so a request gets n_parts partials per
+// step.  A wavefront whose lanes are all greedy (T == 0) runs the key-free
+// argmax epilogue.
 template <int NWAVES, int KS>
 __global__ __launch_bounds__(64 * NWAVES)
 void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
@@ -624,26 +864,14 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
     for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
     const int tro[2][2] = {{tr_offset(lane, 0, 0), tr_offset(lane, 0, 1)},
                            {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
-
-    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
-    stage_w_tr<NWAVES>(w_a, W, r, V, s * kStripV);
-    uint4 bl0[8], bl1[8];
-    load_strip_logits(bl0, brow, s * kStripV, kh, V);
     LaneRun lr = lane_empty();
-    // strips alternate between w_a and w_b, and their logits between bl0 and bl1
-    if (wave_greedy) {
-        while (rk_strip<NWAVES, KS, true>(w_a, w_b, s, bl0, bl1, lr, W, brow, afr, tro, kl, ph, V,
-                                          kh, n_strips, n_parts) &&
-               rk_strip<NWAVES, KS, true>(w_b, w_a, s, bl1, bl0, lr, W, brow, afr, tro, kl, ph, V,
-                                          kh, n_strips, n_parts)) {
-        }
-    } else {
-        while (rk_strip<NWAVES, KS, false>(w_a, w_b, s, bl0, bl1, lr, W, brow, afr, tro, kl, ph,
-                                           V, kh, n_strips, n_parts) &&
-               rk_strip<NWAVES, KS, false>(w_b, w_a, s, bl1, bl0, lr, W, brow, afr, tro, kl, ph,
-                                           V, kh, n_strips, n_parts)) {
-        }
-    }
+    const int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
+    if (wave_greedy)
+        rk_strips<NWAVES, KS, true>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph, V, kh, n_strips,
+                                    n_parts);
+    else
+        rk_strips<NWAVES, KS, false>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph, V, kh, n_strips,
+                                     n_parts);
     // lanes l and l + 32 hold the two halves of every strip for one request
     RowState run = lane_row(lr);
     row_merge(run, xlane_row<5>(run));
@@ -874,25 +1102,6 @@ __global__ __launch_bounds__(1024) void temperature_order(const float* __restric
 // logits of a half are loaded one phase ahead into registers that the phase
 // before has freed: a strip's half-1 base logits go out before the next
 // strip's W, so waiting for them never waits for that W.
-
-// Chunks a = 0..3 of half h of a lane's strip logits (entries v0 + 64 h +
-// 16 a + 8 kh .. + 7); loads in bounds (the row's last chunk stands in past V).
-__device__ __forceinline__ void load_half(uint4 (&q)[4], const uint16_t* row, int v0, int h,
-                                          int kh, int V) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-        q[a] = *reinterpret_cast<const uint4*>(row + min(v0 + 64 * h + 16 * a + 8 * kh, V - 8));
-}
-
-// Chunks past V become bf16 -inf once the loads have landed.
-__device__ __forceinline__ void tail_half(uint4 (&q)[4], int v0, int h, int kh, int V) {
-    if (v0 + kStripV > V) {
-        const uint32_t ninf2 = 0xFF80FF80u;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-            if (v0 + 64 * h + 16 * a + 8 * kh >= V) q[a] = make_uint4(ninf2, ninf2, ninf2, ninf2);
-    }
-}
 
 // Keys of one half (see residual_strip_mfma): acc holds s = base + bias, tq
 // the target logits in the same entry layout (acc_from_logits): entry
