@@ -215,15 +215,21 @@ def dspark_verify(draft_tokens, prev_token, draft_logp, draft_lse, base_logits, 
     target_logits is [rows, V] (or [B, K+1, V], viewed as rows); request b's
     rows start at target_row_offsets[b] (int64, [B] or more entries).
     row_outputs=False passes no per-row outputs (both returned as None): the
-    library then reads only the target rows that can decide the result."""
+    library then reads only the target rows that can decide the result.
+    A = W = None verifies tokens drafted without the Markov head (zero bias)."""
     for t, n in ((draft_tokens, "draft_tokens"), (prev_token, "prev_token"),
                  (draft_logp, "draft_logp"), (draft_lse, "draft_lse"),
-                 (base_logits, "base_logits"), (A, "A"), (W, "W"),
+                 (base_logits, "base_logits"),
                  (target_logits, "target_logits"), (target_row_offsets, "target_row_offsets"),
                  (temperature, "temperature")):
         _dev(t, n)
     B, K, V = base_logits.shape
-    r = A.shape[1]
+    if A is None and W is None:
+        r, fdt = 1, _dtype(base_logits, "base_logits")
+    else:
+        _dev(A, "A")
+        _dev(W, "W")
+        r, fdt = A.shape[1], _dtype(A, "A")
     if target_logits.dtype != base_logits.dtype:
         raise DsparkError(DSPARK_ERR_INVALID_ARG, "target and base logits must share a dtype")
     if target_row_offsets.dtype != torch.int64 or target_row_offsets.numel() < B:
@@ -248,7 +254,7 @@ def dspark_verify(draft_tokens, prev_token, draft_logp, draft_lse, base_logits, 
     _check(lib().dspark_verify(
         _ptr(draft_tokens), _ptr(prev_token), _ptr(draft_logp), _ptr(draft_lse),
         _ptr(base_logits), _dtype(base_logits, "base_logits"), _ptr(A), _ptr(W),
-        _dtype(A, "A"), _ptr(target_logits), n_rows, _ptr(target_row_offsets), _ptr(lengths),
+        fdt, _ptr(target_logits), n_rows, _ptr(target_row_offsets), _ptr(lengths),
         _ptr(temperature), int(seed) & (2**64 - 1), B, K, V, r, _ptr(accepted),
         _ptr(next_token), _ptr(row_lse_t), _ptr(row_logratio), _ptr(workspace),
         workspace.numel(), _stream(stream, dev)))

@@ -154,8 +154,10 @@ dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_tok
     if (!prev_token || !target_logits || !target_row_offsets || !temperature || !accepted ||
         !next_token)
         return fail(DSPARK_ERR_INVALID_ARG, "verify: NULL required pointer");
-    if (K > 0 && (!draft_tokens || !draft_logp || !draft_lse || !base_logits || !A || !W))
+    if (K > 0 && (!draft_tokens || !draft_logp || !draft_lse || !base_logits))
         return fail(DSPARK_ERR_INVALID_ARG, "verify: NULL draft input");
+    if ((A == nullptr) != (W == nullptr))
+        return fail(DSPARK_ERR_INVALID_ARG, "verify: A and W must both be set or both NULL");
     if (static_cast<int64_t>(B) * (K + 1) > (int64_t{1} << 31))
         return fail(DSPARK_ERR_INVALID_ARG, "verify: B*(K+1) too large");
     const size_t need = dspark::verify_workspace_bytes(B, K, V, r);

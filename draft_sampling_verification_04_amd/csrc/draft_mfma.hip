@@ -22,6 +22,7 @@
 //     v = start + 32 (i / 4) + 16 (l / 32) + 4 (i % 4) + t, t = 0..3: exactly
 //     one Philox block, and the lane's 64 entries are four runs of 16.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -1259,9 +1260,10 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
 
 constexpr int kMaxLds = 160 * 1024;
 
-// Devices a kernel's LDS limit has been raised on (the attribute is per device).
+// Devices a kernel's LDS limit has been raised on (the attribute is per device;
+// raising it twice is harmless, so concurrent first calls need no lock).
 struct LdsReady {
-    bool dev[64] = {};
+    std::atomic<bool> dev[64] = {};
 };
 
 // Let the kernel take all the LDS its static arrays leave, once per device.
@@ -1271,29 +1273,31 @@ hipError_t allow_big_lds(Kern* kern, LdsReady& ready) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     const bool track = dev >= 0 && dev < 64;
-    if (track && ready.dev[dev]) return hipSuccess;
+    if (track && ready.dev[dev].load(std::memory_order_acquire)) return hipSuccess;
     hipFuncAttributes fa;
     e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             kMaxLds - static_cast<int>(fa.sharedSizeBytes));
-    if (e == hipSuccess && track) ready.dev[dev] = true;
+    if (e == hipSuccess && track) ready.dev[dev].store(true, std::memory_order_release);
     return e;
 }
 
+// Compute units of the current device, queried once per device (a racing
+// first query stores the same value).
 int device_cus() {
-    static int cus[64] = {};
+    static std::atomic<int> cus[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 // `lds` is the dynamic LDS of the launch (0 for a kernel whose W buffers are
@@ -1405,7 +1409,7 @@ bool mfma_supported(const DraftArgs& a) {
 }
 
 bool residual_mfma_supported(const VerifyArgs& a) {
-    return a.factor_dt == DSPARK_BF16 && a.logit_dt == DSPARK_BF16 && a.r % 16 == 0 &&
+    return a.A != nullptr && a.factor_dt == DSPARK_BF16 && a.logit_dt == DSPARK_BF16 && a.r % 16 == 0 &&
            a.r <= 256 && a.V % 8 == 0 && aligned16(a.base) && aligned16(a.A) &&
            aligned16(a.W) && aligned16(a.target);
 }

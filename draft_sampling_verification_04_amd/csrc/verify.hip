@@ -317,7 +317,7 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
         const int g = e / r;
         const int i = e - g * r;
         float a = 0.0f;
-        if (g < nrows) {
+        if (A != nullptr && g < nrows) {
             const int b = ws.list[slot0 + g];
             const int js = accepted[b] + 1;
             const int p = clamp_token(
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
     for (int g = 0; g < kResRows; ++g)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[g][t] = 0.0f;
-    if (v0 < V) {
+    if (A != nullptr && v0 < V) {  // A = W = NULL: no transition bias
         for (int i = 0; i < r; ++i) {
             const FT* wr = W + static_cast<size_t>(i) * V + v0;
             float w[4];

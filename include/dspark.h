@@ -26,8 +26,12 @@
  * Random draws: Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit seed
  * (low word, high word) with counter (v >> 2, position, request, tag), word
  * v & 3; uniform u = ((w >> 9) + 0.5) * 2^-23; Gumbel G = -log(-log u).
- * Tags: 0 draft Gumbel (position k = 1..K), 1 accept uniform (v = 0,
- * position j), 2 residual or bonus Gumbel (position of the resampled row).
+ * Every token draw is a Gumbel-max over the whole vocabulary with one draw per
+ * entry v.  These are the only tags the library uses:
+ *   0  draft Gumbel of entry v at position k = 1..K;
+ *   1  accept uniform of position j (v = 0);
+ *   2  Gumbel of entry v for the residual, fallback or bonus draw at the
+ *      position of the row it is drawn from.
  * Temperature: per request; T > 0 multiplies logits by the fp32 reciprocal
  * 1/T on both the draft and the target side, T == 0 is greedy on both sides
  * (argmax, ties to the smallest index).  T must be finite and >= 0.
@@ -92,10 +96,8 @@ size_t dspark_draft_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r);
  *   draft_logp   [B, K] float           log p_d(x_k) = z_{x_k} - lse_d (0 for T == 0); nullable
  *   draft_lse    [B, K] float           lse_d = log sum_v exp(z_v), z = (base + bias)/T
  *                                       (the row maximum for T == 0); nullable
- * Draws: for T > 0, x_k ~ p_d by Gumbel-max in two levels with Philox4x32-10
- * words keyed by (seed, request, position k): blocks of 64 consecutive entries
- * compete with log(block mass) + G (tag 3, word = block index), then x_k is the
- * Gumbel-argmax of z inside the winning block (tag 0, word = entry); for
+ * Draws: for T > 0, x_k = argmax_v z_v + G_v with the tag-0 draw of each entry
+ * v, keyed by (seed, request, position k, v): an exact sample of p_d; for
  * T == 0, x_k is the argmax of base + bias (smallest index on ties).
  * Sizes: B >= 0, K >= 0 (either 0 is a no-op), 1 <= V < 2^30, 1 <= r <= 1024.
  * A = W = NULL drafts without the Markov head: p_d(x_k) = softmax(base_k / T)
@@ -149,7 +151,10 @@ size_t dspark_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r)
  *   draft_tokens [B, K] int32, prev_token [B] int32, draft_logp / draft_lse
  *   [B, K] float: as written by dspark_draft_sample.
  *   base_logits [B, K, V], A [V, r], W [r, V]: the draft inputs (the draft row
- *   at the first rejected position is recomputed for the residual).
+ *   at the first rejected position is recomputed for the residual).  A = W =
+ *   NULL verifies tokens drafted without the Markov head (zero transition
+ *   bias, as dspark_draft_sample with A = W = NULL); passing only one of them
+ *   is ERR_INVALID_ARG.
  *   target_logits [rows, V] logit_dt: request b's verify rows j = 1 .. L_b + 1
  *   are rows target_row_offsets[b] + j - 1 (row L_b + 1 gives the bonus).
  *   Dense layout: offsets b * (K + 1); ragged layout: dspark_schedule's
@@ -159,6 +164,12 @@ size_t dspark_verify_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r)
  *   lengths [B] int32 in [0, K]: verified draft tokens per request; NULL = K.
  *   Out-of-range lengths are clamped to [0, K]; token ids are clamped to
  *   [0, V) before they index A or a target row.
+ * Draws: accept x_j iff log u_j < log p_t(x_j) - log p_d(x_j) (tag 1); after
+ * the first rejection, next = argmax over the entries with p_t > p_d of
+ * log(p_t - p_d) + G_v (tag 2, position j*), or, if no entry is positive
+ * (rounding only), argmax_v y_v + G_v with the same draws; after a full
+ * acceptance, next = argmax_v y_v + G_v on row L_b + 1 (tag 2, position
+ * L_b + 1).  T == 0: argmax of the target row.
  * Outputs (device):
  *   accepted    [B] int32   a_b = number of leading accepted draft tokens (<= L_b)
  *   next_token  [B] int32   residual sample at a_b + 1 when a_b < L_b, else the bonus
@@ -193,8 +204,14 @@ dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_tok
  * above (no page defines it).  While a session is open, each launch of a
  * kernel whose bit (1 << dspark_kernel) is in kernel_mask is bracketed by two
  * events recorded on its launch stream; the time between them is the launch's
- * duration on that stream.  The session is process-wide: one at a time, from
- * any thread.
+ * duration on that stream.
+ * The session is the library's one piece of process-wide state (a mutex, an
+ * event pool created by begin and destroyed by end, and launch counters): one
+ * session at a time, opened and closed from any thread; launches from any
+ * thread or stream are recorded while it is open.  With no session open the
+ * three calls above touch no state beyond their arguments and are re-entrant
+ * across threads and streams (apart from per-device caches of the device's
+ * compute-unit count and kernel LDS limits, filled once with atomics).
  */
 typedef enum dspark_kernel {
     DSPARK_KERNEL_DRAFT_STRIP = 0,       /* draft: bias GEMM + logits + block keys over a vocab strip */

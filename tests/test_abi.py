@@ -109,6 +109,11 @@ def test_verify_validation(L):
     # K = 0: draft inputs may be NULL (only the bonus row is used); still needs workspace
     assert call(K=0, tok=None, logp=None, lse=None, base=None, A=None, W=None,
                 wsb=1) == bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
+    # factors: both (Markov head) or neither (zero bias); one alone is rejected
+    assert call(A=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert call(W=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert b"A and W" in L.dspark_last_error()
+    assert call(A=None, W=None, wsb=10) == bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_binding_rejects_host_tensors():
