@@ -118,9 +118,14 @@ def host_cpu():
     return model, os.cpu_count()
 
 
-def cpu_baseline(w, inp, seed, n_req):
+def cpu_baseline(w, inp, seed, n_req, target, row_off, lengths, gpu):
     """Time the oracle (single-threaded C) on n_req requests of the same
-    workload: full draft of K tokens plus full verification."""
+    workload: full draft of K tokens plus verification of the request's
+    scheduled prefix over the same target rows the GPU read.  The oracle's
+    results are then compared with the GPU's (gpu = tokens, accepted, next
+    token) request by request: a divergence is allowed only where the oracle
+    reports a near-tie (top-2 perturbed values, or |log u - log ratio|,
+    within 1e-5)."""
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import numpy as np
     import oracle as orc
@@ -129,23 +134,44 @@ def cpu_baseline(w, inp, seed, n_req):
     W = inp["W"].float().cpu().numpy()
     prev = inp["prev"].cpu().numpy()
     temp = inp["temp"].cpu().numpy()
+    ro = row_off.cpu().numpy()
+    Ls = lengths.cpu().numpy()
+    g_tok, g_acc, g_nxt = (t.cpu().numpy() for t in gpu)
     # sample requests with T > 0 (the expensive, sampled case) first
     order = sorted(range(w.B), key=lambda b: (temp[b] == 0.0, b))[:n_req]
     t_total = 0.0
+    near = matched = 0
     for b in order:
         base = inp["base"][b].float().cpu().numpy()
-        rows = inp["target"][b].float().cpu().numpy()
+        rows = target[int(ro[b]):int(ro[b]) + int(Ls[b]) + 1].float().cpu().numpy()
         t0 = time.perf_counter()
-        tok, _, _, _ = orc.draft_request(base, A, W, int(prev[b]), float(temp[b]), seed, b)
-        orc.verify_request(tok, int(prev[b]), base, A, W, rows, w.K, float(temp[b]), seed, b)
+        tok, _, _, gap = orc.draft_request(base, A, W, int(prev[b]), float(temp[b]), seed, b)
+        v = orc.verify_request(tok, int(prev[b]), base, A, W, rows, int(Ls[b]), float(temp[b]),
+                               seed, b)
         t_total += time.perf_counter() - t0
+        if (g_tok[b] != tok).any():
+            k = int(np.nonzero(g_tok[b] != tok)[0][0])
+            if not gap[k] < 1e-5:
+                raise AssertionError(f"oracle/GPU draft mismatch at request {b}, position {k}")
+            near += 1
+        elif g_acc[b] != v["accepted"] or g_nxt[b] != v["next_token"]:
+            if not min(v["accept_gap"], v["next_gap"]) < 1e-5:
+                raise AssertionError(f"oracle/GPU verify mismatch at request {b}")
+            near += 1
+        else:
+            matched += 1
     tokens = n_req * w.K
     model, ncpu = host_cpu()
-    return dict(value=round(tokens / t_total, 2), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{n_req} request(s) of {w.name} (K={w.K}, V={w.V}, r={w.r}), full draft + "
-                       f"verify of K tokens each, T>0 requests first; {t_total:.2f} s on one "
-                       f"thread of {model} ({ncpu} logical CPUs); requests are independent, so "
-                       f"the rate does not depend on B")
+    base_line = dict(value=round(tokens / t_total, 2), unit="tokens/s", cores=1, kind="oracle",
+                     sample=f"{n_req} request(s) of {w.name} (K={w.K}, V={w.V}, r={w.r}), full "
+                            f"draft of K tokens + verification of the scheduled prefix each, T>0 "
+                            f"requests first; {t_total:.2f} s on one thread of {model} ({ncpu} "
+                            f"logical CPUs); requests are independent, so the rate does not "
+                            f"depend on B")
+    parity = dict(requests=n_req, bit_exact=matched, near_ties=near,
+                  rule="tokens, accepted length and next token equal, or an oracle near-tie "
+                       "(< 1e-5)")
+    return base_line, parity
 
 
 def markov_vs_parallel(d, inp, seed, reps=10):
@@ -416,12 +442,11 @@ def main():
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
     seed = 20260627
-    inp = inputs.make_inputs(w, dev, seed=1)
+    inp = inputs.make_inputs(w, dev, seed=1, with_target=not w.ragged)
     conf, _ = inputs.make_confidence(w, dev, seed=1)
     B, K, V, r = w.B, w.K, w.V, w.r
     budget = w.budget if w.budget else B * (K + 1)
     cn, ct = w.curve()
-    target = inp["target"].reshape(-1, V)
 
     # outputs and workspaces allocated once, outside the timed region
     tok = torch.empty((B, K), dtype=torch.int32, device=dev)
@@ -437,6 +462,21 @@ def main():
                        device=dev)
     ws_v = torch.empty(d.dspark_verify_workspace_bytes(B, K, V, r), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+
+    # The schedule depends on the confidences alone, so one call before timing
+    # lays out the verify rows: ragged workloads get target rows for the
+    # scheduled prefixes only, at the schedule's row offsets; dense ones read
+    # the [B, K+1, V] tensor at offsets b (K+1) with the scheduled lengths.
+    d.dspark_schedule(conf, budget, cn, ct, lengths=L, row_offsets=offs, survival=surv,
+                      workspace=ws_s)
+    torch.cuda.synchronize()
+    if w.ragged:
+        target = inputs.ragged_target(w, inp["base"], L, offs, dev, seed=1)
+        vofs = offs
+    else:
+        target = inp["target"].reshape(-1, V)
+        vofs = inputs.dense_offsets(B, K, dev)
+    torch.cuda.synchronize()
 
     if args.copy_probe_mib > 0:
         # reference kernel for counter scaling: reads and writes exactly N MiB
@@ -459,7 +499,7 @@ def main():
         if events:
             events[2].record(stream)
         d.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"], inp["W"], target,
-                        offs, inp["temp"], seed, L, accepted=acc, next_token=nxt,
+                        vofs, inp["temp"], seed, L, accepted=acc, next_token=nxt,
                         row_outputs=False, workspace=ws_v)
         if events:
             events[3].record(stream)
@@ -509,40 +549,54 @@ def main():
     emitted = int(acc.sum()) + B
     rows_read = target_rows_read(L.cpu().tolist(), acc.cpu().tolist(), K)
     tokens_per_s = B * K / (ms_step / 1e3)
+    prof_steps = max(1, min(args.steps, 5))
 
     es = 2 if w.dtype == torch.bfloat16 else 4
-    # algorithmic bytes and flops per launch of the draft strip kernel (one
-    # draft step): the base-logit slice of every request plus all of W (every
-    # step multiplies by the whole of W), plus the gathered rows of A
-    strip_bytes = es * (B * V + r * V + B * r)
+    # Algorithmic bytes (what the method must read at least once):
+    # draft call: every base logit plus W once (the K steps share it) plus the
+    # gathered A rows; per launch of the draft strip kernel (one draft step)
+    # that is a K-th of the base-plus-W figure.
+    draft_bytes = es * (B * K * V + r * V + K * B * r)
+    strip_bytes = draft_bytes / K
     strip_flops = 2.0 * B * r * V
     achieved_gbs = strip_bytes / strip_avg_s / 1e9
     traffic = stored_traffic()
-
-    # algorithmic bytes of the verify rows kernel per step (several launches):
-    # every target row it reads, once
+    # verify rows: every target row read under the early-exit schedule, once
     rows_ms, _, rows_timed = per_kernel["verify_rows"]
-    prof_steps = max(1, min(args.steps, 5))
     rows_bytes = es * rows_read * V
+    # residual strip: a sampled rejection reads its recomputed draft row and
+    # its target row, a sampled full acceptance its bonus row; W once
+    sampled = inp["temp"] > 0
+    n_rej = int(((acc < L) & sampled).sum())
+    n_bonus = int(((acc >= L) & sampled).sum())
     res_ms, _, res_timed = per_kernel["residual_strip"]
-    rejected = int(((acc < L) & (inp["temp"] > 0)).sum())  # sampled rejections only
-    res_bytes = es * (2 * rejected * V + r * V + rejected * r)
+    res_bytes = es * ((2 * n_rej + n_bonus) * V + r * V + (n_rej + n_bonus) * r)
+    step_bytes = draft_bytes + rows_bytes + res_bytes
 
     def gbs(nbytes, ms, n):
+        """GB/s of nbytes moved per unit, at ms total over n units."""
         return round(nbytes / (ms / max(n, 1) / 1e3) / 1e9, 1) if n else None
+
+    def frac(g):
+        return round(g / HBM_PEAK_GBS, 4) if g is not None else None
 
     kernels = {}
     for k, (ms, n, nt) in per_kernel.items():
-        kernels[k] = {"launches_per_step": round(n / max(1, min(args.steps, 5)), 2),
+        kernels[k] = {"launches_per_step": round(n / prof_steps, 2),
                       "avg_launch_us": round(1e3 * ms / nt, 2) if nt else None}
+    g_strip = gbs(strip_bytes, *per_kernel["draft_strip"][::2])
     kernels["draft_strip"].update(
-        hbm_gbs=gbs(strip_bytes, *per_kernel["draft_strip"][::2]),
+        bytes_per_launch=int(strip_bytes), hbm_gbs=g_strip, hbm_frac=frac(g_strip),
         mfma_tflops=round(strip_flops / (per_kernel["draft_strip"][0] /
                                          max(per_kernel["draft_strip"][2], 1) / 1e3) / 1e12, 1))
-    kernels["verify_rows"].update(hbm_gbs=gbs(rows_bytes, rows_ms, prof_steps),
+    g_rows = gbs(rows_bytes, rows_ms, prof_steps)
+    kernels["verify_rows"].update(bytes_per_step=rows_bytes, hbm_gbs=g_rows, hbm_frac=frac(g_rows),
                                   target_rows_read_per_step=rows_read,
                                   target_rows_scheduled_per_step=verified + B)
-    kernels["residual_strip"].update(hbm_gbs=gbs(res_bytes, res_ms, res_timed))
+    g_res = gbs(res_bytes, res_ms, prof_steps)
+    kernels["residual_strip"].update(bytes_per_step=res_bytes, hbm_gbs=g_res, hbm_frac=frac(g_res),
+                                     sampled_rejections=n_rej, sampled_bonus_rows=n_bonus)
+    g_step = step_bytes / (ms_step / 1e3) / 1e9
 
     model, ncpu = host_cpu()
     out = {
@@ -560,8 +614,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "K": K, "V": V, "r": r,
                    "temperatures": list(w.temps), "budget_tokens": budget,
-                   "verify": "every drafted token; target rows read up to each request's "
-                             "first rejection (position launches "
+                   "target_rows": "ragged, scheduled prefixes only" if w.ragged
+                   else "dense [B, K+1, V] at offsets b(K+1)",
+                   "verify": ("every drafted token" if not w.budget else "scheduled prefixes")
+                             + "; target rows read up to each request's first rejection "
+                               "(position launches "
                              + ", ".join(f"{a}-{b}" for a, b in verify_position_launches(K))
                              + ")",
                    "parallelism": "single GPU"},
@@ -573,12 +630,16 @@ def main():
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": "draft_strip_mfma_rk<8,16>" if r == 256 else "draft_strip_mfma",
-            "algorithmic_bytes_per_launch": strip_bytes,
+            "algorithmic_bytes_per_launch": int(strip_bytes),
+            "bytes_rule": "(base logits + W once + gathered A rows of one draft call) / K",
             "avg_launch_us": round(strip_avg_s * 1e6, 2),
             "launches_timed": strip_timed,
             "timed_steps": f"last {inst} of {args.steps}",
             "mfma_tflops": round(strip_flops / strip_avg_s / 1e12, 1),
             "mfma_frac": round(strip_flops / strip_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "step": {"bytes": int(step_bytes), "achieved": round(g_step, 1),
+                     "frac": round(g_step / HBM_PEAK_GBS, 4),
+                     "bytes_rule": "draft call + verify rows read + residual/bonus rows"},
         },
         "phases_ms": {"draft": round(draft_ms, 4), "schedule": round(sched_ms, 4),
                       "verify": round(verify_ms, 4)},
@@ -592,9 +653,12 @@ def main():
     if args.sps_curve:
         out["sps_curve"] = sps_curve(d, inputs, dev)
     if args.calibration:
+        if w.ragged:
+            raise SystemExit("--calibration needs a workload with dense target rows")
         out["calibration"] = calibration(d, inp, w, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, seed, args.cpu_requests)
+        out["cpu_baseline"], out["oracle_parity"] = cpu_baseline(
+            w, inp, seed, args.cpu_requests, target, vofs, L, (tok, acc, nxt))
     print(json.dumps(out), flush=True)
 
 

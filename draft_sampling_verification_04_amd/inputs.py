@@ -13,9 +13,11 @@ with the shapes and value distributions of the five named workloads:
   conf_sched  B=1024, K=16, V=151936, r=256, bf16, qwen3_4b distributions,
               confidences Beta(mu*20, (1-mu)*20) with mu falling linearly from 0.9
               to 0.3 / 0.6 / 0.8 for a 40/30/30 chat/math/code mix, budget 4096,
-              latency curve flat to 4096 tokens then slope 1.5 per 4096
+              latency curve flat to 4096 tokens then slope 1.5 per 4096; target
+              rows generated for the scheduled prefixes only (ragged)
   high_conc   B=2048, K=16, V=131072, r=256, bf16, long_draft distributions,
-              mixed T, budget 8192 (same curve shape), dense target rows
+              mixed T, budget 8192 (same curve shape), dense target rows [B, K+1, V]
+              read at offsets b (K+1) with the scheduled lengths
 
 The target logits of row j are the backbone logits of an extended draft block
 (K+1 rows) plus Gaussian noise; the transition bias is not part of them.
@@ -43,6 +45,7 @@ class Workload:
     noise_hi: float
     temps: tuple
     budget: int = 0  # 0: verify every drafted token
+    ragged: bool = False  # target rows for the scheduled prefixes only (else dense [B, K+1, V])
 
     def curve(self):
         """Step-latency curve: flat up to `budget` tokens, then +1.5x per `budget`."""
@@ -58,7 +61,7 @@ WORKLOADS = {
     "long_draft": Workload("long_draft", 256, 16, 151936, 256, torch.bfloat16, 3.0, 8.0, 0.05,
                            0.5, 2.0, (0.0, 0.7, 1.0)),
     "conf_sched": Workload("conf_sched", 1024, 16, 151936, 256, torch.bfloat16, 3.0, 8.0, 0.05,
-                           1.0, 1.0, (1.0,), budget=4096),
+                           1.0, 1.0, (1.0,), budget=4096, ragged=True),
     "high_conc": Workload("high_conc", 2048, 16, 131072, 256, torch.bfloat16, 3.0, 8.0, 0.05,
                           0.5, 2.0, (0.0, 0.7, 1.0), budget=8192),
 }

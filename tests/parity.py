@@ -11,6 +11,9 @@ Comparison rules (from the hot path's parity bar):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -35,12 +38,34 @@ def close(a, b, tol) -> bool:
 
 
 class Tally:
+    """compared: draft positions and verify requests that matched; near_ties:
+    divergences excused by a near-tie; draft_clean / verify_clean: requests
+    whose whole draft (every position) / verify result matched."""
+
     def __init__(self):
         self.near_ties = 0
         self.compared = 0
+        self.draft_clean = 0
+        self.verify_clean = 0
 
     def __repr__(self):
-        return f"Tally(compared={self.compared}, near_ties={self.near_ties})"
+        return (f"Tally(compared={self.compared}, near_ties={self.near_ties}, "
+                f"draft_clean={self.draft_clean}, verify_clean={self.verify_clean})")
+
+
+def workers() -> int:
+    """Oracle threads: the oracle is single-threaded C called through ctypes
+    (which releases the GIL), so independent requests run side by side, at
+    most 16 at a time."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _map(fn, idx):
+    idx = list(idx)
+    if len(idx) <= 1:
+        return {b: fn(b) for b in idx}
+    with ThreadPoolExecutor(min(workers(), len(idx))) as ex:
+        return dict(zip(idx, ex.map(fn, idx)))
 
 
 def oracle_draft(orc, inp, idx, seed):
@@ -49,11 +74,9 @@ def oracle_draft(orc, inp, idx, seed):
     W = np32(inp["W"])
     prev = inp["prev"].cpu().numpy()
     temp = inp["temp"].cpu().numpy()
-    out = {}
-    for b in idx:
-        base = np32(inp["base"][b])
-        out[b] = orc.draft_request(base, A, W, int(prev[b]), float(temp[b]), seed, int(b))
-    return out
+    bases = {b: np32(inp["base"][b]) for b in idx}
+    return _map(lambda b: orc.draft_request(bases[b], A, W, int(prev[b]), float(temp[b]), seed,
+                                            int(b)), idx)
 
 
 def compare_draft(gpu_tok, gpu_logp, gpu_lse, ora, temp, tol, tally=None):
@@ -77,6 +100,7 @@ def compare_draft(gpu_tok, gpu_logp, gpu_lse, ora, temp, tol, tally=None):
             tally.compared += 1
         if not diverged:
             clean.add(b)
+            tally.draft_clean += 1
     return clean
 
 
@@ -87,12 +111,10 @@ def oracle_verify(orc, inp, idx, tokens, target_rows, lengths, seed):
     W = np32(inp["W"])
     prev = inp["prev"].cpu().numpy()
     temp = inp["temp"].cpu().numpy()
-    out = {}
-    for b in idx:
-        base = np32(inp["base"][b])
-        out[b] = orc.verify_request(tokens[b], int(prev[b]), base, A, W, target_rows[b],
-                                    int(lengths[b]), float(temp[b]), seed, int(b))
-    return out
+    bases = {b: np32(inp["base"][b]) for b in idx}
+    return _map(lambda b: orc.verify_request(tokens[b], int(prev[b]), bases[b], A, W,
+                                             target_rows[b], int(lengths[b]), float(temp[b]),
+                                             seed, int(b)), idx)
 
 
 def compare_verify(gpu_acc, gpu_next, gpu_lse_rows, gpu_ratio_rows, row_off, ora, tol,
@@ -118,4 +140,5 @@ def compare_verify(gpu_acc, gpu_next, gpu_lse_rows, gpu_ratio_rows, row_off, ora
             tally.near_ties += 1
             continue
         tally.compared += 1
+        tally.verify_clean += 1
     return tally

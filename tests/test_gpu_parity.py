@@ -31,16 +31,6 @@ def inputs():
     return m
 
 
-def _sample_requests(temp, n_per_temp=1, extra=()):
-    """A few requests covering every temperature present (plus extra ones)."""
-    t = temp.cpu().numpy()
-    idx = []
-    for v in sorted(set(t.tolist())):
-        idx += [int(i) for i in np.nonzero(t == v)[0][:n_per_temp]]
-    idx += [int(i) for i in extra if i < len(t)]
-    return sorted(set(idx))
-
-
 def _draft_and_verify(dsp, orc, inp, seed, idx, tol, lengths=None, row_off=None, target=None):
     """GPU draft on all requests, oracle on idx; then verify with the oracle's
     draft for idx (GPU draft elsewhere) and compare."""
@@ -113,14 +103,68 @@ def test_small_shapes_parity(dsp, orc, inputs, V, r, K, B, ldt, fdt):
     assert tally.compared >= 1
 
 
+def _spread_requests(temp, n_min=16, extra=()):
+    """At least n_min requests, the same number at every temperature present
+    (spread over the batch), plus the first and last request."""
+    t = temp.cpu().numpy()
+    vals = sorted(set(t.tolist()))
+    per = -(-n_min // len(vals))
+    idx = [0, len(t) - 1]
+    for v in vals:
+        cand = np.nonzero(t == v)[0]
+        pick = np.linspace(0, len(cand) - 1, min(per, len(cand))).round().astype(int)
+        idx += [int(cand[i]) for i in pick]
+    idx += [int(i) for i in extra if i < len(t)]
+    return sorted(set(idx))
+
+
 @pytest.mark.parametrize("name", ["qwen3_4b", "long_draft", "high_conc"])
 def test_full_size_sampled_parity(dsp, orc, inputs, name):
+    """Full-size workloads, every temperature: at least 16 requests compared
+    with the oracle at the real V, r and K.  At most one near-tie divergence
+    is expected over the sample, so every other request matches whole."""
     w = inputs.WORKLOADS[name]
     inp = inputs.make_inputs(w, "cuda", seed=1)
-    idx = _sample_requests(inp["temp"], 1, extra=(w.B - 1,))
+    idx = _spread_requests(inp["temp"], 16)
     tally, _ = _draft_and_verify(dsp, orc, inp, 5, idx, P.tol_for(w.dtype))
-    print(name, idx, tally)
-    assert tally.compared >= 1
+    temps = sorted(set(inp["temp"].cpu().numpy()[idx].tolist()))
+    print(name, len(idx), temps, tally)
+    assert len(idx) >= 16 and temps == sorted(set(np.float32(w.temps).tolist()))
+    assert tally.near_ties <= 1
+    assert tally.draft_clean >= len(idx) - 1 and tally.verify_clean >= len(idx) - 1
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_high_conc_pipeline_parity(dsp, orc, inputs):
+    """Draft -> schedule -> verify of the scheduled prefixes over the dense
+    target tensor ([B, K+1, V], offsets b (K+1)) at B=2048, V=131072, budget
+    8192; the sampled requests span every scheduled length present."""
+    w = inputs.WORKLOADS["high_conc"]
+    inp = inputs.make_inputs(w, "cuda", seed=4)
+    conf, _ = inputs.make_confidence(w, "cuda", seed=4)
+    cn, ct = w.curve()
+    L, offs, S = dsp.dspark_schedule(conf, w.budget, cn, ct)
+    torch.cuda.synchronize()
+    oL, ooffs, oS, n = orc.schedule(conf.cpu().numpy(), w.budget, np.array(cn), np.array(ct))
+    np.testing.assert_array_equal(S.cpu().numpy(), oS)
+    np.testing.assert_array_equal(L.cpu().numpy(), oL)
+    np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+    Lc = oL
+    assert int(ooffs[-1]) <= w.budget and Lc.min() < Lc.max()
+    # one request per distinct length (up to 16), then the first and last
+    idx = [0, w.B - 1]
+    for v in sorted(set(Lc.tolist())):
+        idx.append(int(np.nonzero(Lc == v)[0][0]))
+    rng = np.random.default_rng(4)
+    while len(set(idx)) < 16:
+        idx.append(int(rng.integers(w.B)))
+    idx = sorted(set(idx))
+    dense = inputs.dense_offsets(w.B, w.K, "cuda")
+    tally, _ = _draft_and_verify(dsp, orc, inp, 13, idx, P.tol_for(w.dtype), lengths=L,
+                                 row_off=dense, target=inp["target"].reshape(-1, w.V))
+    print(len(idx), sorted(set(Lc[idx].tolist())), tally)
+    assert tally.near_ties <= 1 and tally.verify_clean >= len(idx) - 1
     del inp
     torch.cuda.empty_cache()
 
