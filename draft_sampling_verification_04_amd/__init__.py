@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     DsparkError,
     LIB_PATH,
     dspark_draft_sample,
+    dspark_draft_sample_noalloc,
     dspark_draft_workspace_bytes,
     dspark_profile_begin,
     dspark_profile_end,

@@ -64,6 +64,9 @@ def lib():
         L.dspark_draft_sample.restype = ctypes.c_int
         L.dspark_draft_sample.argtypes = [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _U64,
                                           _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
+        L.dspark_draft_sample_noalloc.restype = ctypes.c_int
+        L.dspark_draft_sample_noalloc.argtypes = [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P,
+                                                  _U64, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
         L.dspark_schedule_workspace_bytes.restype = _SZ
         L.dspark_schedule_workspace_bytes.argtypes = [_I32, _I32]
         L.dspark_schedule.restype = ctypes.c_int
@@ -141,11 +144,8 @@ def dspark_verify_workspace_bytes(B, K, V, r) -> int:
     return int(lib().dspark_verify_workspace_bytes(B, K, V, r))
 
 
-def dspark_draft_sample(base_logits, A, W, prev_token, temperature, seed, *, draft_tokens=None,
-                        draft_logp=None, draft_lse=None, workspace=None, stream=None):
-    """Markov-head draft of K tokens per request; returns (tokens, logp, lse).
-    A = W = None drafts without the Markov head (every position from its own
-    base logits, all in one pass)."""
+def _draft_marshal(base_logits, A, W, prev_token, temperature, draft_tokens, draft_logp,
+                   draft_lse):
     _dev(base_logits, "base_logits")
     _dev(prev_token, "prev_token")
     _dev(temperature, "temperature")
@@ -168,6 +168,17 @@ def dspark_draft_sample(base_logits, A, W, prev_token, temperature, seed, *, dra
         draft_logp = torch.empty((B, K), dtype=torch.float32, device=dev)
     if draft_lse is None:
         draft_lse = torch.empty((B, K), dtype=torch.float32, device=dev)
+    return (B, K, V, r, fdt, draft_tokens, draft_logp, draft_lse)
+
+
+def dspark_draft_sample(base_logits, A, W, prev_token, temperature, seed, *, draft_tokens=None,
+                        draft_logp=None, draft_lse=None, workspace=None, stream=None):
+    """Markov-head draft of K tokens per request; returns (tokens, logp, lse).
+    A = W = None drafts without the Markov head (every position from its own
+    base logits, all in one pass)."""
+    B, K, V, r, fdt, draft_tokens, draft_logp, draft_lse = _draft_marshal(
+        base_logits, A, W, prev_token, temperature, draft_tokens, draft_logp, draft_lse)
+    dev = base_logits.device
     nbytes = dspark_draft_workspace_bytes(B, K, V, r)
     workspace = _workspace(workspace, nbytes, dev)
     _check(lib().dspark_draft_sample(
@@ -175,6 +186,21 @@ def dspark_draft_sample(base_logits, A, W, prev_token, temperature, seed, *, dra
         _ptr(prev_token), _ptr(temperature), int(seed) & (2**64 - 1), B, K, V, r,
         _ptr(draft_tokens), _ptr(draft_logp), _ptr(draft_lse), _ptr(workspace),
         workspace.numel(), _stream(stream, dev)))
+    return draft_tokens, draft_logp, draft_lse
+
+
+def dspark_draft_sample_noalloc(base_logits, A, W, prev_token, temperature, seed, *,
+                                draft_tokens=None, draft_logp=None, draft_lse=None, stream=None):
+    """dspark_draft_sample on the library's fixed per-device scratch (no
+    workspace; the library allocates nothing).  Pass the output tensors to
+    allocate nothing on this side either."""
+    B, K, V, r, fdt, draft_tokens, draft_logp, draft_lse = _draft_marshal(
+        base_logits, A, W, prev_token, temperature, draft_tokens, draft_logp, draft_lse)
+    dev = base_logits.device
+    _check(lib().dspark_draft_sample_noalloc(
+        _ptr(base_logits), _dtype(base_logits, "base_logits"), _ptr(A), _ptr(W), fdt,
+        _ptr(prev_token), _ptr(temperature), int(seed) & (2**64 - 1), B, K, V, r,
+        _ptr(draft_tokens), _ptr(draft_logp), _ptr(draft_lse), _stream(stream, dev)))
     return draft_tokens, draft_logp, draft_lse
 
 

@@ -4,7 +4,15 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
+
+// Scratch memory of dspark_draft_sample_noalloc, one copy per device (loaded
+// with the code object; held until the process ends).  Host code never uses
+// this name as an address: it holds a host-side stand-in.  The device address
+// comes from hipGetSymbolAddress, once per device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[DSPARK_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -32,6 +40,65 @@ dspark_status hip_status(hipError_t e, const char* what) {
     return fail(DSPARK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch` per device
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device (with it current) and kept.
+hipError_t noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return hipSuccess;
+}
+
+// Validation shared by both draft entry points; fills everything in a but
+// the workspace.  Returns DSPARK_OK with *nothing = true for empty problems.
+dspark_status draft_checked(const char* who, const void* base_logits, dspark_dtype logit_dt,
+                            const void* A, const void* W, dspark_dtype factor_dt,
+                            const int32_t* prev_token, const float* temperature, uint64_t seed,
+                            int32_t B, int32_t K, int32_t V, int32_t r, int32_t* draft_tokens,
+                            float* draft_logp, float* draft_lse, void* stream,
+                            dspark::DraftArgs* a, bool* nothing) {
+    *nothing = false;
+    if (!valid_dtype(logit_dt) || !valid_dtype(factor_dt))
+        return fail(DSPARK_ERR_UNSUPPORTED_DTYPE, "%s: unsupported dtype (%d, %d)", who,
+                    static_cast<int>(logit_dt), static_cast<int>(factor_dt));
+    if (B < 0 || K < 0) return fail(DSPARK_ERR_INVALID_ARG, "%s: B=%d K=%d", who, B, K);
+    if (V < 1 || V >= (1 << 30)) return fail(DSPARK_ERR_INVALID_ARG, "%s: V=%d", who, V);
+    if (r < 1 || r > 1024) return fail(DSPARK_ERR_INVALID_ARG, "%s: r=%d", who, r);
+    if (B == 0 || K == 0) {
+        *nothing = true;
+        return ok();
+    }
+    if (!base_logits || !prev_token || !temperature || !draft_tokens)
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: NULL required pointer", who);
+    if ((A == nullptr) != (W == nullptr))
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: A and W must both be set or both NULL", who);
+    if (static_cast<int64_t>(B) * K > (int64_t{1} << 31))
+        return fail(DSPARK_ERR_INVALID_ARG, "%s: B*K too large", who);
+    *a = dspark::DraftArgs{base_logits, logit_dt,     A,         W,          factor_dt,
+                           prev_token,  temperature,  seed,      B,          K,
+                           V,           r,            draft_tokens, draft_logp, draft_lse,
+                           nullptr,     0,            static_cast<hipStream_t>(stream)};
+    if (!A && !dspark::parallel_supported(*a))
+        return fail(DSPARK_ERR_INVALID_ARG,
+                    "%s: drafting without factors needs bf16 logits, V %% 8 == 0 and a "
+                    "16-byte aligned base", who);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -51,34 +118,48 @@ dspark_status dspark_draft_sample(const void* base_logits, dspark_dtype logit_dt
                                   uint64_t seed, int32_t B, int32_t K, int32_t V, int32_t r,
                                   int32_t* draft_tokens, float* draft_logp, float* draft_lse,
                                   void* workspace, size_t ws_bytes, void* stream) {
-    if (!valid_dtype(logit_dt) || !valid_dtype(factor_dt))
-        return fail(DSPARK_ERR_UNSUPPORTED_DTYPE, "draft_sample: unsupported dtype (%d, %d)",
-                    static_cast<int>(logit_dt), static_cast<int>(factor_dt));
-    if (B < 0 || K < 0) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: B=%d K=%d", B, K);
-    if (V < 1 || V >= (1 << 30)) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: V=%d", V);
-    if (r < 1 || r > 1024) return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: r=%d", r);
-    if (B == 0 || K == 0) return ok();
-    if (!base_logits || !prev_token || !temperature || !draft_tokens)
-        return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: NULL required pointer");
-    if ((A == nullptr) != (W == nullptr))
-        return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: A and W must both be set or both NULL");
-    if (static_cast<int64_t>(B) * K > (int64_t{1} << 31))
-        return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: B*K too large");
+    dspark::DraftArgs a;
+    bool nothing = false;
+    dspark_status st = draft_checked("draft_sample", base_logits, logit_dt, A, W, factor_dt,
+                                     prev_token, temperature, seed, B, K, V, r, draft_tokens,
+                                     draft_logp, draft_lse, stream, &a, &nothing);
+    if (st != DSPARK_OK || nothing) return st;
     const size_t need = dspark::draft_workspace_bytes(B, K, V, r);
     if (!workspace || ws_bytes < need)
         return fail(DSPARK_ERR_WORKSPACE_TOO_SMALL, "draft_sample: workspace %zu < %zu bytes",
                     ws_bytes, need);
     if (!aligned(workspace, 256))
         return fail(DSPARK_ERR_INVALID_ARG, "draft_sample: workspace not 256-byte aligned");
-    dspark::DraftArgs a{base_logits, logit_dt,     A,         W,          factor_dt,
-                        prev_token,  temperature,  seed,      B,          K,
-                        V,           r,            draft_tokens, draft_logp, draft_lse,
-                        workspace,   ws_bytes,     static_cast<hipStream_t>(stream)};
-    if (!A && !dspark::parallel_supported(a))
-        return fail(DSPARK_ERR_INVALID_ARG,
-                    "draft_sample: drafting without factors needs bf16 logits, V %% 8 == 0 and a "
-                    "16-byte aligned base");
+    a.ws = workspace;
+    a.ws_bytes = ws_bytes;
     return hip_status(dspark::launch_draft(a), "draft_sample");
+}
+
+dspark_status dspark_draft_sample_noalloc(const void* base_logits, dspark_dtype logit_dt,
+                                          const void* A, const void* W, dspark_dtype factor_dt,
+                                          const int32_t* prev_token, const float* temperature,
+                                          uint64_t seed, int32_t B, int32_t K, int32_t V,
+                                          int32_t r, int32_t* draft_tokens, float* draft_logp,
+                                          float* draft_lse, void* stream) {
+    dspark::DraftArgs a;
+    bool nothing = false;
+    dspark_status st = draft_checked("draft_sample_noalloc", base_logits, logit_dt, A, W,
+                                     factor_dt, prev_token, temperature, seed, B, K, V, r,
+                                     draft_tokens, draft_logp, draft_lse, stream, &a, &nothing);
+    if (st != DSPARK_OK || nothing) return st;
+    const size_t need = dspark::draft_workspace_bytes(B, K, V, r);
+    const size_t have = DSPARK_NOALLOC_SCRATCH_BYTES;
+    if (need > have)
+        return fail(DSPARK_ERR_WORKSPACE_TOO_SMALL,
+                    "draft_sample_noalloc: these sizes need %zu bytes of scratch, more than the "
+                    "%zu the library holds per device; call dspark_draft_sample with a workspace",
+                    need, have);
+    void* ptr = nullptr;
+    hipError_t e = noalloc_scratch(&ptr);
+    if (e != hipSuccess) return hip_status(e, "draft_sample_noalloc: scratch address");
+    a.ws = ptr;
+    a.ws_bytes = have;
+    return hip_status(dspark::launch_draft(a), "draft_sample_noalloc");
 }
 
 size_t dspark_schedule_workspace_bytes(int32_t B, int32_t K) {

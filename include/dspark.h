@@ -41,7 +41,9 @@
  *     schedule curve arrays, which are HOST memory read during the call.
  *   - Layouts are row-major with the vocabulary innermost.
  *   - The library allocates nothing: scratch memory comes in `workspace`
- *     (size from the matching *_workspace_bytes query, 256-byte aligned).
+ *     (size from the matching *_workspace_bytes query, 256-byte aligned),
+ *     except for dspark_draft_sample_noalloc, whose scratch is a fixed
+ *     per-device array the library holds.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and returns without synchronising.  Calls on different
  *     streams with different workspaces may run concurrently.
@@ -113,6 +115,33 @@ dspark_status dspark_draft_sample(const void* base_logits, dspark_dtype logit_dt
                                   uint64_t seed, int32_t B, int32_t K, int32_t V, int32_t r,
                                   int32_t* draft_tokens, float* draft_logp, float* draft_lse,
                                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of the per-device scratch behind dspark_draft_sample_noalloc (64 MiB). */
+#define DSPARK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * dspark_draft_sample without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts that
+ * forbid allocation).  Arguments, outputs, draws and errors are those of
+ * dspark_draft_sample, which it shares its kernels with; the results are
+ * bit-identical.  Its scratch is a fixed array of DSPARK_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends
+ * (the device is the current one; `stream` must belong to it).  Sizes whose
+ * dspark_draft_workspace_bytes exceeds that are refused with
+ * ERR_WORKSPACE_TOO_SMALL (for K <= 2374 that admits B <= 1413 at V = 151936
+ * and B <= 1638 at V = 131072).
+ * The call allocates nothing: the first call on a device looks up the
+ * array's address and keeps it.  Every call on a device shares the one array,
+ * and nothing in it needs clearing between calls (each call writes what it
+ * reads): calls that overlap on one device (on different streams, or from
+ * different threads without ordering) race and give undefined results.
+ */
+dspark_status dspark_draft_sample_noalloc(const void* base_logits, dspark_dtype logit_dt,
+                                          const void* A, const void* W, dspark_dtype factor_dt,
+                                          const int32_t* prev_token, const float* temperature,
+                                          uint64_t seed, int32_t B, int32_t K, int32_t V,
+                                          int32_t r, int32_t* draft_tokens, float* draft_logp,
+                                          float* draft_lse, void* stream);
 
 /* --------------------------------------------------------------- schedule */
 size_t dspark_schedule_workspace_bytes(int32_t B, int32_t K);

@@ -62,6 +62,34 @@ def test_draft_validation(L):
     assert _draft(L, K=0, base=None, ws=None, wsb=0) == bd.DSPARK_OK
 
 
+def _draft_noalloc(L, **kw):
+    args = dict(base=FAKE, ldt=1, A=FAKE, W=FAKE, fdt=1, prev=FAKE, temp=FAKE, seed=0, B=4, K=2,
+                V=100, r=16, tok=FAKE, logp=FAKE, lse=FAKE, stream=None)
+    args.update(kw)
+    return L.dspark_draft_sample_noalloc(args["base"], args["ldt"], args["A"], args["W"],
+                                         args["fdt"], args["prev"], args["temp"], args["seed"],
+                                         args["B"], args["K"], args["V"], args["r"], args["tok"],
+                                         args["logp"], args["lse"], args["stream"])
+
+
+def test_draft_noalloc_validation(L):
+    """The no-allocation draft validates like dspark_draft_sample and refuses
+    sizes whose workspace exceeds its fixed 64 MiB scratch, all before any
+    HIP call."""
+    assert _draft_noalloc(L, ldt=7) == bd.DSPARK_ERR_UNSUPPORTED_DTYPE
+    assert _draft_noalloc(L, base=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert _draft_noalloc(L, A=None) == bd.DSPARK_ERR_INVALID_ARG
+    assert b"draft_sample_noalloc" in L.dspark_last_error()
+    assert _draft_noalloc(L, r=0) == bd.DSPARK_ERR_INVALID_ARG
+    for B, K, V in ((1414, 16, 151936), (1639, 16, 131072), (4096, 16, 151936)):
+        assert d.dspark_draft_workspace_bytes(B, K, V, 256) > (64 << 20)
+        assert _draft_noalloc(L, B=B, K=K, V=V, r=256) == bd.DSPARK_ERR_WORKSPACE_TOO_SMALL
+        assert b"scratch" in L.dspark_last_error()
+    for B, K, V in ((1413, 16, 151936), (1638, 16, 131072)):
+        assert d.dspark_draft_workspace_bytes(B, K, V, 256) <= (64 << 20)
+    assert _draft_noalloc(L, B=0, base=None) == bd.DSPARK_OK
+
+
 def test_schedule_validation(L):
     f = L.dspark_schedule
     cn = (ctypes.c_float * 2)(10.0, 20.0)
