@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+VALU_PEAK_TOPS = 39.3        # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz vector-ALU lane operations
 METRIC = "draft+verify tokens/s at B=256,K=16,V=151936; % of HBM / MFMA roofline"
 # Files whose contents define the dominant kernel; the stored PMC traffic figure
 # is only reported while their hash matches the one it was measured with.
@@ -65,21 +66,38 @@ def dominant_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """Per-launch HBM bytes of the dominant kernel from the committed PMC summary,
-    or None when the kernel's sources changed since the counters were taken."""
+def stored_counters():
+    """Per-launch figures of the dominant kernel from the committed PMC summary
+    (HBM bytes, VALU wave instructions, transcendental ones), or None when the
+    kernel's sources changed since the counters were taken."""
+    keys = ("source_hash", "traffic_bytes_per_launch", "valu_instructions_per_launch",
+            "valu_trans_instructions_per_launch")
     try:
         with open(PMC_SUMMARY) as f:
-            fields = dict(l.split(":", 1) for l in f.read().splitlines()
-                          if l.startswith(("source_hash:", "traffic_bytes_per_launch:")))
+            fields = dict(l.split(":", 1) for l in f.read().splitlines() if l.startswith(keys))
     except (OSError, ValueError):
         return None
     if fields.get("source_hash", "").strip() != dominant_source_hash():
         return None
     try:
-        return int(fields["traffic_bytes_per_launch"].strip())
+        return {k: int(fields[k].strip()) for k in keys[1:]}
     except (KeyError, ValueError):
         return None
+
+
+def alu_view(stored, launch_s):
+    """The dominant kernel against the vector-ALU peak, from the committed
+    counters: VALU lane-operations issued per second (wave instructions x 64
+    lanes, a transcendental counted twice: it issues at half rate) over the
+    peak of 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s.  This
+    is issued work, not an algorithmic count; null when the counters are
+    stale."""
+    if not stored:
+        return None
+    ops = 64 * (stored["valu_instructions_per_launch"] + stored["valu_trans_instructions_per_launch"])
+    rate = ops / launch_s
+    return {"lane_ops_per_launch": ops, "achieved": round(rate / 1e12, 2), "peak": VALU_PEAK_TOPS,
+            "unit": "T lane-ops/s", "frac": round(rate / 1e12 / VALU_PEAK_TOPS, 4)}
 
 
 def verify_position_launches(K):
@@ -328,7 +346,7 @@ def ece(conf, label, bins=15):
     return float(err / c.size)
 
 
-def sts_fit(c_raw, label, reached, lo=0.05, hi=20.0, min_samples=50):
+def sts_fit(c_raw, label, reached, lo=0.05, hi=20.0, min_samples=200):
     """Sequential temperature scaling: for positions k = 1..K in order, the
     temperature tau_k that minimises the Bernoulli log-loss of position k's
     acceptance labels over the samples that reached k (every earlier token
@@ -560,7 +578,8 @@ def main():
     strip_bytes = draft_bytes / K
     strip_flops = 2.0 * B * r * V
     achieved_gbs = strip_bytes / strip_avg_s / 1e9
-    traffic = stored_traffic()
+    stored = stored_counters()
+    traffic = stored["traffic_bytes_per_launch"] if stored else None
     # verify rows: every target row read under the early-exit schedule, once
     rows_ms, _, rows_timed = per_kernel["verify_rows"]
     rows_bytes = es * rows_read * V
@@ -637,6 +656,7 @@ def main():
             "timed_steps": f"last {inst} of {args.steps}",
             "mfma_tflops": round(strip_flops / strip_avg_s / 1e12, 1),
             "mfma_frac": round(strip_flops / strip_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "alu": alu_view(stored, strip_avg_s),
             "step": {"bytes": int(step_bytes), "achieved": round(g_step, 1),
                      "frac": round(g_step / HBM_PEAK_GBS, 4),
                      "bytes_rule": "draft call + verify rows read + residual/bonus rows"},
