@@ -576,6 +576,7 @@ def main():
     # that is a K-th of the base-plus-W figure.
     draft_bytes = es * (B * K * V + r * V + K * B * r)
     strip_bytes = draft_bytes / K
+    reread_bytes = es * (B * V + r * V + B * r)
     strip_flops = 2.0 * B * r * V
     achieved_gbs = strip_bytes / strip_avg_s / 1e9
     stored = stored_counters()
@@ -651,6 +652,10 @@ def main():
             "kernel": "draft_strip_mfma_rk<8,16>" if r == 256 else "draft_strip_mfma",
             "algorithmic_bytes_per_launch": int(strip_bytes),
             "bytes_rule": "(base logits + W once + gathered A rows of one draft call) / K",
+            "reread_bytes_per_launch": int(reread_bytes),
+            "reread_frac": round(reread_bytes / strip_avg_s / 1e9 / HBM_PEAK_GBS, 4),
+            "reread_rule": "base slice + all of W + gathered A rows: what one launch must read, "
+                           "since step k's bias needs x_(k-1)",
             "avg_launch_us": round(strip_avg_s * 1e6, 2),
             "launches_timed": strip_timed,
             "timed_steps": f"last {inst} of {args.steps}",

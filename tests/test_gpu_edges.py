@@ -202,3 +202,26 @@ def test_parallel_drafting_equals_zero_transition(dsp, orc, K):
     P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
                     inp["temp"].cpu().numpy(), P.tol_for(torch.bfloat16), tally)
     assert tally.compared >= len(idx) * K - 2
+    # verify without factors (the zero-bias case, vector-ALU residual) equals
+    # verify with zero factors (the rank-256 MFMA residual), and the oracle's
+    # with W = 0
+    g = torch.Generator(device="cuda").manual_seed(50 + K)
+    target = (inp["base"][:, :1].float().expand(-1, K + 1, -1)
+              + 1.5 * torch.randn((w.B, K + 1, w.V), generator=g, device="cuda"))
+    target = target.to(torch.bfloat16).reshape(-1, w.V).contiguous()
+    offs = inputs.dense_offsets(w.B, K, "cuda")
+    a0, n0, r0, q0 = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], None, None,
+                                       target, offs, inp["temp"], 23)
+    a1, n1, r1, q1 = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], Az, Wz,
+                                       target, offs, inp["temp"], 23)
+    torch.cuda.synchronize()
+    assert torch.equal(a0, a1) and torch.equal(n0, n1)
+    assert torch.equal(r0, r1) and torch.equal(q0, q1)
+    assert int((a0 < K).sum()) > 10  # rejections: the residual draw ran
+    rows = {b: P.np32(target[b * (K + 1):(b + 1) * (K + 1)]) for b in idx}
+    orv = P.oracle_verify(orc, inp, idx, {b: tok[b].cpu().numpy() for b in idx}, rows,
+                          {b: K for b in idx}, 23)
+    P.compare_verify(a0.cpu().numpy(), n0.cpu().numpy(), r0.cpu().numpy(), q0.cpu().numpy(),
+                     offs.cpu().numpy(), orv, P.tol_for(torch.bfloat16), tally)
+    print(tally)
+    assert tally.verify_clean >= len(idx) - 1
