@@ -106,6 +106,84 @@ __device__ __forceinline__ void row_chunk(const LT* row, int v0, int V, float (&
     }
 }
 
+// The (request, row) of this workgroup, or live = false when the row cannot
+// decide the request (past L_b + 1, out of range, or after a rejection found
+// by an earlier launch).  Called by every thread of the workgroup.
+struct RowJob {
+    int b, j;
+    int64_t row;
+    float T;
+    bool greedy, bonus, live;
+};
+
+__device__ __forceinline__ RowJob row_begin(const int64_t* __restrict__ row_off,
+                                            const int32_t* __restrict__ lengths,
+                                            const float* __restrict__ temperature, int K,
+                                            int64_t n_rows, VerifyWs ws, int j_lo, int span) {
+    RowJob job{};
+    const int64_t id = blockIdx.x;
+    // the residual list starts empty; verify_resolve appends to it after the
+    // last launch of the row kernels
+    if (j_lo == 1 && id == 0 && threadIdx.x == 0) *ws.count = 0;
+    // this launch covers positions j_lo .. j_lo + span - 1 of every request
+    job.b = static_cast<int>(id / span);
+    job.j = static_cast<int>(id - static_cast<int64_t>(job.b) * span) + j_lo;
+    const int L = lengths ? clamp_len(lengths[job.b], K) : K;
+    job.live = false;
+    if (job.j > L + 1) return job;
+    if (row_off[job.b] < 0 || row_off[job.b] + L + 1 > n_rows) return job;  // reported by verify_resolve
+    // Strict prefix: row j matters only while rows 1 .. j - 1 are all accepted.
+    // Rows of earlier launches are decided (thread i reads row i + 1's flag);
+    // a rejected one among them ends the request.
+    if (j_lo > 1) {
+        const int32_t* acc = ws.accept + static_cast<size_t>(job.b) * (K + 1);
+        const bool rejected = threadIdx.x < j_lo - 1 && !acc[threadIdx.x];
+        if (__syncthreads_or(rejected)) return job;
+    }
+    job.row = row_off[job.b] + (job.j - 1);
+    job.T = temperature[job.b];
+    job.greedy = !(job.T > 0.0f);
+    job.bonus = (job.j == L + 1);
+    job.live = true;
+    return job;
+}
+
+// The end of a verified row, once its state is reduced (thread 0): the target
+// log-normaliser, and the accept test of the drafted token (or the bonus
+// candidate on row L_b + 1).
+template <typename LT>
+__device__ __forceinline__ void row_finish(const RowState& st, const LT* trow, int64_t row, int b,
+                                           int j, bool greedy, bool bonus, float T,
+                                           const int32_t* __restrict__ tokens,
+                                           const float* __restrict__ draft_logp, uint64_t seed,
+                                           int K, int V, float* __restrict__ row_lse_t,
+                                           float* __restrict__ row_logratio, VerifyWs ws) {
+    const size_t slot = static_cast<size_t>(b) * (K + 1) + (j - 1);
+    const float lse_t = greedy ? st.pert : st.m + logf(st.s);
+    ws.lse[slot] = lse_t;
+    if (row_lse_t) row_lse_t[row] = lse_t;
+    if (bonus) {
+        ws.bonus[b] = st.idx;
+        if (row_logratio) row_logratio[row] = 0.0f;
+    } else {
+        const int x = clamp_token(tokens[static_cast<size_t>(b) * K + (j - 1)], V);
+        int acc;
+        float ratio;
+        if (!greedy) {
+            const float yx = to_f32(trow[x]) * inv_temperature(T);
+            ratio = (yx - lse_t) - draft_logp[static_cast<size_t>(b) * K + (j - 1)];
+            const u32x4 rnd = philox_block(seed, b, j, kTagAccept, 0);
+            acc = logf(uniform_of(rnd.x)) < ratio;
+        } else {
+            acc = (x == st.idx);
+            ratio = acc ? 0.0f : -INFINITY;
+        }
+        ws.accept[slot] = acc;
+        ws.arg[slot] = st.idx;
+        if (row_logratio) row_logratio[row] = ratio;
+    }
+}
+
 // verify_rows: one 512-thread workgroup per visited row with four 16-byte
 // loads in flight per lane (512 threads measured best among 64 / 256 / 512 /
 // 1024; four loads 4% faster than two on the long-draft step, 40 VGPRs -> 56).
@@ -120,28 +198,12 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
     int K, int V, int64_t n_rows, bool bonus_draw, float* __restrict__ row_lse_t,
     float* __restrict__ row_logratio, VerifyWs ws, int j_lo, int span) {
     __shared__ RowState red[kVRowThreads / kWave];
-    const int64_t id = blockIdx.x;
-    // the residual list starts empty; verify_resolve appends to it after the
-    // last launch of this kernel
-    if (j_lo == 1 && id == 0 && threadIdx.x == 0) *ws.count = 0;
-    // this launch covers positions j_lo .. j_lo + span - 1 of every request
-    const int b = static_cast<int>(id / span);
-    const int j = static_cast<int>(id - static_cast<int64_t>(b) * span) + j_lo;
-    const int L = lengths ? clamp_len(lengths[b], K) : K;
-    if (j > L + 1) return;
-    if (row_off[b] < 0 || row_off[b] + L + 1 > n_rows) return;  // reported by verify_resolve
-    // Strict prefix: row j matters only while rows 1 .. j - 1 are all accepted.
-    // Rows of earlier launches are decided (thread i reads row i + 1's flag);
-    // a rejected one among them ends the request.
-    if (j_lo > 1) {
-        const int32_t* acc = ws.accept + static_cast<size_t>(b) * (K + 1);
-        const bool rejected = threadIdx.x < j_lo - 1 && !acc[threadIdx.x];
-        if (__syncthreads_or(rejected)) return;
-    }
-    const int64_t row = row_off[b] + (j - 1);
-    const float T = temperature[b];
-    const bool greedy = !(T > 0.0f);
-    const bool bonus = (j == L + 1);
+    const RowJob job = row_begin(row_off, lengths, temperature, K, n_rows, ws, j_lo, span);
+    if (!job.live) return;
+    const int b = job.b, j = job.j;
+    const int64_t row = job.row;
+    const float T = job.T;
+    const bool greedy = job.greedy, bonus = job.bonus;
     // the sampled bonus draw is made here only when the residual kernel does
     // not make it (bonus_draw); the normaliser is always computed
     const bool draw = bonus && bonus_draw;
@@ -233,32 +295,9 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
         st.idx = bi;
     }
     st = block_reduce_row<kVRowThreads>(st, red);
-    if (threadIdx.x == 0) {
-        const size_t slot = static_cast<size_t>(b) * (K + 1) + (j - 1);
-        const float lse_t = greedy ? st.pert : st.m + logf(st.s);
-        ws.lse[slot] = lse_t;
-        if (row_lse_t) row_lse_t[row] = lse_t;
-        if (bonus) {
-            ws.bonus[b] = st.idx;
-            if (row_logratio) row_logratio[row] = 0.0f;
-        } else {
-            const int x = clamp_token(tokens[static_cast<size_t>(b) * K + (j - 1)], V);
-            int acc;
-            float ratio;
-            if (!greedy) {
-                const float yx = to_f32(trow[x]) * inv_temperature(T);
-                ratio = (yx - lse_t) - draft_logp[static_cast<size_t>(b) * K + (j - 1)];
-                const u32x4 rnd = philox_block(seed, b, j, kTagAccept, 0);
-                acc = logf(uniform_of(rnd.x)) < ratio;
-            } else {
-                acc = (x == st.idx);
-                ratio = acc ? 0.0f : -INFINITY;
-            }
-            ws.accept[slot] = acc;
-            ws.arg[slot] = st.idx;
-            if (row_logratio) row_logratio[row] = ratio;
-        }
-    }
+    if (threadIdx.x == 0)
+        row_finish(st, trow, row, b, j, greedy, bonus, T, tokens, draft_logp, seed, K, V, row_lse_t,
+                   row_logratio, ws);
 }
 
 __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_rows,
