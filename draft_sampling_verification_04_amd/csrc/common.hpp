@@ -200,6 +200,19 @@ __device__ __forceinline__ float entry_l2(uint32_t w, const KeyLane& kl) {
 // with the entry's tag-2 draw: log2(e) (y + G) and log2(e) (log(p_t - p_d) + G)
 // up to constants shared by the row.  dm is formed from the logit difference so
 // that a target row equal to the draft row gives every such entry the same dm.
+// The verifier's residual list: the sampled first rejections at
+// list[0 .. count[0]) and the sampled full acceptances (whose next token is the
+// bonus draw) from the back, list[B - 1 - i] for i < count[1].  Slot s in
+// [0, count[0] + count[1]) names one listed request, rejections first, so that
+// the wavefronts of the residual kernels hold one kind of request (but for the
+// one at the boundary).
+__device__ __forceinline__ int listed_count(const int32_t* count) { return count[0] + count[1]; }
+
+__device__ __forceinline__ int listed_request(const int32_t* list, const int32_t* count, int B,
+                                              int s) {
+    return s < count[0] ? list[s] : list[B - 1 - (s - count[0])];
+}
+
 struct ResRow {
     float c2;    // log2(e) / T
     float lt2;   // lse_t log2(e)

@@ -953,10 +953,11 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     const int32_t* __restrict__ prev_token, const float* __restrict__ draft_lse,
     const float* __restrict__ temperature, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ list, const int32_t* __restrict__ count_ptr,
-    const int32_t* __restrict__ lengths, const float* __restrict__ lse_tab, uint64_t seed, int K,
+    const int32_t* __restrict__ lengths, const float* __restrict__ lse_tab, uint64_t seed, int B,
+    int K,
     int V, int r, PartialBuf res, PartialBuf fall, int n_strips, int n_parts) {
     extern __shared__ uint16_t w_sh[];  // two buffers of [r][kPitch]
-    const int count = *count_ptr;
+    const int count = listed_count(count_ptr);
     const int slot0 = blockIdx.y * NWAVES * 32;
     if (slot0 >= count) return;  // whole workgroup idle
     const int lane = threadIdx.x & 63;
@@ -966,7 +967,7 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
     // waves wholly past the list only help stage W and meet the barriers
     const bool wave_busy = slot0 + (threadIdx.x >> 6) * 32 < count;
     // lanes past the list run request list[0]'s rows and store nothing
-    const int b = list[active ? slot : 0];
+    const int b = listed_request(list, count_ptr, B, active ? slot : 0);
     const int js = accepted[b] + 1;
     // js > L_b: a full acceptance listed for its bonus, which is this kernel's
     // fallback draw over row L_b + 1; it takes no residual draw, and its draft
@@ -1126,6 +1127,30 @@ __device__ __forceinline__ void residual_half(ResBest& rb, const f32x16 (&acc)[2
     }
 }
 
+// Fallback keys only, for a wavefront of listed full acceptances (their bonus
+// draw is the fallback draw over row L_b + 1): the same keys as residual_half
+// gives them, with no draft row.
+__device__ __forceinline__ void bonus_half(ResBest& rb, const uint4 (&tq)[4], int vh,
+                                           const ResRow& R) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const u32x4 rnd = philox_row_block(R.ph, static_cast<uint32_t>(vh >> 2) + 4 * a + tt);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t dw = dword_of(tq[a], 2 * tt + (w >> 1));
+                const float tv = __uint_as_float((w & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
+                const float kf = fmaf(tv, R.c2, -R.lt2) - entry_l2(pick(rnd, w), R.kl);
+                if (kf > rb.bf) {
+                    rb.bf = kf;
+                    rb.jf = vh + 16 * a + 4 * tt + w;
+                }
+            }
+        }
+    }
+}
+
 struct ResLane {
     const uint16_t* brow;
     const uint16_t* trow;
@@ -1142,7 +1167,7 @@ __device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t*
                                                   const uint16_t* __restrict__ W,
                                                   const uint4 (&afr)[KS], const int (&tro)[2][2],
                                                   int V, int kh, int n_strips, int n_parts,
-                                                  bool busy) {
+                                                  bool busy, bool bonus_only) {
     // this strip's W (all waves' shares) and half-0 logits have landed, and
     // every wave is done with the other buffer
     __builtin_amdgcn_s_waitcnt(0);
@@ -1153,6 +1178,23 @@ __device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t*
         const int sn = s + n_parts;
         if (sn >= n_strips) return false;
         stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
+        s = sn;
+        return true;
+    }
+    if (bonus_only) {
+        // a wave of listed full acceptances stages its share of W and keys
+        // the target row alone
+        tail_half(t0, v0, 0, kh, V);
+        const int sn = s + n_parts;
+        const bool more = sn < n_strips;
+        uint4 t1[4];
+        load_half(t1, L.trow, v0, 1, kh, V);
+        if (more) stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
+        bonus_half(L.best, t0, v0 + 8 * kh, L.R);
+        if (more) load_half(t0, L.trow, sn * kStripV, 0, kh, V);
+        tail_half(t1, v0, 1, kh, V);
+        bonus_half(L.best, t1, v0 + 64 + 8 * kh, L.R);
+        if (!more) return false;
         s = sn;
         return true;
     }
@@ -1194,11 +1236,12 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     const int32_t* __restrict__ prev_token, const float* __restrict__ draft_lse,
     const float* __restrict__ temperature, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ list, const int32_t* __restrict__ count_ptr,
-    const int32_t* __restrict__ lengths, const float* __restrict__ lse_tab, uint64_t seed, int K,
+    const int32_t* __restrict__ lengths, const float* __restrict__ lse_tab, uint64_t seed, int B,
+    int K,
     int V, int r, PartialBuf res, PartialBuf fall, int n_strips, int n_parts) {
     __shared__ __attribute__((aligned(16))) uint16_t w_a[16 * KS * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t w_b[16 * KS * kPitch];
-    const int count = *count_ptr;
+    const int count = listed_count(count_ptr);
     const int slot0 = blockIdx.y * NWAVES * 32;
     if (slot0 >= count) return;  // whole workgroup idle
     const int lane = threadIdx.x & 63;
@@ -1209,7 +1252,7 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     const bool busy = slot0 + (threadIdx.x >> 6) * 32 < count;
     // lanes past the list run request list[0]'s rows and store nothing
     ResLane L;
-    const int b = list[active ? slot : 0];
+    const int b = listed_request(list, count_ptr, B, active ? slot : 0);
     const int js = accepted[b] + 1;
     // js > L_b: a listed full acceptance (its bonus is the fallback draw over
     // row L_b + 1); its draft side reads row 1 as an in-range stand-in
@@ -1228,24 +1271,24 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     L.trow = target + (row_off[b] + js - 1) * static_cast<int64_t>(V);
     L.best = res_empty();
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
+    // a wave whose listed requests are all full acceptances needs no draft row
+    const bool bonus_only = busy && __all(!active || bonus);
     uint4 afr[KS];
     uint4 b0[4], t0[4];
     int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
-    if (busy) {
+    if (busy && !bonus_only) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
     }
     const int tro[2][2] = {{tr_offset(lane, 0, 0), tr_offset(lane, 0, 1)},
                            {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
     stage_w_tr<NWAVES>(w_a, W, r, V, s * kStripV);
-    if (busy) {
-        load_half(b0, L.brow, s * kStripV, 0, kh, V);
-        load_half(t0, L.trow, s * kStripV, 0, kh, V);
-    }
+    if (busy && !bonus_only) load_half(b0, L.brow, s * kStripV, 0, kh, V);
+    if (busy) load_half(t0, L.trow, s * kStripV, 0, kh, V);
     while (residual_rk_strip<NWAVES, KS>(w_a, w_b, s, b0, t0, L, W, afr, tro, V, kh, n_strips,
-                                         n_parts, busy) &&
+                                         n_parts, busy, bonus_only) &&
            residual_rk_strip<NWAVES, KS>(w_b, w_a, s, b0, t0, L, W, afr, tro, V, kh, n_strips,
-                                         n_parts, busy)) {
+                                         n_parts, busy, bonus_only)) {
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
     RowState sr{-INFINITY, 0.0f, L.best.br, 0.0f, L.best.ir};
@@ -1352,7 +1395,7 @@ hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
                            static_cast<const uint16_t*>(v.A), static_cast<const uint16_t*>(v.W),
                            static_cast<const uint16_t*>(v.target), v.row_off, v.tokens,
                            v.prev_token, v.draft_lse, v.temperature, v.accepted, a.list, a.count,
-                           v.lengths, a.lse_tab, v.seed, v.K, v.V, v.r, a.res, a.fall, a.n_strips,
+                           v.lengths, a.lse_tab, v.seed, v.B, v.K, v.V, v.r, a.res, a.fall, a.n_strips,
                            parts);
         return hipGetLastError();
     }
@@ -1368,7 +1411,7 @@ hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
                        static_cast<const uint16_t*>(v.base), static_cast<const uint16_t*>(v.A),
                        static_cast<const uint16_t*>(v.W), static_cast<const uint16_t*>(v.target),
                        v.row_off, v.tokens, v.prev_token, v.draft_lse, v.temperature, v.accepted,
-                       a.list, a.count, v.lengths, a.lse_tab, v.seed, v.K, v.V, v.r, a.res, a.fall,
+                       a.list, a.count, v.lengths, a.lse_tab, v.seed, v.B, v.K, v.V, v.r, a.res, a.fall,
                        a.n_strips, parts);
     return hipGetLastError();
 }

@@ -124,7 +124,7 @@ __device__ __forceinline__ RowJob row_begin(const int64_t* __restrict__ row_off,
     const int64_t id = blockIdx.x;
     // the residual list starts empty; verify_resolve appends to it after the
     // last launch of the row kernels
-    if (j_lo == 1 && id == 0 && threadIdx.x == 0) *ws.count = 0;
+    if (j_lo == 1 && id == 0 && threadIdx.x < 2) ws.count[threadIdx.x] = 0;
     // this launch covers positions j_lo .. j_lo + span - 1 of every request
     job.b = static_cast<int>(id / span);
     job.j = static_cast<int>(id - static_cast<int64_t>(job.b) * span) + j_lo;
@@ -324,11 +324,13 @@ __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_ro
         next_token[b] = ws.bonus[b];
     } else if (!sampled) {
         next_token[b] = ws.arg[static_cast<size_t>(b) * (K + 1) + a];
+    } else if (a < L) {
+        // a sampled first rejection: from the front of the list
+        ws.list[atomicAdd(&ws.count[0], 1)] = b;
     } else {
-        // a sampled first rejection, or (bonus_in_list) a sampled full
-        // acceptance whose bonus the residual kernel draws as its fallback
-        const int slot = atomicAdd(ws.count, 1);
-        ws.list[slot] = b;
+        // (bonus_in_list) a sampled full acceptance whose bonus the residual
+        // kernel draws as its fallback: from the back of the list
+        ws.list[B - 1 - atomicAdd(&ws.count[1], 1)] = b;
     }
 }
 
@@ -341,14 +343,14 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
     const LT* __restrict__ target, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ prev_token,
     const float* __restrict__ draft_lse, const float* __restrict__ temperature,
-    const int32_t* __restrict__ accepted, uint64_t seed, int K, int V, int r, VerifyWs ws,
+    const int32_t* __restrict__ accepted, uint64_t seed, int B, int K, int V, int r, VerifyWs ws,
     int n_strips) {
     extern __shared__ float a_sh[];  // [kResRows][r]
     __shared__ RowState red_r[4][kResRows];
     __shared__ RowState red_f[4][kResRows];
     const int tid = threadIdx.x;
     const int slot0 = blockIdx.x * kResRows;
-    const int count = *ws.count;
+    const int count = listed_count(ws.count);
     if (slot0 >= count) return;
     const int nrows = min(kResRows, count - slot0);
     const int strip = blockIdx.y;
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
         const int i = e - g * r;
         float a = 0.0f;
         if (A != nullptr && g < nrows) {
-            const int b = ws.list[slot0 + g];
+            const int b = listed_request(ws.list, ws.count, B, slot0 + g);
             const int js = accepted[b] + 1;
             const int p = clamp_token(
                 (js == 1) ? prev_token[b] : tokens[static_cast<size_t>(b) * K + js - 2], V);
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
 #pragma unroll
     for (int g = 0; g < kResRows; ++g) {
         if (g >= nrows) break;
-        const int b = ws.list[slot0 + g];
+        const int b = listed_request(ws.list, ws.count, B, slot0 + g);
         const int js = accepted[b] + 1;
         const float T = temperature[b];
         // keys of the thread's 4 entries (one Philox block), see residual_entry
@@ -439,10 +441,10 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
 // winner of the residual keys when any entry had positive residual mass, else
 // the winner of the fallback keys (for a listed full acceptance, its bonus).
 // One wavefront per listed request.
-__global__ __launch_bounds__(kWave) void verify_residual_combine(VerifyWs ws, int n_strips,
+__global__ __launch_bounds__(kWave) void verify_residual_combine(VerifyWs ws, int B, int n_strips,
                                                                  int32_t* __restrict__ next_token) {
     const int slot = blockIdx.x;
-    if (slot >= *ws.count) return;
+    if (slot >= listed_count(ws.count)) return;
     const int lane = threadIdx.x;
     RowState sr = row_empty();
     RowState sf = row_empty();
@@ -463,7 +465,9 @@ __global__ __launch_bounds__(kWave) void verify_residual_combine(VerifyWs ws, in
     }
     wave_reduce_row(sr);
     wave_reduce_row(sf);
-    if (lane == 0) next_token[ws.list[slot]] = (sr.pert > -INFINITY) ? sr.idx : sf.idx;
+    if (lane == 0)
+        next_token[listed_request(ws.list, ws.count, B, slot)] =
+            (sr.pert > -INFINITY) ? sr.idx : sf.idx;
 }
 
 struct WsLayout {
@@ -496,8 +500,8 @@ void launch_residual_valu(const VerifyArgs& a, const VerifyWs& ws, int n_strips)
     hipLaunchKernelGGL((verify_residual_valu<LT, FT>), grid, dim3(256), lds, a.stream,
                        static_cast<const LT*>(a.base), static_cast<const FT*>(a.A),
                        static_cast<const FT*>(a.W), static_cast<const LT*>(a.target), a.row_off,
-                       a.tokens, a.prev_token, a.draft_lse, a.temperature, a.accepted, a.seed, a.K,
-                       a.V, a.r, ws, n_strips);
+                       a.tokens, a.prev_token, a.draft_lse, a.temperature, a.accepted, a.seed, a.B,
+                       a.K, a.V, a.r, ws, n_strips);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -602,7 +606,7 @@ hipError_t launch_verify(const VerifyArgs& a) {
     res_scope.slot = -1;
     ProfScope combine_scope(DSPARK_KERNEL_RESIDUAL_COMBINE, a.stream);
     hipLaunchKernelGGL(verify_residual_combine, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0,
-                       a.stream, ws, n_strips, a.next_token);
+                       a.stream, ws, a.B, n_strips, a.next_token);
     return hipGetLastError();
 }
 
