@@ -255,9 +255,9 @@ __device__ __forceinline__ void residual_entry(ResBest& rb, float sv, float tv, 
 // ---------------------------------------------------------------- row state
 // Partial reduction state of one logits row over a subset of the vocabulary:
 // online-softmax max m and sum s = sum exp(z - m); the winner of a keyed
-// argmax (its key, a value carried with it, its index): a perturbed entry, a
-// draft block (key = log-mass + Gumbel, index = block start) or, for T == 0,
-// the largest logit.  Ties go to the smaller index.
+// argmax (its key, a value carried with it, its index): the entry with the
+// largest perturbed key (its own Gumbel draw) or, for T == 0, the largest
+// logit.  Ties go to the smaller index.
 struct RowState {
     float m;
     float s;

@@ -11,8 +11,10 @@
 // Workgroup = NWAVES wavefronts = a persistent walk over 128-entry vocabulary
 // strips x 32*NWAVES requests.  The strip of W (r x 128 bf16) is staged in LDS
 // and shared by the waves; each wave owns 32 requests (one MFMA column tile).
-// The rank-256 kernel works a strip in two 64-entry halves (one draft block
-// each) with transposing LDS reads; the runtime-rank kernel keeps four 32-row
+// The rank-256 kernel works a strip as four tiles in two 64-entry halves with
+// transposing LDS reads, software-pipelined a tile at a time (the bias MFMAs of
+// one tile interleaved with the per-entry draws of the one before); the
+// runtime-rank kernel keeps four 32-row
 // tiles per strip, where row m of tile t is entry v = strip start + 4 m + t:
 //   - an A-operand lane (row m) reads 4 consecutive entries of 8 rank rows
 //     with one 8-byte LDS read per row, and the 16 lanes of an LDS pass read
@@ -1100,7 +1102,7 @@ __global__ __launch_bounds__(1024) void temperature_order(const float* __restric
 // The residual strip of residual_strip_mfma for rank 256, built like
 // draft_strip_mfma_rk: factor fragments in registers (the MFMA loops issue no
 // vector-memory loads), W double-buffered in two static LDS arrays, and a
-// strip worked in two 64-entry halves (one block each).  The base and target
+// strip worked in two 64-entry halves.  The base and target
 // logits of a half are loaded one phase ahead into registers that the phase
 // before has freed: a strip's half-1 base logits go out before the next
 // strip's W, so waiting for them never waits for that W.
