@@ -1160,71 +1160,181 @@ struct ResLane {
     ResBest best;
 };
 
-// One strip: this strip's W is in `cur`, the next strip's goes into `nxt`;
-// b0 / t0 hold this strip's half-0 logits on entry and the next strip's on
-// return.
+// One strip of a wave with no draft row to recompute: this strip's W is in
+// `cur`, the next strip's goes into `nxt`.  A wave with no listed request only
+// stages its share of W; a wave of listed full acceptances (bonus_only) also
+// keys the target row alone (t0 holds this strip's half-0 target logits on
+// entry and the next strip's on return).  The barrier and W staging match
+// residual_rk_pipe's, so waves of both kinds share a workgroup.
 template <int NWAVES, int KS>
-__device__ __forceinline__ bool residual_rk_strip(const uint16_t* cur, uint16_t* nxt, int& s,
-                                                  uint4 (&b0)[4], uint4 (&t0)[4], ResLane& L,
-                                                  const uint16_t* __restrict__ W,
-                                                  const uint4 (&afr)[KS], const int (&tro)[2][2],
-                                                  int V, int kh, int n_strips, int n_parts,
-                                                  bool busy, bool bonus_only) {
-    // this strip's W (all waves' shares) and half-0 logits have landed, and
-    // every wave is done with the other buffer
+__device__ __forceinline__ bool residual_rk_light(const uint16_t* cur, uint16_t* nxt, int& s,
+                                                  uint4 (&t0)[4], ResLane& L,
+                                                  const uint16_t* __restrict__ W, int V, int kh,
+                                                  int n_strips, int n_parts, bool bonus_only) {
+    // this strip's W (all waves' shares) and logits have landed, and every
+    // wave is done with the other buffer
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int v0 = s * kStripV;
-    if (!busy) {
-        // a wave with no listed request only stages its share of W
-        const int sn = s + n_parts;
-        if (sn >= n_strips) return false;
+    const int sn = s + n_parts;
+    const bool more = sn < n_strips;
+    if (!bonus_only) {
+        if (!more) return false;
         stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
         s = sn;
         return true;
     }
-    if (bonus_only) {
-        // a wave of listed full acceptances stages its share of W and keys
-        // the target row alone
-        tail_half(t0, v0, 0, kh, V);
-        const int sn = s + n_parts;
-        const bool more = sn < n_strips;
-        uint4 t1[4];
-        load_half(t1, L.trow, v0, 1, kh, V);
-        if (more) stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
-        bonus_half(L.best, t0, v0 + 8 * kh, L.R);
-        if (more) load_half(t0, L.trow, sn * kStripV, 0, kh, V);
-        tail_half(t1, v0, 1, kh, V);
-        bonus_half(L.best, t1, v0 + 64 + 8 * kh, L.R);
-        if (!more) return false;
-        s = sn;
-        return true;
+    uint4 t1[4];
+    load_half(t1, L.trow, v0, 1, kh, V);
+    if (more) stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
+    bonus_half(L.best, t0, v0 + 8 * kh, L.R);
+    if (more) load_half(t0, L.trow, sn * kStripV, 0, kh, V);
+    bonus_half(L.best, t1, v0 + 64 + 8 * kh, L.R);
+    if (!more) return false;
+    s = sn;
+    return true;
+}
+
+// Four bf16 -inf: the piece that stands in for tile pieces past V.
+__device__ uint2 kNegInfPiece = {0xFF80FF80u, 0xFF80FF80u};
+
+// The four 8-byte pieces of one tile's entries in a row (acc_from_logits'
+// layout): piece g holds entries 16 g + 4 (ts ^ (g % 2)) + 0..3 of the lane's
+// half, whose values accumulator 4 g + w of the tile holds.  A piece starts
+// on a multiple of 4 and V is a multiple of 8, so a piece is wholly below V or
+// wholly past it; pieces past V read the -inf piece.
+__device__ __forceinline__ void load_tile(uint2 (&q)[4], const uint16_t* row, int v0, int h, int ts,
+                                          int kh, int V) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int v = v0 + 64 * h + 16 * g + 8 * kh + 4 * (ts ^ (g & 1));
+        const uint2* p = (v < V) ? reinterpret_cast<const uint2*>(row + v) : &kNegInfPiece;
+        q[g] = *p;
     }
-    tail_half(b0, v0, 0, kh, V);
-    tail_half(t0, v0, 0, kh, V);
+}
+
+__device__ __forceinline__ float piece_value(const uint2 (&q)[4], int g, int w) {
+    const uint32_t dw = (w >> 1) ? q[g].y : q[g].x;
+    return __uint_as_float((w & 1) ? (dw & 0xFFFF0000u) : (dw << 16));
+}
+
+__device__ __forceinline__ void tile_from_pieces(f32x16& acc, const uint2 (&q)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[4 * g + w] = piece_value(q, g, w);
+}
+
+// The residual counterpart of rk_unit: the KS bias MFMAs of one tile into accm
+// and, in the same instruction stream, the residual and fallback keys of the
+// tile before (accs, with its target pieces tq) into rb, cut into KS slices
+// fenced by sched_barrier (slice kk: the MFMA of rank step kk, entry kk of the
+// previous tile, an eighth of the next draw block's Philox rounds).
+template <int KS, bool SAMPLE>
+__device__ __forceinline__ void res_unit(f32x16& accm, const uint16_t* wt, const uint4 (&afr)[KS],
+                                         const f32x16& accs, const uint2 (&tq)[4], ResBest& rb,
+                                         int vs, int ts, const ResRow& R) {
+    static_assert(KS == 16, "the slice schedule covers 16 rank steps (four Philox blocks)");
+    uint2 lo[3], hi[3];
+    lo[0] = lds_tr16(wt);
+    hi[0] = lds_tr16(wt + 4 * kPitch);
+    lo[1] = lds_tr16(wt + 16 * kPitch);
+    hi[1] = lds_tr16(wt + 16 * kPitch + 4 * kPitch);
+    PhiloxState cur{}, nxt{};
+    if constexpr (SAMPLE) {
+        nxt = philox_head(R.ph, static_cast<uint32_t>((vs + 4 * ts) >> 2));
+#pragma unroll
+        for (int i = 4; i <= 10; ++i) philox_round(nxt, R.ph, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 2 < KS) {
+            lo[(kk + 2) % 3] = lds_tr16(wt + (kk + 2) * 16 * kPitch);
+            hi[(kk + 2) % 3] = lds_tr16(wt + (kk + 2) * 16 * kPitch + 4 * kPitch);
+        }
+        const uint4 a = make_uint4(lo[kk % 3].x, lo[kk % 3].y, hi[kk % 3].x, hi[kk % 3].y);
+        accm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(afr[kk]), accm, 0, 0,
+                                                       0);
+        if constexpr (SAMPLE) {
+            const int g = kk >> 2, w = kk & 3;
+            if (w == 0) cur = nxt;
+            const int o = 16 * g + 4 * (ts ^ (g & 1));
+            residual_entry(rb, accs[4 * g + w], piece_value(tq, g, w), state_word(cur, w),
+                           vs + o + w, R);
+            if (g < 3) {
+                const int gn = g + 1;
+                if (w == 0) {
+                    nxt = philox_head(R.ph,
+                                      static_cast<uint32_t>((vs + 16 * gn + 4 * (ts ^ (gn & 1))) >> 2));
+                    philox_round(nxt, R.ph, 4);
+                } else {
+                    philox_round(nxt, R.ph, 2 * w + 3);
+                    philox_round(nxt, R.ph, 2 * w + 4);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The keys of one tile with no MFMAs beside them (the last tile of a launch).
+__device__ __forceinline__ void res_tile(ResBest& rb, const f32x16& acc, const uint2 (&tq)[4],
+                                         int vs, int ts, const ResRow& R) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int o = 16 * g + 4 * (ts ^ (g & 1));
+        const u32x4 rnd = philox_row_block(R.ph, static_cast<uint32_t>((vs + o) >> 2));
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            residual_entry(rb, acc[4 * g + w], piece_value(tq, g, w), pick(rnd, w), vs + o + w, R);
+    }
+}
+
+// One strip of a wave that recomputes draft rows, software-pipelined a tile at
+// a time like rk_strip (tiles 0..3 = half 0 tiles 0, 1, half 1 tiles 0, 1):
+// this strip's W is in `cur`, the next strip's goes into `nxt`.  Base logits go
+// by half as in rk_strip (L0 / L1 hold this strip's halves on entry and the
+// next strip's on return, each reloaded once both of its tiles are unpacked);
+// target logits go by tile in a two-slot ring, Tq[u % 2] holding tile u's
+// pieces, requested one tile ahead (as soon as tile u - 2 is keyed).  On entry
+// T0 holds this strip's tile 0, T1 the previous strip's tile 3 and accB that
+// tile's s (unkeyed); on return the same for the next strip.
+template <int NWAVES, int KS, bool FIRST>
+__device__ __forceinline__ bool residual_rk_pipe(const uint16_t* cur, uint16_t* nxt, int& s,
+                                                 uint4 (&L0)[4], uint4 (&L1)[4], uint2 (&T0)[4],
+                                                 uint2 (&T1)[4], f32x16& accA, f32x16& accB,
+                                                 int& vsB, ResLane& L,
+                                                 const uint16_t* __restrict__ W,
+                                                 const uint4 (&afr)[KS], const int (&tro)[2][2],
+                                                 int V, int kh, int n_strips, int n_parts) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int v0 = s * kStripV;
     const int sn = s + n_parts;
     const bool more = sn < n_strips;
-    uint4 b1[4], t1[4];
-    load_half(b1, L.brow, v0, 1, kh, V);  // before the next W: its wait does not include it
+    const int vn = more ? sn * kStripV : v0;  // past the last strip: in-range loads, unused
     if (more) stage_w_tr<NWAVES>(nxt, W, 16 * KS, V, sn * kStripV);
-    f32x16 acc[2];
-    {
-        const uint16_t* const wt[2] = {cur + tro[0][0], cur + tro[0][1]};
-        acc_from_logits(acc, b0);
-        bias_half<KS>(acc, wt, afr);
-    }
-    if (more) load_half(b0, L.brow, sn * kStripV, 0, kh, V);
-    residual_half(L.best, acc, t0, v0 + 8 * kh, L.R);
-    load_half(t1, L.trow, v0, 1, kh, V);
-    if (more) load_half(t0, L.trow, sn * kStripV, 0, kh, V);
-    tail_half(b1, v0, 1, kh, V);
-    {
-        const uint16_t* const wt[2] = {cur + tro[1][0], cur + tro[1][1]};
-        acc_from_logits(acc, b1);
-        bias_half<KS>(acc, wt, afr);
-    }
-    tail_half(t1, v0, 1, kh, V);
-    residual_half(L.best, acc, t1, v0 + 64 + 8 * kh, L.R);
+    const int vh0 = v0 + 8 * kh, vh1 = v0 + 64 + 8 * kh;
+    // tile 0 (keys the previous strip's tile 3)
+    tile_from_logits(accA, L0, 0);
+    res_unit<KS, !FIRST>(accA, cur + tro[0][0], afr, accB, T1, L.best, vsB, 1, L.R);
+    load_tile(T1, L.trow, v0, 0, 1, kh, V);  // tile 1
+    // tile 1 (keys tile 0)
+    tile_from_logits(accB, L0, 1);
+    load_half(L0, L.brow, vn, 0, kh, V);  // next strip's half 0
+    res_unit<KS, true>(accB, cur + tro[0][1], afr, accA, T0, L.best, vh0, 0, L.R);
+    load_tile(T0, L.trow, v0, 1, 0, kh, V);  // tile 2
+    // tile 2 (keys tile 1)
+    tile_from_logits(accA, L1, 0);
+    res_unit<KS, true>(accA, cur + tro[1][0], afr, accB, T1, L.best, vh0, 1, L.R);
+    load_tile(T1, L.trow, v0, 1, 1, kh, V);  // tile 3
+    // tile 3 (keys tile 2)
+    tile_from_logits(accB, L1, 1);
+    load_half(L1, L.brow, vn, 1, kh, V);  // next strip's half 1
+    res_unit<KS, true>(accB, cur + tro[1][1], afr, accA, T0, L.best, vh1, 0, L.R);
+    load_tile(T0, L.trow, vn, 0, 0, kh, V);  // next strip's tile 0
+    vsB = vh1;
     if (!more) return false;
     s = sn;
     return true;
@@ -1285,12 +1395,33 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     const int tro[2][2] = {{tr_offset(lane, 0, 0), tr_offset(lane, 0, 1)},
                            {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
     stage_w_tr<NWAVES>(w_a, W, r, V, s * kStripV);
-    if (busy && !bonus_only) load_half(b0, L.brow, s * kStripV, 0, kh, V);
-    if (busy) load_half(t0, L.trow, s * kStripV, 0, kh, V);
-    while (residual_rk_strip<NWAVES, KS>(w_a, w_b, s, b0, t0, L, W, afr, tro, V, kh, n_strips,
-                                         n_parts, busy, bonus_only) &&
-           residual_rk_strip<NWAVES, KS>(w_b, w_a, s, b0, t0, L, W, afr, tro, V, kh, n_strips,
-                                         n_parts, busy, bonus_only)) {
+    if (busy && !bonus_only) {
+        uint4 B0[4], B1[4];
+        uint2 T0[4], T1[4];
+        load_half(B0, L.brow, s * kStripV, 0, kh, V);
+        load_half(B1, L.brow, s * kStripV, 1, kh, V);
+        load_tile(T0, L.trow, s * kStripV, 0, 0, kh, V);
+        f32x16 accA, accB;
+        int vsB = 0;
+        // strips alternate between w_a and w_b
+        if (residual_rk_pipe<NWAVES, KS, true>(w_a, w_b, s, B0, B1, T0, T1, accA, accB, vsB, L, W,
+                                               afr, tro, V, kh, n_strips, n_parts)) {
+            while (residual_rk_pipe<NWAVES, KS, false>(w_b, w_a, s, B0, B1, T0, T1, accA, accB,
+                                                       vsB, L, W, afr, tro, V, kh, n_strips,
+                                                       n_parts) &&
+                   residual_rk_pipe<NWAVES, KS, false>(w_a, w_b, s, B0, B1, T0, T1, accA, accB,
+                                                       vsB, L, W, afr, tro, V, kh, n_strips,
+                                                       n_parts)) {
+            }
+        }
+        res_tile(L.best, accB, T1, vsB, 1, L.R);  // the last tile (half 1, tile 1)
+    } else {
+        if (busy) load_half(t0, L.trow, s * kStripV, 0, kh, V);
+        while (residual_rk_light<NWAVES, KS>(w_a, w_b, s, t0, L, W, V, kh, n_strips, n_parts,
+                                             bonus_only) &&
+               residual_rk_light<NWAVES, KS>(w_b, w_a, s, t0, L, W, V, kh, n_strips, n_parts,
+                                             bonus_only)) {
+        }
     }
     // lanes l and l + 32 hold the two halves of every strip for one request
     RowState sr{-INFINITY, 0.0f, L.best.br, 0.0f, L.best.ir};
