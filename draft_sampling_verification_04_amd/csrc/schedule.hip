@@ -281,10 +281,26 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
         return b * uK + c;
     };
     if (staged) {
+        // eight loads in flight per thread: a load-then-store loop waits for
+        // each load in turn (16 to 32 round trips at the scheduled batch sizes)
         float* stage = reinterpret_cast<float*>(sh_sort);
-        for (long long o = tid; o < n_items; o += kThreads) {
-            const unsigned b = static_cast<unsigned>(o) / uK, k = static_cast<unsigned>(o) - b * uK;
-            stage[slot_of(b, k)] = conf[o];
+        constexpr int kStageBatch = 8;
+        for (long long o0 = tid; o0 < n_items; o0 += static_cast<long long>(kThreads) * kStageBatch) {
+            float v[kStageBatch];
+#pragma unroll
+            for (int u = 0; u < kStageBatch; ++u) {
+                const long long o = o0 + static_cast<long long>(u) * kThreads;
+                v[u] = o < n_items ? conf[o] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kStageBatch; ++u) {
+                const long long o = o0 + static_cast<long long>(u) * kThreads;
+                if (o < n_items) {
+                    const unsigned b = static_cast<unsigned>(o) / uK;
+                    const unsigned k = static_cast<unsigned>(o) - b * uK;
+                    stage[slot_of(b, k)] = v[u];
+                }
+            }
         }
         __syncthreads();
         for (int b = tid; b < B; b += kThreads) {
@@ -583,9 +599,14 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
     if (!take_all) {
         for (int b = tid; b < B; b += kThreads) {
             int L = 0;
-            for (int k = 0; k < K; ++k) {
-                const uint64_t key = keys[static_cast<size_t>(b) * K + k];
-                L += (key != kNoKey && key <= theta);
+            const uint64_t* row = keys + static_cast<size_t>(b) * K;
+            for (int k0 = 0; k0 < K; k0 += 8) {  // eight loads in flight, none conditional
+                uint64_t kv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) kv[u] = row[min(k0 + u, K - 1)];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    L += (k0 + u < K && kv[u] != kNoKey && kv[u] <= theta);
             }
             lengths[b] = L;
             if (b == tid) my_len = L;
