@@ -46,3 +46,23 @@ def test_rows_read_sums_over_requests():
     per = [bench.target_rows_read([l], [x], 16) for l, x in zip(L, a)]
     assert per == [4, 17, 17, 4, 1]
     assert bench.target_rows_read(L, a, 16) == sum(per)
+
+
+def test_stored_counters_follow_the_kernel_sources(monkeypatch):
+    """The committed counter figures are reported only while the dominant
+    kernel's sources hash to the value stored beside them; the vector-ALU view
+    is built from them and is null without them."""
+    text = open(bench.PMC_SUMMARY).read()
+    stored_hash = [l.split(":", 1)[1].strip() for l in text.splitlines()
+                   if l.startswith("source_hash:")][0]
+    monkeypatch.setattr(bench, "dominant_source_hash", lambda: stored_hash)
+    got = bench.stored_counters()
+    assert got is not None
+    assert got["traffic_bytes_per_launch"] > 0 and got["valu_instructions_per_launch"] > 0
+    view = bench.alu_view(got, 60e-6)
+    ops = 64 * (got["valu_instructions_per_launch"] + got["valu_trans_instructions_per_launch"])
+    assert view["lane_ops_per_launch"] == ops
+    assert abs(view["frac"] - ops / 60e-6 / 1e12 / bench.VALU_PEAK_TOPS) < 1e-3
+    monkeypatch.setattr(bench, "dominant_source_hash", lambda: "0" * 16)
+    assert bench.stored_counters() is None
+    assert bench.alu_view(None, 60e-6) is None
