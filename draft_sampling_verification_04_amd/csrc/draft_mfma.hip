@@ -741,6 +741,75 @@ __device__ __forceinline__ void rk_unit(f32x16& accm, const uint16_t* wt, const 
     if constexpr (SAMPLE && GREEDY) greedy_tile(run, accs, vs, ts);
 }
 
+// Load balancing of the rank-256 draft kernel.  Wavefronts w and w + 4 of a
+// workgroup share a SIMD, and requests are visited greedy first, so with a
+// third of the requests greedy two SIMDs hold two sampled wavefronts each
+// while the other two hold a greedy one (argmax only) beside a sampled one.
+// A sampled wavefront on a loaded SIMD then hands the last tile of every strip
+// but the final one to the greedy wavefront of a light SIMD: it writes the
+// tile's s values (16 per lane, 4 KiB) to LDS before the next strip's barrier,
+// and the helper draws that tile's keys and softmax terms for the same lanes
+// after the barrier, with the owner's request constants, into states of its
+// own that are merged into the owner's at the end.  Every key is computed by
+// the same code either way, so the draw does not depend on who takes a tile.
+constexpr int kRoleNone = 0;    // samples all its tiles
+constexpr int kRoleHelped = 1;  // hands the last tile of each strip to a helper
+constexpr int kRoleHelper = 2;  // greedy wavefront drawing two helped tiles per strip
+// s_waitcnt operand: vector-memory count <= 4 and every LDS access complete
+constexpr int kWaitVm4Lds = 4 | (7 << 4) | (0 << 8);
+// Handoff slots: [strip parity][helped index 0..3][4 float4 per lane][64 lanes].
+constexpr int kHandoffSlots = 2 * 4 * 4 * 64;
+
+// Barrier for LDS traffic only: waits for this wave's LDS accesses, not for
+// its outstanding global loads (which __syncthreads' fence would drain).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (0x3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// A helper's constants and running states for the lanes of the two wavefronts
+// it serves (helped indices h and h + 2 for helper wavefront h).
+struct Helper {
+    KeyLane kl[2];
+    PhiloxRow ph[2];
+    LaneRun run[2];
+};
+
+__device__ __forceinline__ float4* handoff_slot(float4* hs, int par, int idx) {
+    return hs + (par * 4 + idx) * 4 * 64;
+}
+
+__device__ __forceinline__ void put_tile(float4* slot, const f32x16& acc, int lane) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        slot[c * 64 + lane] = make_float4(acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]);
+}
+
+__device__ __forceinline__ void get_tile(f32x16& acc, const float4* slot, int lane) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float4 q = slot[c * 64 + lane];
+        acc[4 * c] = q.x;
+        acc[4 * c + 1] = q.y;
+        acc[4 * c + 2] = q.z;
+        acc[4 * c + 3] = q.w;
+    }
+}
+
+// Merge of two lane states (the softmax partials rescaled to the larger
+// maximum; the key by beats(), so the result does not depend on the order).
+__device__ __forceinline__ void run_merge(LaneRun& a, const LaneRun& b) {
+    const float M = fmaxf(a.m2, b.m2);
+    const float Mr = (M == -INFINITY) ? 0.0f : M;
+    a.s = a.s * __builtin_amdgcn_exp2f(a.m2 - Mr) + b.s * __builtin_amdgcn_exp2f(b.m2 - Mr);
+    a.m2 = M;
+    if (beats(b.key, b.idx, a.key, a.idx)) {
+        a.key = b.key;
+        a.idx = b.idx;
+    }
+}
+
 // One strip of draft_strip_mfma_rk: this strip's W is in `cur`, the next
 // strip's goes into `nxt`.  The caller alternates two static LDS arrays, so
 // every LDS access here names one array: the compiler then sees that the
@@ -749,15 +818,19 @@ __device__ __forceinline__ void rk_unit(f32x16& accm, const uint16_t* wt, const 
 // hold this strip's half-0 / half-1 logits on entry and the next strip's on
 // return (each is reloaded once both of its tiles are unpacked); accB holds the
 // previous strip's last tile (unsampled) on entry, and this strip's on return.
-// FIRST: no previous tile to sample.  Returns false after the last strip.
-template <int NWAVES, int KS, bool GREEDY, bool FIRST>
+// FIRST: no previous tile to sample.  PAR: the strip's parity (the handoff
+// slot it writes or reads).  Returns false after the last strip.
+template <int NWAVES, int KS, bool GREEDY, bool FIRST, int ROLE, int PAR>
 __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int& s, uint4 (&L0)[4],
                                          uint4 (&L1)[4], f32x16& accA, f32x16& accB, int& vsB,
                                          LaneRun& run, const uint16_t* __restrict__ W,
                                          const uint16_t* brow, const uint4 (&afr)[KS],
                                          const int (&tro)[2][2], const KeyLane& kl,
                                          const PhiloxRow& ph, int V, int kh, int n_strips,
-                                         int n_parts) {
+                                         int n_parts, float4* hs, int hidx, Helper& H) {
+    const int lane = threadIdx.x & 63;
+    // the previous strip's last tile goes to the helper
+    if constexpr (ROLE == kRoleHelped && !FIRST) put_tile(handoff_slot(hs, PAR, hidx), accB, lane);
     // This strip's W (all waves' shares) and half-0 logits have landed, and
     // every wave is done with the other buffer.  The wave's loads were issued
     // in the order W, half-0 logits, half-1 logits (the slices' scheduling
@@ -768,8 +841,12 @@ __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int
     // for every outstanding load) is enough: each wave has waited for its own
     // direct-to-LDS loads of this strip, every LDS read of the other buffer has
     // been consumed by an MFMA before it, and the empty asm keeps the compiler
-    // from moving memory accesses across it.
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    // from moving memory accesses across it.  A helped wave also waits for its
+    // handoff writes, so the helper reads them after the barrier.
+    if constexpr (ROLE == kRoleHelped)
+        __builtin_amdgcn_s_waitcnt(kWaitVm4Lds);
+    else
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const int v0 = s * kStripV;
@@ -782,10 +859,25 @@ __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int
     stage_w_tr_fixed<NWAVES, KS>(nxt, W, V, vn);
     const int vh0 = v0 + 8 * kh, vh1 = v0 + 64 + 8 * kh;
     tile_from_logits(accA, L0, 0);
-    rk_unit<KS, GREEDY, !FIRST>(accA, cur + tro[0][0], afr, accB, run, vsB, 1, kl, ph);
+    if constexpr (ROLE == kRoleHelped)
+        rk_unit<KS, GREEDY, false>(accA, cur + tro[0][0], afr, accB, run, vsB, 1, kl, ph);
+    else
+        rk_unit<KS, GREEDY, !FIRST>(accA, cur + tro[0][0], afr, accB, run, vsB, 1, kl, ph);
+    // a helper draws the two handed-off tiles of the previous strip, one after
+    // each of its first two units (the lanes' entry offsets are its own vsB)
+    if constexpr (ROLE == kRoleHelper && !FIRST) {
+        f32x16 acch;
+        get_tile(acch, handoff_slot(hs, PAR, threadIdx.x >> 6), lane);
+        sample_tile(H.run[0], acch, vsB, 1, H.kl[0], H.ph[0]);
+    }
     tile_from_logits(accB, L0, 1);
     load_half(L0, brow, vn, 0, kh, V);
     rk_unit<KS, GREEDY, true>(accB, cur + tro[0][1], afr, accA, run, vh0, 0, kl, ph);
+    if constexpr (ROLE == kRoleHelper && !FIRST) {
+        f32x16 acch;
+        get_tile(acch, handoff_slot(hs, PAR, (threadIdx.x >> 6) + 2), lane);
+        sample_tile(H.run[1], acch, vsB, 1, H.kl[1], H.ph[1]);
+    }
     tile_from_logits(accA, L1, 0);
     rk_unit<KS, GREEDY, true>(accA, cur + tro[1][0], afr, accB, run, vh0, 1, kl, ph);
     tile_from_logits(accB, L1, 1);
@@ -797,30 +889,32 @@ __device__ __forceinline__ bool rk_strip(const uint16_t* cur, uint16_t* nxt, int
     return true;
 }
 
-template <int NWAVES, int KS, bool GREEDY>
+template <int NWAVES, int KS, bool GREEDY, int ROLE>
 __device__ __forceinline__ void rk_strips(uint16_t* w_a, uint16_t* w_b, int s, LaneRun& run,
                                           const uint16_t* __restrict__ W, const uint16_t* brow,
                                           const uint4 (&afr)[KS], const int (&tro)[2][2],
                                           const KeyLane& kl, const PhiloxRow& ph, int V, int kh,
-                                          int n_strips, int n_parts) {
+                                          int n_strips, int n_parts, float4* hs, int hidx,
+                                          Helper& H) {
     stage_w_tr_fixed<NWAVES, KS>(w_a, W, V, s * kStripV);
     uint4 L0[4], L1[4];
     load_half(L0, brow, s * kStripV, 0, kh, V);
     load_half(L1, brow, s * kStripV, 1, kh, V);
     f32x16 accA, accB;
     int vsB = 0;
-    // strips alternate between w_a and w_b
-    if (rk_strip<NWAVES, KS, GREEDY, true>(w_a, w_b, s, L0, L1, accA, accB, vsB, run, W, brow,
-                                           afr, tro, kl, ph, V, kh, n_strips, n_parts)) {
-        while (rk_strip<NWAVES, KS, GREEDY, false>(w_b, w_a, s, L0, L1, accA, accB, vsB, run, W,
-                                                   brow, afr, tro, kl, ph, V, kh, n_strips,
-                                                   n_parts) &&
-               rk_strip<NWAVES, KS, GREEDY, false>(w_a, w_b, s, L0, L1, accA, accB, vsB, run, W,
-                                                   brow, afr, tro, kl, ph, V, kh, n_strips,
-                                                   n_parts)) {
+    // strips alternate between w_a (parity 0) and w_b (parity 1)
+    if (rk_strip<NWAVES, KS, GREEDY, true, ROLE, 0>(w_a, w_b, s, L0, L1, accA, accB, vsB, run, W,
+                                                    brow, afr, tro, kl, ph, V, kh, n_strips,
+                                                    n_parts, hs, hidx, H)) {
+        while (rk_strip<NWAVES, KS, GREEDY, false, ROLE, 1>(w_b, w_a, s, L0, L1, accA, accB, vsB,
+                                                            run, W, brow, afr, tro, kl, ph, V, kh,
+                                                            n_strips, n_parts, hs, hidx, H) &&
+               rk_strip<NWAVES, KS, GREEDY, false, ROLE, 0>(w_a, w_b, s, L0, L1, accA, accB, vsB,
+                                                            run, W, brow, afr, tro, kl, ph, V, kh,
+                                                            n_strips, n_parts, hs, hidx, H)) {
         }
     }
-    // the last tile (half 1, tile 1)
+    // the last tile (half 1, tile 1): never handed off
     if constexpr (GREEDY)
         greedy_tile(run, accB, vsB, 1);
     else
@@ -835,7 +929,8 @@ __device__ __forceinline__ void rk_strips(uint16_t* w_a, uint16_t* w_b, int s, L
 // half of the current strip are free.  Each lane folds the halves and strips
 // it visits into one running state, so a request gets n_parts partials per
 // step.  A wavefront whose lanes are all greedy (T == 0) runs the key-free
-// argmax epilogue.
+// argmax epilogue.  With eight wavefronts, greedy ones take tiles from the
+// sampled wavefronts of loaded SIMDs (the handoff above).
 template <int NWAVES, int KS>
 __global__ __launch_bounds__(64 * NWAVES)
 void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __restrict__ A,
@@ -843,12 +938,16 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
                       int prev_stride, const float* __restrict__ temperature,
                       const int32_t* __restrict__ order, uint64_t seed, int B, int K, int V,
                       int r, int k, PartialBuf part, int n_strips, int n_parts) {
-    // the two W buffers, [16 KS][kPitch] each (r == 16 KS)
+    constexpr bool kBalance = NWAVES == 8;
+    // the two W buffers, [16 KS][kPitch] each (r == 16 KS), and the handoff
+    // slots (160 KiB in all with eight wavefronts)
     __shared__ __attribute__((aligned(16))) uint16_t w_a[16 * KS * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t w_b[16 * KS * kPitch];
+    __shared__ float4 hs[kBalance ? kHandoffSlots : 1];
     const int lane = threadIdx.x & 63;
     const int kh = lane >> 5;
-    const int slot = (blockIdx.y * NWAVES + (threadIdx.x >> 6)) * 32 + (lane & 31);
+    const int wave = threadIdx.x >> 6;
+    const int slot = (blockIdx.y * NWAVES + wave) * 32 + (lane & 31);
     const bool active = slot < B;
     // lanes past B run request 0's row (every wave takes part in the MFMAs and
     // barriers) and store nothing
@@ -860,6 +959,35 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
                                     kTagDraft);
     // one epilogue per wavefront: the greedy one when no lane samples
     const bool wave_greedy = __all(!active || !(T > 0.0f));
+    // Roles: helper h in {0, 1} (greedy) serves wavefronts h + 2 and h + 6
+    // (one SIMD) when both sample.  The flags go through the handoff slots,
+    // which are first written after the first strip's barrier.
+    int role = kRoleNone;
+    int hidx = 0;
+    Helper H;
+    if constexpr (kBalance) {
+        int* flags = reinterpret_cast<int*>(hs);
+        if (lane == 0) flags[wave] = wave_greedy ? 1 : 0;
+        lds_barrier();
+        const int h = wave & 1;
+        const bool pair = flags[h] && !flags[h + 2] && !flags[h + 6];
+        if (wave < 2 && pair) role = kRoleHelper;
+        if (wave >= 2 && (wave & 3) >= 2 && pair) {
+            role = kRoleHelped;
+            hidx = (wave < 4) ? wave - 2 : wave - 4;
+        }
+        if (role == kRoleHelper) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int hslot = (blockIdx.y * NWAVES + wave + 2 + 4 * j) * 32 + (lane & 31);
+                const int hb = hslot < B ? order[hslot] : 0;
+                H.kl[j] = key_lane(temperature[hb]);
+                H.ph[j] = philox_row(seed, static_cast<uint32_t>(hb), static_cast<uint32_t>(k + 1),
+                                     kTagDraft);
+                H.run[j] = lane_empty();
+            }
+        }
+    }
     const uint16_t* arow = A + static_cast<size_t>(p) * r + 8 * kh;
     const uint16_t* brow = base + (static_cast<size_t>(b) * K + k) * V;
     uint4 afr[KS];  // r == 16 KS
@@ -869,12 +997,44 @@ void draft_strip_mfma_rk(const uint16_t* __restrict__ base, const uint16_t* __re
                            {tr_offset(lane, 1, 0), tr_offset(lane, 1, 1)}};
     LaneRun lr = lane_empty();
     const int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
-    if (wave_greedy)
-        rk_strips<NWAVES, KS, true>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph, V, kh, n_strips,
-                                    n_parts);
-    else
-        rk_strips<NWAVES, KS, false>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph, V, kh, n_strips,
-                                     n_parts);
+    // With balancing every wavefront meets two more barriers after its strips:
+    // after the first every handoff slot has been read, and the helpers' states
+    // for the helped lanes go through LDS to be merged into the owners'.
+    if (wave_greedy) {
+        if (kBalance && role == kRoleHelper) {
+            rk_strips<NWAVES, KS, true, kRoleHelper>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph, V,
+                                                     kh, n_strips, n_parts, hs, hidx, H);
+            lds_barrier();
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                hs[(wave + 2 * j) * 64 + lane] =
+                    make_float4(H.run[j].m2, H.run[j].s, H.run[j].key, __int_as_float(H.run[j].idx));
+            lds_barrier();
+        } else {
+            rk_strips<NWAVES, KS, true, kRoleNone>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph, V,
+                                                   kh, n_strips, n_parts, hs, hidx, H);
+            if constexpr (kBalance) {
+                lds_barrier();
+                lds_barrier();
+            }
+        }
+    } else {
+        if (kBalance && role == kRoleHelped) {
+            rk_strips<NWAVES, KS, false, kRoleHelped>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph,
+                                                      V, kh, n_strips, n_parts, hs, hidx, H);
+            lds_barrier();
+            lds_barrier();
+            const float4 q = hs[hidx * 64 + lane];
+            run_merge(lr, LaneRun{q.x, q.y, q.z, __float_as_int(q.w)});
+        } else {
+            rk_strips<NWAVES, KS, false, kRoleNone>(w_a, w_b, s, lr, W, brow, afr, tro, kl, ph, V,
+                                                    kh, n_strips, n_parts, hs, hidx, H);
+            if constexpr (kBalance) {
+                lds_barrier();
+                lds_barrier();
+            }
+        }
+    }
     // lanes l and l + 32 hold the two halves of every strip for one request
     RowState run = lane_row(lr);
     row_merge(run, xlane_row<5>(run));

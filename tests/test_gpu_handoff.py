@@ -1,0 +1,88 @@
+"""GPU parity of the rank-256 draft kernel's load balancing.
+
+With eight wavefronts per workgroup, a greedy wavefront draws the last tile of
+every strip but the final one for the sampled wavefronts of a loaded SIMD
+(wavefronts h + 2 and h + 6 for helper h in {0, 1}).  These cases place
+exactly n_greedy greedy requests at random positions, so the visit order
+(greedy first) puts chosen wavefronts in each role, with V large enough that
+every workgroup walks several strips.  The compared requests are the ones in
+the helped wavefronts' slots (greedy lanes of a mixed helped wavefront
+included) and a few from the others.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsp():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import draft_sampling_verification_04_amd as d
+
+    d.lib()  # raises when the HIP library is missing
+    return d
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    from draft_sampling_verification_04_amd import inputs as m
+
+    return m
+
+
+def _visit_order(temp):
+    t = temp.cpu().numpy()
+    return [b for b in range(len(t)) if not t[b] > 0] + [b for b in range(len(t)) if t[b] > 0]
+
+
+# (B, V, K, n_greedy): 64 -> both helpers; 70 -> helper 0 serves a mixed
+# wavefront 2; 40 -> only helper 0 (wavefront 1 mixed); 96 -> only helper 1;
+# B = 300 -> a second request group with no helpers; B = 512 -> two groups,
+# the second all sampled
+CASES = [
+    (256, 70016, 3, 64),
+    (256, 66048, 2, 70),
+    (256, 66048, 2, 40),
+    (256, 66048, 2, 96),
+    (300, 40064, 3, 70),
+    (512, 40064, 2, 64),
+]
+
+
+@pytest.mark.parametrize("B,V,K,n_greedy", CASES)
+def test_rank256_handoff_parity(dsp, orc, inputs, B, V, K, n_greedy):
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=B, K=K, V=V)
+    inp = inputs.make_inputs(w, "cuda", seed=11, with_target=False)
+    rng = np.random.default_rng(B + V + n_greedy)
+    t = np.where(rng.random(B) < 0.5, 0.7, 1.0).astype(np.float32)
+    t[rng.permutation(B)[:n_greedy]] = 0.0
+    inp["temp"] = torch.from_numpy(t).to("cuda")
+    order = _visit_order(inp["temp"])
+    # slots of wavefronts 2, 3, 6 and 7 of every request group, six per wavefront
+    idx = set()
+    for g in range((B + 255) // 256):
+        for wv in (2, 3, 6, 7):
+            slots = [s for s in range((g * 8 + wv) * 32, (g * 8 + wv + 1) * 32) if s < B]
+            for s in slots[:: max(1, len(slots) // 6)][:6]:
+                idx.add(order[s])
+        for wv in (0, 1, 4, 5):
+            s = (g * 8 + wv) * 32 + 5
+            if s < B:
+                idx.add(order[s])
+    idx = sorted(idx)
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], 7)
+    torch.cuda.synchronize()
+    ora = P.oracle_draft(orc, inp, idx, 7)
+    tally = P.Tally()
+    P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
+                    inp["temp"].cpu().numpy(), P.tol_for(w.dtype), tally)
+    print(B, V, K, n_greedy, len(idx), tally)
+    assert tally.near_ties <= 1
+    assert tally.draft_clean >= len(idx) - 1
+    del inp
+    torch.cuda.empty_cache()
