@@ -1620,22 +1620,6 @@ hipError_t allow_big_lds(Kern* kern, LdsReady& ready) {
     return e;
 }
 
-// Compute units of the current device, queried once per device (a racing
-// first query stores the same value).
-int device_cus() {
-    static std::atomic<int> cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cus[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cus[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // `lds` is the dynamic LDS of the launch (0 for a kernel whose W buffers are
 // static arrays).
 template <int NWAVES, typename Kern>
@@ -1712,6 +1696,22 @@ hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
+
+// Compute units of the current device, queried once per device (a racing
+// first query stores the same value).
+int device_cus() {
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 int mfma_draft_strip() { return kStripV; }
 

@@ -106,6 +106,8 @@ struct ResidualArgs {
 bool residual_mfma_supported(const VerifyArgs& a);
 hipError_t launch_residual_mfma(const ResidualArgs& a, int* n_parts);
 hipError_t launch_verify(const VerifyArgs& a);
+// Compute units of the current device (queried once per device).
+int device_cus();
 
 constexpr int kMaxCurvePoints = 64;
 

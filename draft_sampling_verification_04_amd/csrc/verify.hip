@@ -20,6 +20,8 @@
 // bf16, VALU otherwise) and stream the target row j* again, split in
 // vocabulary strips, keeping the best residual and fallback keys; (4) the
 // strips are folded into the next token.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -190,16 +192,16 @@ __device__ __forceinline__ void row_finish(const RowState& st, const LT* trow, i
 constexpr int kVRowThreads = 512;
 constexpr int kVRowUnroll = 4;
 
+// One target row (job.live): its normaliser, argmax or bonus draw, reduced
+// over the workgroup, and the row's end (row_finish).  Called by every thread.
 template <typename LT, bool VEC>
-__global__ __launch_bounds__(kVRowThreads) void verify_rows(
-    const LT* __restrict__ target, const int64_t* __restrict__ row_off,
-    const int32_t* __restrict__ lengths, const int32_t* __restrict__ tokens,
-    const float* __restrict__ draft_logp, const float* __restrict__ temperature, uint64_t seed,
-    int K, int V, int64_t n_rows, bool bonus_draw, float* __restrict__ row_lse_t,
-    float* __restrict__ row_logratio, VerifyWs ws, int j_lo, int span) {
-    __shared__ RowState red[kVRowThreads / kWave];
-    const RowJob job = row_begin(row_off, lengths, temperature, K, n_rows, ws, j_lo, span);
-    if (!job.live) return;
+__device__ __forceinline__ void verify_row(const RowJob& job, const LT* __restrict__ target,
+                                           const int32_t* __restrict__ tokens,
+                                           const float* __restrict__ draft_logp, uint64_t seed,
+                                           int K, int V, bool bonus_draw,
+                                           float* __restrict__ row_lse_t,
+                                           float* __restrict__ row_logratio, VerifyWs ws,
+                                           RowState* red) {
     const int b = job.b, j = job.j;
     const int64_t row = job.row;
     const float T = job.T;
@@ -298,6 +300,109 @@ __global__ __launch_bounds__(kVRowThreads) void verify_rows(
     if (threadIdx.x == 0)
         row_finish(st, trow, row, b, j, greedy, bonus, T, tokens, draft_logp, seed, K, V, row_lse_t,
                    row_logratio, ws);
+}
+
+template <typename LT, bool VEC>
+__global__ __launch_bounds__(kVRowThreads) void verify_rows(
+    const LT* __restrict__ target, const int64_t* __restrict__ row_off,
+    const int32_t* __restrict__ lengths, const int32_t* __restrict__ tokens,
+    const float* __restrict__ draft_logp, const float* __restrict__ temperature, uint64_t seed,
+    int K, int V, int64_t n_rows, bool bonus_draw, float* __restrict__ row_lse_t,
+    float* __restrict__ row_logratio, VerifyWs ws, int j_lo, int span) {
+    __shared__ RowState red[kVRowThreads / kWave];
+    const RowJob job = row_begin(row_off, lengths, temperature, K, n_rows, ws, j_lo, span);
+    if (!job.live) return;
+    verify_row<LT, VEC>(job, target, tokens, draft_logp, seed, K, V, bonus_draw, row_lse_t,
+                        row_logratio, ws, red);
+}
+
+// The second launch of the decisive rows (positions j_lo .. L_b + 1, after
+// the launch of positions 1 .. j_lo - 1) over a fixed grid: every workgroup
+// first lists, in LDS, the rows still needed, those of the requests whose rows
+// 1 .. j_lo - 1 were all accepted, then takes rows blockIdx.x, blockIdx.x +
+// gridDim.x, ... of that list.  A one-row-per-workgroup grid over every
+// (request, position) spent most of its workgroups on requests already
+// rejected.  B <= kTailMaxB.
+constexpr int kTailMaxB = 4096;
+
+template <typename LT, bool VEC>
+__global__ __launch_bounds__(kVRowThreads) void verify_rows_tail(
+    const LT* __restrict__ target, const int64_t* __restrict__ row_off,
+    const int32_t* __restrict__ lengths, const int32_t* __restrict__ tokens,
+    const float* __restrict__ draft_logp, const float* __restrict__ temperature, uint64_t seed,
+    int B, int K, int V, int64_t n_rows, bool bonus_draw, VerifyWs ws, int j_lo) {
+    __shared__ RowState red[kVRowThreads / kWave];
+    __shared__ int pre[kTailMaxB];  // exclusive prefix of the rows each request needs
+    __shared__ int wsum[kVRowThreads / kWave];
+    __shared__ int total;
+    constexpr int kPer = kTailMaxB / kVRowThreads;  // requests per thread
+    int cnt[kPer];
+    int mine = 0;
+    const int b0 = threadIdx.x * kPer;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = b0 + i;
+        int n = 0;
+        if (b < B) {
+            const int L = lengths ? clamp_len(lengths[b], K) : K;
+            const int64_t o = row_off[b];
+            if (L + 1 >= j_lo && o >= 0 && o + L + 1 <= n_rows) {
+                n = L + 2 - j_lo;
+                const int32_t* acc = ws.accept + static_cast<size_t>(b) * (K + 1);
+                for (int q = 0; q < j_lo - 1; ++q) n = acc[q] ? n : 0;
+            }
+        }
+        cnt[i] = n;
+        mine += n;
+    }
+    // exclusive scan of the per-thread totals: within each wavefront, then
+    // over the wavefront totals
+    const int lane = threadIdx.x & (kWave - 1);
+    int inc = mine;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    if (lane == kWave - 1) wsum[threadIdx.x / kWave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < kVRowThreads / kWave; ++w) {
+        before += (w < static_cast<int>(threadIdx.x / kWave)) ? wsum[w] : 0;
+        all += wsum[w];
+    }
+    int run = before + inc - mine;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (b0 + i < B) pre[b0 + i] = run;
+        run += cnt[i];
+    }
+    if (threadIdx.x == 0) total = all;
+    __syncthreads();
+    const int n_jobs = total;
+    for (int q = blockIdx.x; q < n_jobs; q += gridDim.x) {
+        // the request of list entry q: the last b with pre[b] <= q
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= q)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        RowJob job{};
+        job.b = lo;
+        job.j = j_lo + (q - pre[lo]);
+        const int L = lengths ? clamp_len(lengths[job.b], K) : K;
+        job.row = row_off[job.b] + (job.j - 1);
+        job.T = temperature[job.b];
+        job.greedy = !(job.T > 0.0f);
+        job.bonus = (job.j == L + 1);
+        job.live = true;
+        verify_row<LT, VEC>(job, target, tokens, draft_logp, seed, K, V, bonus_draw, nullptr,
+                            nullptr, ws, red);
+        __syncthreads();  // red is reused by the next row
+    }
 }
 
 __global__ __launch_bounds__(256) void verify_resolve(int B, int K, int64_t n_rows,
@@ -554,7 +659,25 @@ hipError_t launch_verify(const VerifyArgs& a) {
         const int span = every_row ? a.K + 1 : verify_rows_chunk(j_lo, a.K);
         const dim3 rows_grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * span));
         ProfScope rows_scope(DSPARK_KERNEL_VERIFY_ROWS, a.stream);
-        if (a.logit_dt == DSPARK_BF16) {
+        if (!every_row && j_lo > 1 && a.B <= kTailMaxB) {
+            // the rows still needed, listed by every workgroup of a fixed grid
+            // (four 512-thread workgroups per CU)
+            const int64_t most = static_cast<int64_t>(a.B) * span;
+            const dim3 tail_grid(static_cast<unsigned>(std::max<int64_t>(
+                1, std::min<int64_t>(most, 4 * static_cast<int64_t>(device_cus())))));
+            if (a.logit_dt == DSPARK_BF16)
+                hipLaunchKernelGGL((vec ? verify_rows_tail<bf16_t, true> : verify_rows_tail<bf16_t, false>),
+                                   tail_grid, dim3(kVRowThreads), 0, a.stream,
+                                   static_cast<const bf16_t*>(a.target), a.row_off, a.lengths,
+                                   a.tokens, a.draft_logp, a.temperature, a.seed, a.B, a.K, a.V,
+                                   a.n_rows, !bonus_in_residual, ws, j_lo);
+            else
+                hipLaunchKernelGGL((vec ? verify_rows_tail<float, true> : verify_rows_tail<float, false>),
+                                   tail_grid, dim3(kVRowThreads), 0, a.stream,
+                                   static_cast<const float*>(a.target), a.row_off, a.lengths,
+                                   a.tokens, a.draft_logp, a.temperature, a.seed, a.B, a.K, a.V,
+                                   a.n_rows, !bonus_in_residual, ws, j_lo);
+        } else if (a.logit_dt == DSPARK_BF16) {
             hipLaunchKernelGGL((vec ? verify_rows<bf16_t, true> : verify_rows<bf16_t, false>),
                                rows_grid, dim3(kVRowThreads), 0, a.stream,
                                static_cast<const bf16_t*>(a.target), a.row_off, a.lengths,
