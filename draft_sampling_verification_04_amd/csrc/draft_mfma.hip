@@ -584,6 +584,43 @@ __device__ __forceinline__ void load_half(uint4 (&q)[4], const uint16_t* row, in
     }
 }
 
+// The first strip's logits of a launch, coalesced.  Every CU asks for its
+// first strip at once, and per-lane loads (32 rows x 32 bytes per instruction)
+// make four times the cache requests of whole row pieces.  So the wave's 32
+// rows x 256 bytes go by direct loads into LDS (the second W buffer, free
+// until the first strip's barrier), 16 lanes per row piece: chunk c of row j
+// lands in slot c ^ (j % 16), which spreads the lanes of a later read over all
+// banks.  Then each lane reads its eight chunks (those of load_half, with the
+// same -inf chunks past V) into L0 / L1.
+__device__ __forceinline__ void first_strip_logits(uint4 (&L0)[4], uint4 (&L1)[4], uint16_t* lds,
+                                                   const uint16_t* brow, int v0, int kh, int V) {
+    const int lane = threadIdx.x & 63;
+    uint16_t* wl = lds + (threadIdx.x >> 6) * 32 * kStripV;  // the wave's 32 rows (8 KiB)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 4 * q + (lane >> 4);
+        const uint16_t* rp = reinterpret_cast<const uint16_t*>(
+            __shfl(reinterpret_cast<unsigned long long>(brow), row, kWave));
+        const int v = v0 + 8 * ((lane & 15) ^ (row & 15));
+        const void* src = (v < V) ? static_cast<const void*>(rp + v)
+                                  : static_cast<const void*>(&kNegInfChunk);
+        __builtin_amdgcn_global_load_lds(src, wl + q * 4 * kStripV, 16, 0, 0);
+    }
+    // the wave's own direct loads have landed: wait for every load it has out
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    const int j = lane & 31;
+    const uint16_t* rl = wl + j * kStripV;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        L0[a] = *reinterpret_cast<const uint4*>(rl + 8 * ((2 * a + kh) ^ (j & 15)));
+        L1[a] = *reinterpret_cast<const uint4*>(rl + 8 * ((8 + 2 * a + kh) ^ (j & 15)));
+    }
+    // every read of the buffer is done before this wave meets the first strip's
+    // barrier, after which the next strip's W goes into it
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (0x3 << 14));
+}
+
 // The -inf fix-up for chunks past V, for callers that load with the row's
 // last chunk standing in (the residual kernel).
 __device__ __forceinline__ void tail_half(uint4 (&q)[4], int v0, int h, int kh, int V) {
@@ -898,8 +935,7 @@ __device__ __forceinline__ void rk_strips(uint16_t* w_a, uint16_t* w_b, int s, L
                                           Helper& H) {
     stage_w_tr_fixed<NWAVES, KS>(w_a, W, V, s * kStripV);
     uint4 L0[4], L1[4];
-    load_half(L0, brow, s * kStripV, 0, kh, V);
-    load_half(L1, brow, s * kStripV, 1, kh, V);
+    first_strip_logits(L0, L1, w_b, brow, s * kStripV, kh, V);
     f32x16 accA, accB;
     int vsB = 0;
     // strips alternate between w_a (parity 0) and w_b (parity 1)
