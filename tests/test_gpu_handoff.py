@@ -1,4 +1,5 @@
-"""GPU parity of the rank-256 draft kernel's load balancing.
+"""GPU parity of the rank-256 draft kernel's load balancing, and of the
+residual kernel with a long residual list.
 
 With eight wavefronts per workgroup, a greedy wavefront draws the last tile of
 every strip but the final one for the sampled wavefronts of a loaded SIMD
@@ -84,5 +85,47 @@ def test_rank256_handoff_parity(dsp, orc, inputs, B, V, K, n_greedy):
     print(B, V, K, n_greedy, len(idx), tally)
     assert tally.near_ties <= 1
     assert tally.draft_clean >= len(idx) - 1
+    del inp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n_sampled", [140, 170, 185])
+def test_residual_handoff_parity(dsp, orc, inputs, n_sampled):
+    """The residual strip kernel with a long residual list: with a target far
+    from the draft most sampled requests reject at their first row, so the list
+    holds about n_sampled requests and fills five to six of the eight
+    wavefronts, over several strips per workgroup.  Every sampled request's
+    verify result is compared with the oracle's on the GPU's drafted tokens."""
+    B, V, K = 256, 70016, 3
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=B, K=K, V=V, noise_lo=6.0, noise_hi=6.0)
+    inp = inputs.make_inputs(w, "cuda", seed=13)
+    rng = np.random.default_rng(n_sampled)
+    t = np.zeros(B, np.float32)
+    t[rng.permutation(B)[:n_sampled]] = rng.choice(np.float32([0.7, 1.0]), n_sampled)
+    inp["temp"] = torch.from_numpy(t).to("cuda")
+    seed = 9
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], seed)
+    target = inp["target"].reshape(-1, V)
+    offs = torch.arange(B, dtype=torch.int64, device="cuda") * (K + 1)
+    acc, nxt, rl, rr = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                         inp["W"], target, offs, inp["temp"], seed)
+    acc2, nxt2, _, _ = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                         inp["W"], target, offs, inp["temp"], seed,
+                                         row_outputs=False)
+    torch.cuda.synchronize()
+    assert torch.equal(acc2, acc) and torch.equal(nxt2, nxt)
+    idx = [int(b) for b in np.nonzero(t > 0)[0]]
+    acc_np = acc.cpu().numpy()
+    assert (acc_np[idx] < K).sum() >= 0.9 * len(idx)  # the list is about n_sampled long
+    tok_np = tok.cpu().numpy()
+    rows = {b: P.np32(target[b * (K + 1):(b + 1) * (K + 1)]) for b in idx}
+    orv = P.oracle_verify(orc, inp, idx, {b: tok_np[b] for b in idx}, rows, {b: K for b in idx},
+                          seed)
+    tally = P.compare_verify(acc_np, nxt.cpu().numpy(), rl.cpu().numpy(), rr.cpu().numpy(),
+                             offs.cpu().numpy(), orv, P.tol_for(w.dtype))
+    print(n_sampled, len(idx), tally)
+    assert tally.near_ties <= 1
+    assert tally.verify_clean >= len(idx) - 1
     del inp
     torch.cuda.empty_cache()
