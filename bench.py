@@ -17,6 +17,7 @@ import os
 import subprocess
 import sys
 import time
+from types import SimpleNamespace
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -51,6 +52,10 @@ def parse():
                     help="also calibrate a synthetic, over-confident confidence head against "
                          "the acceptance outcomes of dspark_verify with sequential temperature "
                          "scaling, and report the expected calibration error before and after")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="report the headline measurement only (by default the line also "
+                         "carries --markov-vs-parallel, --sps-curve, --calibration and short "
+                         "timed runs of the other workloads, measured after the headline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain copy kernel (torch.neg, fp32) of this many MiB before "
                          "warmup, as the reference for HBM counter scaling")
@@ -443,23 +448,9 @@ def calibration(d, inp, w, dev, seeds=16, over=2.0):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): requests are "
-              "independent, so more GPUs would each run this same path on their own share of "
-              "the batch, and no multi-GPU figure is produced", file=sys.stderr)
-        sys.exit(2)
-    import torch
-
-    import draft_sampling_verification_04_amd as d
-    from draft_sampling_verification_04_amd import inputs
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    d.lib()
-    dev = torch.device("cuda:0")
-    w = inputs.WORKLOADS[args.workload]
-    seed = 20260627
+def prepare(d, inputs, torch, w, dev, seed):
+    """Inputs, outputs and workspaces of one workload, laid out before any
+    timing, and the step that runs draft -> schedule -> verify on them."""
     inp = inputs.make_inputs(w, dev, seed=1, with_target=not w.ragged)
     conf, _ = inputs.make_confidence(w, dev, seed=1)
     B, K, V, r = w.B, w.K, w.V, w.r
@@ -496,15 +487,6 @@ def main():
         vofs = inputs.dense_offsets(B, K, dev)
     torch.cuda.synchronize()
 
-    if args.copy_probe_mib > 0:
-        # reference kernel for counter scaling: reads and writes exactly N MiB
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-
     def step(events=None):
         if events:
             events[0].record(stream)
@@ -521,6 +503,74 @@ def main():
                         row_outputs=False, workspace=ws_v)
         if events:
             events[3].record(stream)
+
+    return SimpleNamespace(inp=inp, conf=conf, B=B, K=K, V=V, r=r, budget=budget, tok=tok,
+                           logp=logp, lse=lse, L=L, offs=offs, acc=acc, nxt=nxt, target=target,
+                           vofs=vofs, stream=stream, step=step)
+
+
+def quick_workload(d, inputs, torch, name, dev, seed, steps=5, warmup=1):
+    """A short timed run of another workload (its own inputs at full size):
+    tokens/s over `steps` steps after `warmup`, and the phases of one more
+    step bracketed with events."""
+    w = inputs.WORKLOADS[name]
+    st = prepare(d, inputs, torch, w, dev, seed)
+    for _ in range(warmup):
+        st.step()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(st.stream)
+    for _ in range(steps):
+        st.step()
+    t1.record(st.stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    st.step(ev)
+    torch.cuda.synchronize()
+    out = {"B": w.B, "K": w.K, "V": w.V, "budget_tokens": st.budget,
+           "tokens_per_s": round(w.B * w.K / (ms_step / 1e3), 1), "ms_per_step": round(ms_step, 4),
+           "steps": steps, "warmup": warmup,
+           "phases_ms": {"draft": round(ev[0].elapsed_time(ev[1]), 4),
+                         "schedule": round(ev[1].elapsed_time(ev[2]), 4),
+                         "verify": round(ev[2].elapsed_time(ev[3]), 4)},
+           "verified_tokens_per_step": int(st.L.sum())}
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): requests are "
+              "independent, so more GPUs would each run this same path on their own share of "
+              "the batch, and no multi-GPU figure is produced", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import draft_sampling_verification_04_amd as d
+    from draft_sampling_verification_04_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    d.lib()
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    seed = 20260627
+    st = prepare(d, inputs, torch, w, dev, seed)
+    inp, conf, B, K, V, r, budget = st.inp, st.conf, st.B, st.K, st.V, st.r, st.budget
+    tok, logp, lse, L, offs, acc, nxt = st.tok, st.logp, st.lse, st.L, st.offs, st.acc, st.nxt
+    target, vofs, stream, step = st.target, st.vofs, st.stream, st.step
+
+    if args.copy_probe_mib > 0:
+        # reference kernel for counter scaling: reads and writes exactly N MiB
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -673,17 +723,26 @@ def main():
         "vocab_logits_per_s": round((B * K * V + rows_read * V) / (ms_step / 1e3), 1),
         "host_cpu": f"{model} x{ncpu}",
     }
-    if args.markov_vs_parallel:
-        out["markov_vs_parallel"] = markov_vs_parallel(d, inp, seed)
-    if args.sps_curve:
-        out["sps_curve"] = sps_curve(d, inputs, dev)
-    if args.calibration:
-        if w.ragged:
-            raise SystemExit("--calibration needs a workload with dense target rows")
-        out["calibration"] = calibration(d, inp, w, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["oracle_parity"] = cpu_baseline(
             w, inp, seed, args.cpu_requests, target, vofs, L, (tok, acc, nxt))
+    # The other measurements run after the headline one, outside its timed
+    # region: the cost of the sequential head against parallel drafting, a
+    # measured stair-step latency curve in the scheduler, calibration of a
+    # synthetic confidence head, and short runs of the budgeted workloads.
+    extras = not args.no_extras
+    if args.markov_vs_parallel or extras:
+        out["markov_vs_parallel"] = markov_vs_parallel(d, inp, seed)
+    if args.sps_curve or extras:
+        out["sps_curve"] = sps_curve(d, inputs, dev)
+    if args.calibration or (extras and not w.ragged):
+        if w.ragged:
+            raise SystemExit("--calibration needs a workload with dense target rows")
+        out["calibration"] = calibration(d, inp, w, dev)
+    if extras:
+        out["other_workloads"] = {
+            name: quick_workload(d, inputs, torch, name, dev, seed)
+            for name in ("qwen3_4b", "conf_sched", "high_conc") if name != w.name}
     print(json.dumps(out), flush=True)
 
 
