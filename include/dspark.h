@@ -245,7 +245,7 @@ dspark_status dspark_verify(const int32_t* draft_tokens, const int32_t* prev_tok
 typedef enum dspark_kernel {
     DSPARK_KERNEL_DRAFT_STRIP = 0,       /* draft: bias GEMM + logits + per-entry keys over vocab strips */
     DSPARK_KERNEL_DRAFT_COMBINE = 1,     /* draft: merge of the partials (token, logp, lse) */
-    DSPARK_KERNEL_VERIFY_ROWS = 2,       /* verify: target normaliser and accept test per row */
+    DSPARK_KERNEL_VERIFY_ROWS = 2,       /* verify: target normaliser and accept test per row (both launches) */
     DSPARK_KERNEL_VERIFY_RESOLVE = 3,    /* verify: strict-prefix resolution per request */
     DSPARK_KERNEL_RESIDUAL_STRIP = 4,    /* verify: residual / fallback Gumbel over a vocab strip */
     DSPARK_KERNEL_RESIDUAL_COMBINE = 5,  /* verify: merge of the residual partials */
