@@ -42,10 +42,12 @@ def _visit_order(temp):
 
 # (B, V, K, n_greedy): 64 -> both helpers; 70 -> helper 0 serves a mixed
 # wavefront 2; 40 -> only helper 0 (wavefront 1 mixed); 96 -> only helper 1;
+# B = 200 -> wavefront 6 half active and 7 inactive (helper 0 only);
 # B = 300 -> a second request group with no helpers; B = 512 -> two groups,
 # the second all sampled
 CASES = [
     (256, 70016, 3, 64),
+    (200, 66048, 2, 64),
     (256, 66048, 2, 70),
     (256, 66048, 2, 40),
     (256, 66048, 2, 96),
