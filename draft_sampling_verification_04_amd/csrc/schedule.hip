@@ -23,6 +23,12 @@
 // across wavefronts pass through LDS): the walk depends only on the S
 // sequence, and the exact threshold key is then selected among the keys that
 // share the stop item's S.  Larger inputs sort whole keys in workspace memory.
+// A curve that is one positive constant over every batch size the walk can
+// reach ([B, B + D]) cannot stop it before D while the taken S are far above
+// the fp64 rounding of the running total: then the D-th key is the threshold
+// and nothing is sorted.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,11 +43,12 @@ constexpr int kKeyRegs = 32;     // keys per thread kept in registers while B * 
 
 struct Curve {
     int n;
+    int flat;  // tau is one positive constant on [B, B + D] (set by the launcher)
     double cn[kMaxCurvePoints];
     double ct[kMaxCurvePoints];
 };
 
-__device__ double curve_tau(const Curve& c, double N) {
+__host__ __device__ double curve_tau(const Curve& c, double N) {
     if (c.n <= 0) return 1.0;
     if (c.n == 1 || N <= c.cn[0]) return c.ct[0];
     for (int i = 1; i < c.n; ++i) {
@@ -499,7 +506,17 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
         theta = select_key(0, 0, static_cast<unsigned>(dsel - 1), 7, kNoKey - 1, in_regs);
     }
 
-    if (curve.n > 0 && dsel > 0) {
+    // With tau one positive constant over every batch size the walk visits
+    // ([B, B + D]), the objective (B + sum S) / tau rises strictly exactly
+    // when a taken S does not vanish against the fp64 running total (at most
+    // B + dsel).  When the smallest candidate S is at least (B + dsel) 2^-40,
+    // no comparison comes near rounding and the walk takes all dsel
+    // candidates: the threshold found above stands and nothing is sorted.
+    const bool flat_walk =
+        curve.n > 0 && curve.flat && dsel > 0 && dsel < static_cast<long long>(n_pos) &&
+        static_cast<double>(survival_of(static_cast<uint32_t>(theta >> 32))) >=
+            static_cast<double>(B + dsel) * 0x1p-40;
+    if (curve.n > 0 && dsel > 0 && !flat_walk) {
         // 3. sort the candidates; the strict-rise test sets the threshold
         int npow = kThreads;
         while (npow < dsel) npow <<= 1;
@@ -660,6 +677,18 @@ hipError_t launch_schedule(const ScheduleArgs& a) {
     for (int i = 0; i < kMaxCurvePoints; ++i) {
         c.cn[i] = i < a.n_points ? a.curve_n[i] : 0.0;
         c.ct[i] = i < a.n_points ? a.curve_tau[i] : 0.0;
+    }
+    // tau is constant on [B, B + D] when it takes one value at both ends and
+    // at every point inside (piecewise linear between the points)
+    c.flat = 0;
+    if (c.n > 0) {
+        const double lo = static_cast<double>(a.B);
+        const double hi = lo + static_cast<double>(std::max<long long>(0, a.budget - a.B));
+        const double t0 = curve_tau(c, lo);
+        bool flat = t0 > 0.0 && curve_tau(c, hi) == t0;
+        for (int i = 0; i < c.n && flat; ++i)
+            if (c.cn[i] > lo && c.cn[i] < hi && c.ct[i] != t0) flat = false;
+        c.flat = flat ? 1 : 0;
     }
     ProfScope scope(DSPARK_KERNEL_SCHEDULE, a.stream);
     hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, a.stream, a.conf, a.B, a.K,

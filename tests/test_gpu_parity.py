@@ -258,6 +258,45 @@ def test_schedule_large_parity(dsp, orc, B, K, extra, conf_kind):
         np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
 
 
+def test_schedule_flat_curve_boundaries(dsp, orc):
+    """A latency curve that is constant over every batch size the walk can
+    reach ([B, B + D]) lets the scheduler take the threshold without sorting,
+    when no taken S is small enough to vanish against the running total.
+    Around that shortcut: survival values that do vanish in fp64 (the
+    oracle's walk stops before D), a constant curve with a point inside the
+    range, a dip inside the range, and a rise one token before B + D."""
+    rng = np.random.default_rng(17)
+    B, K = 100, 8
+    cases = []
+    # S = 1e-3^k: from k = 5 on, S < (B + sum S) 2^-53, so E + S == E
+    tiny = np.full((B, K), 1e-3, np.float32)
+    cases.append(("vanishing S", tiny, B + 700, [float(B), float(B + 700)], [2.0, 2.0], True))
+    conf = rng.beta(5, 2, (B, K)).astype(np.float32)
+    D = 500
+    cases.append(("point inside", conf, B + D, [B - 5.0, B + 7.0, B + D + 3.0], [2.0, 2.0, 2.0],
+                  False))
+    cases.append(("dip inside", conf, B + D, [float(B), B + 250.0, float(B + D)], [1.0, 0.5, 1.0],
+                  False))
+    cases.append(("rise before B + D", conf, B + D, [float(B), B + D - 1.0, B + D + 100.0],
+                  [1.0, 1.0, 3.0], False))
+    c_t = {}
+    for name, conf_c, budget, cn, ct, early in cases:
+        key = id(conf_c)
+        if key not in c_t:
+            c_t[key] = torch.from_numpy(conf_c).cuda()
+        cn32, ct32 = np.array(cn, np.float32), np.array(ct, np.float32)
+        L, offs, S = dsp.dspark_schedule(c_t[key], budget, cn32.tolist(), ct32.tolist())
+        torch.cuda.synchronize()
+        oL, ooffs, oS, n = orc.schedule(conf_c, budget, cn32.astype(np.float64),
+                                        ct32.astype(np.float64))
+        print(name, "taken", n, "of", budget - B)
+        np.testing.assert_array_equal(S.cpu().numpy(), oS)
+        np.testing.assert_array_equal(L.cpu().numpy(), oL)
+        np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+        if early:
+            assert 0 < n < budget - B  # the oracle's walk stopped at a vanishing S
+
+
 @pytest.mark.parametrize("jump", [1.05, 1.3, 2.0])
 def test_schedule_stair_step_curve_parity(dsp, orc, inputs, jump):
     """A stair-step latency curve over the whole selectable range (49 points
