@@ -1546,12 +1546,22 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     const int32_t* __restrict__ list, const int32_t* __restrict__ count_ptr,
     const int32_t* __restrict__ lengths, const float* __restrict__ lse_tab, uint64_t seed, int B,
     int K,
-    int V, int r, PartialBuf res, PartialBuf fall, int n_strips, int n_parts) {
+    int V, int r, PartialBuf res, PartialBuf fall, int n_strips, int n_wgs) {
     __shared__ __attribute__((aligned(16))) uint16_t w_a[16 * KS * kPitch];
     __shared__ __attribute__((aligned(16))) uint16_t w_b[16 * KS * kPitch];
+    // The listed requests fill `groups` request groups; the n_wgs workgroups
+    // of the grid are split over those groups only (the list's length is
+    // known on the device alone), so that every CU works however long it is.
+    // The launch has n_wgs >= the groups B requests can fill, so n_parts >= 1
+    // parts of every group are covered.
     const int count = listed_count(count_ptr);
-    const int slot0 = blockIdx.y * NWAVES * 32;
-    if (slot0 >= count) return;  // whole workgroup idle
+    const int groups = (count + NWAVES * 32 - 1) / (NWAVES * 32);
+    if (groups == 0) return;
+    const int n_parts = residual_parts(n_strips, n_wgs, groups);
+    const int group = blockIdx.x / n_parts;
+    const int part = blockIdx.x - group * n_parts;
+    if (group >= groups) return;  // whole workgroup idle
+    const int slot0 = group * NWAVES * 32;
     const int lane = threadIdx.x & 63;
     const int kh = lane >> 5;
     const int slot = slot0 + (threadIdx.x >> 6) * 32 + (lane & 31);
@@ -1583,7 +1593,7 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     const bool bonus_only = busy && __all(!active || bonus);
     uint4 afr[KS];
     uint4 b0[4], t0[4];
-    int s = blockIdx.x;  // < n_strips: the launch has n_parts <= n_strips
+    int s = part;  // < n_strips: n_parts <= n_strips
     if (busy && !bonus_only) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) afr[kk] = *reinterpret_cast<const uint4*>(arow + 16 * kk);
@@ -1625,8 +1635,8 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma_rk(
     row_merge(sr, xlane_row<5>(sr));
     row_merge(sf, xlane_row<5>(sf));
     if (active && kh == 0) {
-        store_partial(res, static_cast<size_t>(slot) * n_parts + blockIdx.x, sr);
-        store_partial(fall, static_cast<size_t>(slot) * n_parts + blockIdx.x, sf);
+        store_partial(res, static_cast<size_t>(slot) * n_parts + part, sr);
+        store_partial(fall, static_cast<size_t>(slot) * n_parts + part, sf);
     }
 }
 
@@ -1693,23 +1703,24 @@ hipError_t launch_draft_step_nw(const DraftArgs& a, const int32_t* prev, int pre
 }
 
 template <int NWAVES>
-hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
+hipError_t launch_residual_strip(const ResidualArgs& a, ResGeom* geom) {
     const VerifyArgs& v = *a.v;
     if (v.r == 256) {
         static LdsReady lds_rk;
         hipError_t e = allow_big_lds(&residual_strip_mfma_rk<NWAVES, 16>, lds_rk);
         if (e != hipSuccess) return e;
-        const int groups = static_cast<int>(ceil_div(v.B, 32 * NWAVES));
-        const int parts = std::max(1, std::min(a.n_strips, device_cus() / groups));
-        *n_parts = parts;
-        dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(groups));
-        hipLaunchKernelGGL((residual_strip_mfma_rk<NWAVES, 16>), grid, dim3(64 * NWAVES), 0,
-                           v.stream, static_cast<const uint16_t*>(v.base),
+        // one workgroup per CU, split on the device over the groups the list
+        // fills, and at least one per request group the list can fill
+        const int wgs =
+            std::max(device_cus(), static_cast<int>(ceil_div(v.B, 32 * NWAVES)));
+        *geom = ResGeom{0, wgs, NWAVES};
+        hipLaunchKernelGGL((residual_strip_mfma_rk<NWAVES, 16>), dim3(static_cast<unsigned>(wgs)),
+                           dim3(64 * NWAVES), 0, v.stream, static_cast<const uint16_t*>(v.base),
                            static_cast<const uint16_t*>(v.A), static_cast<const uint16_t*>(v.W),
                            static_cast<const uint16_t*>(v.target), v.row_off, v.tokens,
                            v.prev_token, v.draft_lse, v.temperature, v.accepted, a.list, a.count,
                            v.lengths, a.lse_tab, v.seed, v.B, v.K, v.V, v.r, a.res, a.fall, a.n_strips,
-                           parts);
+                           wgs);
         return hipGetLastError();
     }
     static LdsReady lds_ok;
@@ -1718,7 +1729,7 @@ hipError_t launch_residual_strip(const ResidualArgs& a, int* n_parts) {
     const size_t lds = 2 * sizeof(uint16_t) * static_cast<size_t>(v.r) * kPitch;
     const int groups = static_cast<int>(ceil_div(v.B, 32 * NWAVES));
     const int parts = std::max(1, std::min(a.n_strips, device_cus() / groups));
-    *n_parts = parts;
+    *geom = ResGeom{parts, 0, NWAVES};
     dim3 grid(static_cast<unsigned>(parts), static_cast<unsigned>(groups));
     hipLaunchKernelGGL(residual_strip_mfma<NWAVES>, grid, dim3(64 * NWAVES), lds, v.stream,
                        static_cast<const uint16_t*>(v.base), static_cast<const uint16_t*>(v.A),
@@ -1802,10 +1813,10 @@ hipError_t launch_draft_mfma_step(const DraftArgs& a, const int32_t* prev, int p
     return launch_draft_step_nw<2>(a, prev, prev_stride, k, order, part, n_strips, n_parts);
 }
 
-hipError_t launch_residual_mfma(const ResidualArgs& a, int* n_parts) {
-    if (a.v->B > 128) return launch_residual_strip<8>(a, n_parts);
-    if (a.v->B > 64) return launch_residual_strip<4>(a, n_parts);
-    return launch_residual_strip<2>(a, n_parts);
+hipError_t launch_residual_mfma(const ResidualArgs& a, ResGeom* geom) {
+    if (a.v->B > 128) return launch_residual_strip<8>(a, geom);
+    if (a.v->B > 64) return launch_residual_strip<4>(a, geom);
+    return launch_residual_strip<2>(a, geom);
 }
 
 }  // namespace dspark

@@ -104,7 +104,22 @@ struct ResidualArgs {
     int n_strips;
 };
 bool residual_mfma_supported(const VerifyArgs& a);
-hipError_t launch_residual_mfma(const ResidualArgs& a, int* n_parts);
+// How the residual strip partials of one listed request are laid out: n_parts
+// per request, or (wgs > 0) a split of a wgs-workgroup grid over the request
+// groups of nw wavefronts the list fills, known only on the device
+// (residual_parts).
+struct ResGeom {
+    int n_parts;
+    int wgs;
+    int nw;
+};
+// Parts per request group when the list fills `groups` groups of a grid of
+// `wgs` workgroups over n_strips strips.
+__host__ __device__ inline int residual_parts(int n_strips, int wgs, int groups) {
+    const int p = wgs / (groups > 0 ? groups : 1);
+    return p < 1 ? 1 : (p < n_strips ? p : n_strips);
+}
+hipError_t launch_residual_mfma(const ResidualArgs& a, ResGeom* geom);
 hipError_t launch_verify(const VerifyArgs& a);
 // Compute units of the current device (queried once per device).
 int device_cus();

@@ -545,11 +545,17 @@ __global__ __launch_bounds__(256) void verify_residual_valu(
 // Fold the residual strips of each listed request into its next token: the
 // winner of the residual keys when any entry had positive residual mass, else
 // the winner of the fallback keys (for a listed full acceptance, its bonus).
-// One wavefront per listed request.
-__global__ __launch_bounds__(kWave) void verify_residual_combine(VerifyWs ws, int B, int n_strips,
+// One wavefront per listed request.  The partials per request are g.n_parts,
+// or with g.wgs > 0 the split residual_parts makes of the list's length.
+__global__ __launch_bounds__(kWave) void verify_residual_combine(VerifyWs ws, int B, int n_strips_v,
+                                                                 ResGeom g,
                                                                  int32_t* __restrict__ next_token) {
     const int slot = blockIdx.x;
-    if (slot >= listed_count(ws.count)) return;
+    const int count = listed_count(ws.count);
+    if (slot >= count) return;
+    const int n_strips =
+        g.wgs > 0 ? residual_parts(n_strips_v, g.wgs, (count + 32 * g.nw - 1) / (32 * g.nw))
+                  : g.n_parts;
     const int lane = threadIdx.x;
     RowState sr = row_empty();
     RowState sf = row_empty();
@@ -706,14 +712,16 @@ hipError_t launch_verify(const VerifyArgs& a) {
     if (e != hipSuccess) return e;
     if (a.K == 0) return hipSuccess;  // no draft rows: every next token is a bonus draw
     int n_strips;
+    ResGeom geom{0, 0, 0};  // partials per listed request
     ProfScope res_scope(DSPARK_KERNEL_RESIDUAL_STRIP, a.stream);
     if (residual_mfma_supported(a)) {
         n_strips = static_cast<int>(ceil_div(a.V, kMfmaStrip));
         ResidualArgs ra{&a, ws.list, ws.count, ws.lse, ws.res, ws.fall, n_strips};
-        e = launch_residual_mfma(ra, &n_strips);  // partials per listed request
+        e = launch_residual_mfma(ra, &geom);
         if (e != hipSuccess) return e;
     } else {
         n_strips = static_cast<int>(ceil_div(a.V, kValuStrip));
+        geom.n_parts = n_strips;
         if (a.logit_dt == DSPARK_BF16 && a.factor_dt == DSPARK_BF16)
             launch_residual_valu<bf16_t, bf16_t>(a, ws, n_strips);
         else if (a.logit_dt == DSPARK_BF16)
@@ -729,7 +737,7 @@ hipError_t launch_verify(const VerifyArgs& a) {
     res_scope.slot = -1;
     ProfScope combine_scope(DSPARK_KERNEL_RESIDUAL_COMBINE, a.stream);
     hipLaunchKernelGGL(verify_residual_combine, dim3(static_cast<unsigned>(a.B)), dim3(kWave), 0,
-                       a.stream, ws, a.B, n_strips, a.next_token);
+                       a.stream, ws, a.B, n_strips, geom, a.next_token);
     return hipGetLastError();
 }
 
