@@ -1240,8 +1240,31 @@ __global__ __launch_bounds__(64 * NWAVES) void residual_strip_mfma(
 }
 
 // ------------------------------------------------------------ visit order
-// Requests are visited greedy (T == 0) first, then sampled, each group in
-// request order, so a wavefront rarely mixes the two epilogues.  One workgroup.
+// Requests are visited greedy (T == 0) first, then sampled, each kind in
+// request order, so a wavefront rarely mixes the two epilogues.  With more
+// than one request group (kOrderGroup slots each, one workgroup row of the
+// strip kernels) every group takes its share of the greedy requests, greedy
+// first: group g holds greedy ranks [Q(g), Q(g + 1)), Q(g) = floor(n_greedy
+// g kOrderGroup / B), then the sampled ones that fill it.  Groups of one
+// kind only would give the launch workgroups of very different length.
+// One workgroup.
+constexpr int kOrderGroup = 256;
+
+__device__ __forceinline__ int order_slot(int rank, bool greedy, int n_greedy, int B) {
+    auto q = [&](int slot) {
+        return static_cast<int>(static_cast<int64_t>(n_greedy) * slot / B);
+    };
+    int g = 0;
+    while (true) {
+        const int end = min((g + 1) * kOrderGroup, B);
+        if (greedy ? rank < q(end) : rank < end - q(end)) break;
+        ++g;
+    }
+    const int start = g * kOrderGroup;
+    const int q0 = q(start), q1 = q(min(start + kOrderGroup, B));
+    return greedy ? start + (rank - q0) : start + (q1 - q0) + (rank - (start - q0));
+}
+
 __global__ __launch_bounds__(1024) void temperature_order(const float* __restrict__ temperature,
                                                           int B, int32_t* __restrict__ order) {
     __shared__ int sh[1024 / kWave];
@@ -1259,7 +1282,7 @@ __global__ __launch_bounds__(1024) void temperature_order(const float* __restric
     }
     __syncthreads();
     const int n_greedy = sh_total;
-    int off_g = 0, off_s = n_greedy;
+    int off_g = 0, off_s = 0;  // ranks among the greedy / sampled requests
     for (int c0 = 0; c0 < B; c0 += 1024) {
         const int b = c0 + tid;
         const int g = (b < B) && !(temperature[b] > 0.0f);
@@ -1287,8 +1310,8 @@ __global__ __launch_bounds__(1024) void temperature_order(const float* __restric
             tg += vg;
             ts += vs;
         }
-        if (g) order[off_g + bg + ig - 1] = b;
-        if (s) order[off_s + bs + is - 1] = b;
+        if (g) order[order_slot(off_g + bg + ig - 1, true, n_greedy, B)] = b;
+        if (s) order[order_slot(off_s + bs + is - 1, false, n_greedy, B)] = b;
         off_g += tg;
         off_s += ts;
     }

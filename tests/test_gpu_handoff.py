@@ -36,15 +36,29 @@ def inputs():
 
 
 def _visit_order(temp):
+    """The strip kernels' visit order: greedy requests first, then sampled,
+    each kind in request order, with every group of 256 slots taking its share
+    floor(n_greedy (g + 1) 256 / B) - floor(n_greedy g 256 / B) of the greedy
+    ones (first in the group)."""
     t = temp.cpu().numpy()
-    return [b for b in range(len(t)) if not t[b] > 0] + [b for b in range(len(t)) if t[b] > 0]
+    B = len(t)
+    greedy = [b for b in range(B) if not t[b] > 0]
+    sampled = [b for b in range(B) if t[b] > 0]
+    ng = len(greedy)
+    order = []
+    for start in range(0, B, 256):
+        end = min(start + 256, B)
+        q0, q1 = ng * start // B, ng * end // B
+        order += greedy[q0:q1] + sampled[start - q0:end - q1]
+    assert sorted(order) == list(range(B))
+    return order
 
 
 # (B, V, K, n_greedy): 64 -> both helpers; 70 -> helper 0 serves a mixed
 # wavefront 2; 40 -> only helper 0 (wavefront 1 mixed); 96 -> only helper 1;
 # B = 200 -> wavefront 6 half active and 7 inactive (helper 0 only);
-# B = 300 -> a second request group with no helpers; B = 512 -> two groups,
-# the second all sampled
+# B = 300 -> a second request group of 44 slots; B = 512 -> two groups, each
+# with its share of the greedy requests
 CASES = [
     (256, 70016, 3, 64),
     (200, 66048, 2, 64),
