@@ -203,14 +203,25 @@ __device__ __forceinline__ float entry_l2(uint32_t w, const KeyLane& kl) {
 // The verifier's residual list: the sampled first rejections at
 // list[0 .. count[0]) and the sampled full acceptances (whose next token is the
 // bonus draw) from the back, list[B - 1 - i] for i < count[1].  Slot s in
-// [0, count[0] + count[1]) names one listed request, rejections first, so that
-// the wavefronts of the residual kernels hold one kind of request (but for the
-// one at the boundary).
+// [0, n), n = count[0] + count[1], names one listed request.  Slots come in
+// groups of 256 (a workgroup row of the residual strip kernels); each group
+// takes its share of the rejections, first, then of the full acceptances:
+// group [start, end) holds rejection ranks [q(start), q(end)), q(x) =
+// floor(count[0] x / n).  So the groups carry like work (a rejection
+// recomputes its draft row, a full acceptance keys the target row alone), and
+// a wavefront holds one kind of request (but for the one at the boundary).
 __device__ __forceinline__ int listed_count(const int32_t* count) { return count[0] + count[1]; }
 
 __device__ __forceinline__ int listed_request(const int32_t* list, const int32_t* count, int B,
                                               int s) {
-    return s < count[0] ? list[s] : list[B - 1 - (s - count[0])];
+    const int nr = count[0], n = count[0] + count[1];
+    if (n <= 0) return list[B - 1];  // no listed request: an in-range stand-in
+    const int start = s & ~255, end = min(start + 256, n);
+    const int q0 = static_cast<int>(static_cast<int64_t>(nr) * start / n);
+    const int q1 = static_cast<int>(static_cast<int64_t>(nr) * end / n);
+    const int o = s - start;
+    if (o < q1 - q0) return list[q0 + o];
+    return list[B - 1 - ((start - q0) + (o - (q1 - q0)))];
 }
 
 struct ResRow {
