@@ -33,7 +33,9 @@ def close(a, b, tol) -> bool:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    ok = both_inf | (np.abs(a - b) <= tol * np.maximum(1.0, np.abs(b)))
+    finite = np.isfinite(a) & np.isfinite(b)
+    diff = np.abs(np.where(finite, a, 0.0) - np.where(finite, b, 0.0))
+    ok = both_inf | (finite & (diff <= tol * np.maximum(1.0, np.abs(np.where(finite, b, 0.0)))))
     return bool(ok.all())
 
 
