@@ -1,6 +1,7 @@
 """GPU edge cases through the C ABI: exact ties (smallest index wins on every
 path and across strips and lanes), the smallest batch and draft length,
-extreme temperatures, a flat distribution, and degenerate schedules.  Where a
+extreme temperatures, a flat distribution, degenerate schedules, and
+verification with nothing drafted (K = 0).  Where a
 result has a closed form it is checked directly; elsewhere against the oracle
 with the near-tie rule of tests/parity.py."""
 import numpy as np
@@ -225,3 +226,41 @@ def test_parallel_drafting_equals_zero_transition(dsp, orc, K):
                      offs.cpu().numpy(), orv, P.tol_for(torch.bfloat16), tally)
     print(tally)
     assert tally.verify_clean >= len(idx) - 1
+
+
+@pytest.mark.parametrize("V,ldt", [(3000, torch.bfloat16), (3001, torch.bfloat16),
+                                   (3000, torch.float32)])
+def test_verify_with_nothing_drafted(dsp, orc, V, ldt):
+    """K = 0: no drafted token, so every request accepts none and its next token
+    is the bonus draw from its single target row (row L_b + 1 = 1).  The draft
+    inputs are empty and the factors absent (NULL at the boundary).  Greedy and
+    sampled requests; whole 16-byte chunks (V = 3000) and a ragged row end
+    (V = 3001); with and without the per-row outputs."""
+    B, seed, dev = 70, 13, "cuda"
+    g = torch.Generator().manual_seed(40 + V)
+    target = (3.0 * torch.randn((B, V), generator=g)).to(ldt)
+    temp = torch.tensor([(0.0, 0.7, 1.0)[b % 3] for b in range(B)], dtype=torch.float32)
+    prev = torch.randint(0, V, (B,), generator=g, dtype=torch.int32)
+    no_tok = torch.empty((B, 0), dtype=torch.int32, device=dev)
+    no_f = torch.empty((B, 0), dtype=torch.float32, device=dev)
+    no_base = torch.empty((B, 0, V), dtype=ldt, device=dev)
+    offs = torch.arange(B, dtype=torch.int64, device=dev)
+    args = (no_tok, prev.to(dev), no_f, no_f, no_base, None, None, target.to(dev), offs,
+            temp.to(dev), seed)
+    acc, nxt, rl, _ = dsp.dspark_verify(*args)
+    acc2, nxt2, _, _ = dsp.dspark_verify(*args, row_outputs=False)
+    torch.cuda.synchronize()
+    assert (acc == 0).all() and torch.equal(acc2, acc) and torch.equal(nxt2, nxt)
+    t32 = P.np32(target)
+    rl = rl.cpu().numpy()
+    zA, zW = np.zeros((V, 1), np.float32), np.zeros((1, V), np.float32)
+    near = 0
+    for b in range(B):
+        res = orc.verify_request(np.zeros(0, np.int32), int(prev[b]), np.zeros((0, V), np.float32),
+                                 zA, zW, t32[b:b + 1], 0, float(temp[b]), seed, b)
+        assert res["accepted"] == 0
+        assert P.close(rl[b:b + 1], res["row_lse_t"], P.tol_for(ldt)), (b, rl[b], res["row_lse_t"])
+        if int(nxt[b]) != res["next_token"]:
+            assert res["next_gap"] < P.NEAR_TIE, (b, int(nxt[b]), res["next_token"])
+            near += 1
+    assert near <= 1
