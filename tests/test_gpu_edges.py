@@ -1,7 +1,7 @@
 """GPU edge cases through the C ABI: exact ties (smallest index wins on every
 path and across strips and lanes), the smallest batch and draft length,
-extreme temperatures, a flat distribution, degenerate schedules, and
-verification with nothing drafted (K = 0).  Where a
+extreme temperatures, a flat distribution, degenerate schedules,
+verification with nothing drafted (K = 0) and a one-entry vocabulary (V = 1).  Where a
 result has a closed form it is checked directly; elsewhere against the oracle
 with the near-tie rule of tests/parity.py."""
 import numpy as np
@@ -264,3 +264,45 @@ def test_verify_with_nothing_drafted(dsp, orc, V, ldt):
             assert res["next_gap"] < P.NEAR_TIE, (b, int(nxt[b]), res["next_token"])
             near += 1
     assert near <= 1
+
+
+@pytest.mark.parametrize("ldt", [torch.float32, torch.bfloat16])
+def test_one_entry_vocabulary(dsp, orc, ldt):
+    """V = 1: draft and target put all mass on entry 0, so every drafted and
+    every next token is 0, log p_d = 0 (up to the rounding of the key and its
+    draw term) and every greedy draft is accepted.  A sampled draft is accepted
+    unless log u >= -log p_d, which that rounding allows only for u within about
+    1e-6 of 1.  Everything is also compared with the oracle."""
+    B, K, V, r, seed, dev = 40, 3, 1, 16, 29, "cuda"
+    g = torch.Generator().manual_seed(31)
+    inp = dict(base=(2.0 * torch.randn((B, K, V), generator=g)).to(ldt).to(dev),
+               A=(0.3 * torch.randn((V, r), generator=g)).to(ldt).to(dev),
+               W=(0.3 * torch.randn((r, V), generator=g)).to(ldt).to(dev),
+               prev=torch.zeros(B, dtype=torch.int32, device=dev),
+               temp=torch.tensor([(0.0, 0.7, 1.0)[b % 3] for b in range(B)],
+                                 dtype=torch.float32, device=dev))
+    target = (2.0 * torch.randn((B * (K + 1), V), generator=g)).to(ldt).to(dev)
+    offs = torch.arange(B, dtype=torch.int64, device=dev) * (K + 1)
+    tok, logp, lse = dsp.dspark_draft_sample(inp["base"], inp["A"], inp["W"], inp["prev"],
+                                             inp["temp"], seed)
+    acc, nxt, rl, rr = dsp.dspark_verify(tok, inp["prev"], logp, lse, inp["base"], inp["A"],
+                                         inp["W"], target, offs, inp["temp"], seed)
+    torch.cuda.synchronize()
+    assert (tok == 0).all() and (nxt == 0).all()
+    greedy = inp["temp"] == 0
+    assert (acc[greedy] == K).all() and int((acc[~greedy] != K).sum()) <= 1
+    assert float(logp.abs().max()) < 1e-5
+    idx = list(range(B))
+    tol = P.tol_for(ldt)
+    tally = P.Tally()
+    ora = P.oracle_draft(orc, inp, idx, seed)
+    P.compare_draft(tok.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), ora,
+                    inp["temp"].cpu().numpy(), tol, tally)
+    assert tally.draft_clean == B
+    rows = {b: P.np32(target[b * (K + 1):(b + 1) * (K + 1)]) for b in idx}
+    orv = P.oracle_verify(orc, inp, idx, {b: ora[b][0] for b in idx}, rows, {b: K for b in idx},
+                          seed)
+    P.compare_verify(acc.cpu().numpy(), nxt.cpu().numpy(), rl.cpu().numpy(), rr.cpu().numpy(),
+                     offs.cpu().numpy(), orv, tol, tally)
+    print(tally)
+    assert tally.verify_clean >= B - 1
