@@ -139,6 +139,26 @@ def test_full_size_sampled_parity(dsp, orc, inputs, name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("B", [4096, 4097])
+def test_verify_tail_list_limits(dsp, orc, inputs, B):
+    """The second verify launch lists in LDS the rows still needed by up to
+    4096 requests: B = 4096 fills that list, and B = 4097 takes per-row launches
+    instead.  Both equal verification with every row read, and the oracle on
+    requests at the edges of the 256-request groups and of the list.  Enough
+    requests reach positions 5-7 (the second launch) and enough reject."""
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=B, K=6, V=2056)
+    inp = inputs.make_inputs(w, "cuda", seed=3)
+    idx = _spread_requests(inp["temp"], 16, extra=(255, 256, 2047, 2048, 4095, 4096))
+    tally, (_, _, _, acc, _) = _draft_and_verify(dsp, orc, inp, 9, idx, P.tol_for(w.dtype))
+    n_tail, n_rej = int((acc >= 4).sum()), int((acc < w.K).sum())
+    print(B, len(idx), tally, "reach position 5:", n_tail, "reject:", n_rej)
+    assert n_tail >= 20 and n_rej >= 20
+    assert tally.near_ties <= 1
+    assert tally.draft_clean >= len(idx) - 1 and tally.verify_clean >= len(idx) - 1
+    del inp
+    torch.cuda.empty_cache()
+
+
 def test_high_conc_pipeline_parity(dsp, orc, inputs):
     """Draft -> schedule -> verify of the scheduled prefixes over the dense
     target tensor ([B, K+1, V], offsets b (K+1)) at B=2048, V=131072, budget
