@@ -248,6 +248,36 @@ def test_schedule_parity_random(dsp, orc, seed):
             np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
 
 
+@pytest.mark.parametrize("B", [500, 700])
+def test_schedule_longest_drafts(dsp, orc, B):
+    """K = 64, the longest draft the scheduler takes: 32000 items (staged in LDS,
+    keys in registers) and 44800 (rows walked in memory), with budgets that
+    stop inside, at and past the items, under no curve, a curve whose rise
+    stops the walk (a sort) and a flat curve (the threshold alone)."""
+    K = 64
+    rng = np.random.default_rng(B)
+    conf = rng.beta(8, 1, (B, K)).astype(np.float32)
+    conf[rng.random((B, K)) < 0.01] = 0.0
+    c = torch.from_numpy(conf).cuda()
+    curves = (None, ([float(B), float(B + 20000)], [1.0, 3.0]),
+              ([float(B), float(B + B * K)], [2.0, 2.0]))
+    for budget in (B + 777, B + 9000, B + 25000, B * (K + 1)):
+        for curve in curves:
+            if curve is None:
+                L, offs, S = dsp.dspark_schedule(c, budget)
+                oL, ooffs, oS, n = orc.schedule(conf, budget)
+            else:
+                L, offs, S = dsp.dspark_schedule(c, budget, curve[0], curve[1])
+                oL, ooffs, oS, n = orc.schedule(conf, budget,
+                                                np.float32(curve[0]).astype(np.float64),
+                                                np.float32(curve[1]).astype(np.float64))
+            torch.cuda.synchronize()
+            print(B, budget, None if curve is None else curve[1], "taken", n)
+            np.testing.assert_array_equal(S.cpu().numpy(), oS)
+            np.testing.assert_array_equal(L.cpu().numpy(), oL)
+            np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+
+
 @pytest.mark.parametrize("B,K,extra,conf_kind", [
     (2048, 16, 12000, "beta"),    # 32768 items in registers, 12000 candidates: 16 per thread
     (2048, 16, 12000, "ones"),    # every S equal: the stop falls inside one run of ties
