@@ -139,6 +139,20 @@ def test_full_size_sampled_parity(dsp, orc, inputs, name):
     torch.cuda.empty_cache()
 
 
+def test_longest_draft_chain(dsp, orc, inputs):
+    """A 64-step Markov chain (each token feeds the next step's factor row) on
+    the rank-256 kernel, every request compared with the oracle, then verified
+    over its 65 target rows (the second verify launch covers positions 5-65)."""
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=40, K=64, V=2056)
+    inp = inputs.make_inputs(w, "cuda", seed=6)
+    tally, (_, _, _, acc, _) = _draft_and_verify(dsp, orc, inp, 12, list(range(w.B)),
+                                                 P.tol_for(w.dtype))
+    print(tally, "accepted:", sorted(acc.cpu().numpy().tolist()))
+    assert tally.near_ties <= 1
+    assert tally.draft_clean >= w.B - 1 and tally.verify_clean >= w.B - 1
+    assert tally.compared >= (w.B - 1) * w.K
+
+
 @pytest.mark.parametrize("B", [4096, 4097])
 def test_verify_tail_list_limits(dsp, orc, inputs, B):
     """The second verify launch lists in LDS the rows still needed by up to
