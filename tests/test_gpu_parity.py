@@ -139,6 +139,31 @@ def test_full_size_sampled_parity(dsp, orc, inputs, name):
     torch.cuda.empty_cache()
 
 
+def test_misaligned_inputs(dsp, orc, inputs):
+    """Logits and factors that start 2 bytes past a 16-byte boundary (views
+    into a larger buffer) cannot take the kernels with 16-byte and direct-to-LDS
+    loads; the library takes the element-load kernels instead (draft strip,
+    verify rows and residual), with the same results against the oracle."""
+    w = inputs.resized(inputs.WORKLOADS["long_draft"], B=24, K=3, V=2056)
+    inp = inputs.make_inputs(w, "cuda", seed=4)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+        v = buf[1:1 + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 == 2
+        return v
+
+    for k in ("base", "A", "W", "target"):
+        inp[k] = shifted(inp[k])
+    tally, (_, _, _, acc, _) = _draft_and_verify(dsp, orc, inp, 7, list(range(w.B)),
+                                                 P.tol_for(w.dtype))
+    print(tally)
+    assert int((acc < w.K).sum()) >= 5  # rejections: the residual kernel ran
+    assert tally.near_ties <= 1
+    assert tally.draft_clean >= w.B - 1 and tally.verify_clean >= w.B - 1
+
+
 def test_longest_draft_chain(dsp, orc, inputs):
     """A 64-step Markov chain (each token feeds the next step's factor row) on
     the rank-256 kernel, every request compared with the oracle, then verified
