@@ -90,7 +90,8 @@ size_t dspark_draft_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t r);
  *   base_logits  [B, K, V]  logit_dt    backbone logits per draft position
  *   A            [V, r]     factor_dt   transition factor looked up by the previous token
  *   W            [r, V]     factor_dt   transition factor over the next token
- *   prev_token   [B] int32              x_0, the last committed token (0 <= x_0 < V)
+ *   prev_token   [B] int32              x_0, the last committed token (0 <= x_0 < V;
+ *                                       an id outside is clamped to [0, V))
  *   temperature  [B] float              T per request
  *   seed                                Philox key
  * Outputs (device):

@@ -1,7 +1,8 @@
 """GPU edge cases through the C ABI: exact ties (smallest index wins on every
 path and across strips and lanes), the smallest batch and draft length,
 extreme temperatures, a flat distribution, degenerate schedules,
-verification with nothing drafted (K = 0) and a one-entry vocabulary (V = 1).  Where a
+verification with nothing drafted (K = 0), a one-entry vocabulary (V = 1), and
+out-of-range token ids and lengths (clamped).  Where a
 result has a closed form it is checked directly; elsewhere against the oracle
 with the near-tie rule of tests/parity.py."""
 import numpy as np
@@ -306,3 +307,46 @@ def test_one_entry_vocabulary(dsp, orc, ldt):
                      offs.cpu().numpy(), orv, tol, tally)
     print(tally)
     assert tally.verify_clean >= B - 1
+
+
+@pytest.mark.parametrize("V,r,dt", [(2056, 256, torch.bfloat16), (2003, 16, torch.float32)])
+def test_out_of_range_ids_and_lengths_are_clamped(dsp, V, r, dt):
+    """Token ids and lengths read from device memory are clamped before they
+    index anything (ids to [0, V), lengths to [0, K]): out-of-range previous
+    tokens, drafted tokens and lengths give exactly the results of their
+    clamped values, on the rank-256 MFMA paths and on the fp32 VALU paths."""
+    from draft_sampling_verification_04_amd import inputs as inputs_mod
+
+    w = inputs_mod.resized(inputs_mod.WORKLOADS["long_draft"], B=24, K=4, V=V, r=r, dtype=dt)
+    inp = inputs_mod.make_inputs(w, "cuda", seed=5)
+    B, K = w.B, w.K
+    bad_prev = inp["prev"].clone()
+    bad_prev[0::4] = -7
+    bad_prev[1::4] = V + 11
+    args = (inp["base"], inp["A"], inp["W"])
+    d_bad = dsp.dspark_draft_sample(*args, bad_prev, inp["temp"], 8)
+    d_ok = dsp.dspark_draft_sample(*args, bad_prev.clamp(0, V - 1), inp["temp"], 8)
+    torch.cuda.synchronize()
+    for x, y in zip(d_bad, d_ok):
+        assert torch.equal(x, y)
+    tok, logp, lse = d_ok
+    bad_tok = tok.clone()
+    bad_tok[0::3, 0] = -3
+    bad_tok[1::3, 1] = V + 5
+    bad_len = torch.full((B,), K, dtype=torch.int32, device="cuda")
+    bad_len[0::5] = -2
+    bad_len[1::5] = K + 6
+    bad_len[2::5] = 2
+    target = inp["target"].reshape(-1, V)
+    offs = inputs_mod.dense_offsets(B, K, "cuda")
+
+    def verify(t, L, p):
+        return dsp.dspark_verify(t, p, logp, lse, inp["base"], inp["A"], inp["W"], target, offs,
+                                 inp["temp"], 8, L)
+
+    v_bad = verify(bad_tok, bad_len, bad_prev)
+    v_ok = verify(bad_tok.clamp(0, V - 1), bad_len.clamp(0, K), bad_prev.clamp(0, V - 1))
+    torch.cuda.synchronize()
+    for x, y in zip(v_bad, v_ok):
+        assert torch.equal(x.nan_to_num(7.0), y.nan_to_num(7.0))
+    assert int((v_ok[0] < bad_len.clamp(0, K)).sum()) >= 3  # some rejections (residual draws)
