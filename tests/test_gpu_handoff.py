@@ -58,9 +58,12 @@ def _visit_order(temp):
 # wavefront 2; 40 -> only helper 0 (wavefront 1 mixed); 96 -> only helper 1;
 # B = 200 -> wavefront 6 half active and 7 inactive (helper 0 only);
 # B = 300 -> a second request group of 44 slots; B = 512 -> two groups, each
-# with its share of the greedy requests
+# with its share of the greedy requests; 0 -> every wavefront samples (no
+# helper); 256 -> every wavefront greedy (argmax epilogue only, nothing handed)
 CASES = [
     (256, 70016, 3, 64),
+    (256, 40064, 2, 0),
+    (256, 40064, 2, 256),
     (200, 66048, 2, 64),
     (256, 66048, 2, 70),
     (256, 66048, 2, 40),
